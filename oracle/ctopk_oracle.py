@@ -1,0 +1,285 @@
+"""Plain fp64 CPU oracle for certified Top-k attention truncation.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke entry point and the
+benchmark's CPU-baseline leg may import this module.  The library under
+``certified_top_sparse_amd`` never imports it, and this module imports nothing
+from the library: the two share no code.
+
+Source of every definition below: "A Mathematical Theory of Top-k Sparse
+Attention via Total Variation Distance" (Tzachristas, Deng, Tzachristas,
+Zhang, Chen; arXiv 2512.07647), Abstract.  The abstract defines:
+
+* P, the softmax attention distribution of one query over its keys;
+* the Top-k truncation P_hat, which keeps the k largest-score keys (the head H)
+  and renormalises them, giving zero weight to the tail T;
+* TV(P, P_hat), which equals the softmax mass of the discarded tail, and the
+  identity TV = 1 - exp(-KL(P_hat || P));
+* the head-only output Attn_k, its exact head/tail decomposition with
+  tau = TV, and the bound by tau times the head/tail diameter;
+* the minimal k_eps with TV <= eps, and its Gaussian-score design rule
+  k_eps / n ~ Phi_c(sigma + Phi^{-1}(eps)).
+
+Readings where the page leaves a step open (each is listed in the design doc):
+
+* the certificate is inclusive, TV <= eps, and k ranges over 1..n;
+* keys are ordered by score descending and, among equal scores, by index
+  ascending, so the lower index enters the head first;
+* the tail mass is summed directly from the smallest term upward, never as
+  1 - head mass;
+* diam_{H,T} is the largest Euclidean distance between a head value row and a
+  tail value row;
+* a row is "near-boundary" when T_{k_eps} or T_{k_eps - 1} lies within
+  1e-6 * eps of eps; such rows are reported, not failed, on a k_eps mismatch.
+
+Everything is computed in float64.  bf16 and fp32 inputs convert to float64
+exactly.  The score scale is applied as the float64 value of the float32 the
+device receives.
+
+Parity status: every function here is pinned by the tests in
+``tests/test_oracle_pins.py`` (identities, brute force, closed forms and the
+Gaussian design rule).  No value printed on the pages pins a specific
+(q, K, V) -> (k_eps, tau, out) triple; see the design doc.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+NEAR_BOUNDARY_REL = 1e-6
+
+
+# ---------------------------------------------------------------------------
+# input decoding (the oracle's own; shares nothing with the device path)
+# ---------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 value of bfloat16 bit patterns (uint16 array)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def as_f64(x) -> np.ndarray:
+    """float64 view of an input array: uint16 is taken as bf16 bits."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return x.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# scores
+# ---------------------------------------------------------------------------
+def scores(q, K, scale) -> np.ndarray:
+    """s_i = scale * <q, k_i> for every key row k_i (Abstract: P is the softmax
+    of these scores).  q: [d]; K: [n, d]; returns float64 [n]."""
+    q64 = as_f64(q)
+    K64 = as_f64(K)
+    return float(scale) * (K64 @ q64)
+
+
+def gqa_kv_head(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """KV head read by query head h: consecutive query heads share a KV head
+    (the grouped-query layout the second page's scan shares across)."""
+    return h // (n_q_heads // n_kv_heads)
+
+
+# ---------------------------------------------------------------------------
+# certified Top-k on given scores
+# ---------------------------------------------------------------------------
+def order_desc(s: np.ndarray) -> np.ndarray:
+    """Key order: score descending, index ascending among equal scores.
+    -0.0 and +0.0 compare equal here, as numpy compares them."""
+    s = np.asarray(s, dtype=np.float64)
+    idx = np.arange(s.shape[-1])
+    idx = np.broadcast_to(idx, s.shape)
+    return np.lexsort((idx, -s), axis=-1)
+
+
+def tail_masses(s: np.ndarray):
+    """For scores s [..., n]: returns (order, w, Z, T) where w = exp(s - max),
+    Z = sum(w) and T[..., k] is the softmax mass left out when the first k keys
+    of ``order`` are kept (k = 0..n).  T is accumulated from the smallest term
+    upward (Abstract: TV equals the discarded tail mass)."""
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1, keepdims=True)
+    w = np.exp(s - m)
+    Z = np.sum(w, axis=-1, keepdims=True)
+    P = w / Z
+    order = order_desc(s)
+    Ps = np.take_along_axis(P, order, axis=-1)
+    rev = np.cumsum(Ps[..., ::-1], axis=-1)[..., ::-1]  # rev[k] = sum_{j>=k} Ps[j]
+    zeros = np.zeros(s.shape[:-1] + (1,), dtype=np.float64)
+    T = np.concatenate([rev, zeros], axis=-1)
+    return order, w, Z[..., 0], T
+
+
+def minimal_k(T: np.ndarray, eps: float) -> np.ndarray:
+    """k_eps = min{k in 1..n : T[k] <= eps} (Abstract: the minimal k that keeps
+    TV(P, P_hat) <= eps).  T has n+1 entries with T[n] = 0."""
+    ok = T[..., 1:] <= eps
+    return np.argmax(ok, axis=-1) + 1
+
+
+def certify_scores(S, V, eps: float, row_to_v=None, with_diagnostics: bool = True):
+    """Certified Top-k truncation for every row of the score matrix S.
+
+    S: [R, n] scores; V: [Hv, n, dv] value rows; row r reads V[row_to_v[r]]
+    (default: all rows read V[0]).  Returns a dict of float64/int64 arrays:
+    k_eps [R], tau [R], out [R, dv], lse [R], T_prev [R] (= T_{k_eps - 1}),
+    near_boundary [R] (bool), head_mask [R, n] (bool), and, with diagnostics,
+    s_star [R] (score of the last kept key).
+    """
+    S = np.atleast_2d(np.asarray(S, dtype=np.float64))
+    V = as_f64(V)
+    if V.ndim == 2:
+        V = V[None]
+    R, n = S.shape
+    if row_to_v is None:
+        row_to_v = np.zeros(R, dtype=np.int64)
+    row_to_v = np.asarray(row_to_v, dtype=np.int64)
+    if not (0.0 < eps < 1.0):
+        raise ValueError("eps must lie in (0, 1)")
+
+    order, w, Z, T = tail_masses(S)
+    k = minimal_k(T, eps)
+    rows = np.arange(R)
+    tau = T[rows, k]
+    T_prev = T[rows, k - 1]
+    near = (np.abs(tau - eps) <= NEAR_BOUNDARY_REL * eps) | (
+        np.abs(T_prev - eps) <= NEAR_BOUNDARY_REL * eps)
+
+    rank = np.empty_like(order)
+    np.put_along_axis(rank, order, np.broadcast_to(np.arange(n), order.shape), axis=-1)
+    head = rank < k[:, None]
+
+    # Attn_k: renormalised head-only output (Abstract).
+    wh = np.where(head, w, 0.0)
+    num = np.empty((R, V.shape[-1]), dtype=np.float64)
+    for g in np.unique(row_to_v):
+        sel = row_to_v == g
+        num[sel] = wh[sel] @ V[g]
+    den = np.sum(wh, axis=-1)
+    out = num / den[:, None]
+
+    res = {
+        "k_eps": k.astype(np.int64),
+        "tau": tau,
+        "out": out,
+        "lse": np.log(Z) + np.max(S, axis=-1),
+        "T_prev": T_prev,
+        "near_boundary": near,
+        "head_mask": head,
+    }
+    if with_diagnostics:
+        last = np.take_along_axis(order, (k - 1)[:, None], axis=-1)[:, 0]
+        res["s_star"] = S[rows, last]
+    return res
+
+
+def certify(q, K, V, eps: float, n_q_heads: int, n_kv_heads: int, head_scale=None):
+    """Decode-shaped entry: q [Hq, d], K/V [Hkv, n, d] (float or bf16 bits).
+
+    head_scale: per-query-head float32 scale; default float32(1/sqrt(d)).
+    Returns the dict of ``certify_scores`` plus the fp64 scores "S".
+    """
+    q64 = as_f64(q).reshape(n_q_heads, -1)
+    K64 = as_f64(K)
+    d = q64.shape[1]
+    if head_scale is None:
+        head_scale = np.full(n_q_heads, np.float32(1.0 / math.sqrt(d)), dtype=np.float32)
+    sc = np.asarray(head_scale, dtype=np.float32).astype(np.float64)
+    G = n_q_heads // n_kv_heads
+    n = K64.shape[1]
+    S = np.empty((n_q_heads, n), dtype=np.float64)
+    for g in range(n_kv_heads):
+        hs = slice(g * G, (g + 1) * G)
+        S[hs] = sc[hs, None] * (q64[hs] @ K64[g].T)
+    row_to_v = np.arange(n_q_heads) // G
+    res = certify_scores(S, V, eps, row_to_v)
+    res["S"] = S
+    return res
+
+
+def certify_logits(logits, V, eps: float, n_v: int = 1):
+    """Select-only entry on given logits [rows, n]; row r reads V head
+    r // (rows / n_v) of V [n_v, n, dv]."""
+    L = np.asarray(logits, dtype=np.float64)
+    R = L.shape[0]
+    row_to_v = np.arange(R) // (R // n_v)
+    return certify_scores(L, V, eps, row_to_v)
+
+
+# ---------------------------------------------------------------------------
+# quantities the Abstract relates to one another (used by the pins)
+# ---------------------------------------------------------------------------
+def softmax(s) -> np.ndarray:
+    s = np.asarray(s, dtype=np.float64)
+    w = np.exp(s - np.max(s))
+    return w / np.sum(w)
+
+
+def truncation(P: np.ndarray, head: np.ndarray) -> np.ndarray:
+    """P_hat: P restricted to the head and renormalised (Abstract)."""
+    Ph = np.where(head, P, 0.0)
+    return Ph / np.sum(Ph)
+
+
+def tv_half_l1(P: np.ndarray, Q: np.ndarray) -> float:
+    """Total variation distance as half the L1 distance."""
+    return 0.5 * float(np.sum(np.abs(P - Q)))
+
+
+def tv_sup_events(P: np.ndarray, Q: np.ndarray) -> float:
+    """Total variation distance as the largest gap |P(A) - Q(A)| over all
+    events A; brute force, so only for tiny supports."""
+    n = P.shape[0]
+    best = 0.0
+    for r in range(n + 1):
+        for A in itertools.combinations(range(n), r):
+            A = list(A)
+            best = max(best, abs(float(P[A].sum() - Q[A].sum())))
+    return best
+
+
+def kl(Q: np.ndarray, P: np.ndarray) -> float:
+    """KL(Q || P) over the support of Q."""
+    m = Q > 0
+    return float(np.sum(Q[m] * np.log(Q[m] / P[m])))
+
+
+def head_tail_means(P: np.ndarray, V: np.ndarray, head: np.ndarray):
+    """mu_head and mu_tail: P-weighted means of the value rows over H and T."""
+    V = as_f64(V)
+    PH = np.where(head, P, 0.0)
+    PT = np.where(head, 0.0, P)
+    mu_h = PH @ V / PH.sum()
+    mu_t = PT @ V / PT.sum() if PT.sum() > 0 else np.zeros(V.shape[1])
+    return mu_h, mu_t
+
+
+def diam_head_tail(V: np.ndarray, head: np.ndarray) -> float:
+    """diam_{H,T}: largest distance between a head value row and a tail value
+    row (reading of the Abstract's head-tail diameter)."""
+    V = as_f64(V)
+    VH = V[head]
+    VT = V[~head]
+    if VT.shape[0] == 0:
+        return 0.0
+    d2 = (np.sum(VH * VH, 1)[:, None] + np.sum(VT * VT, 1)[None, :]
+          - 2.0 * VH @ VT.T)
+    return float(np.sqrt(max(0.0, float(np.max(d2)))))
+
+
+def gaussian_design_rule(sigma: float, eps: float) -> float:
+    """k_eps / n ~ Phi_c(sigma + Phi^{-1}(eps)) for i.i.d. N(mu, sigma^2)
+    scores (Abstract), with Phi_c = 1 - Phi."""
+    from scipy.special import ndtr, ndtri
+    return float(1.0 - ndtr(sigma + ndtri(eps)))
+
+
+def gaussian_tail_fraction(sigma: float, z: float) -> float:
+    """Closed-form softmax mass below mu + z*sigma for N(mu, sigma^2) scores in
+    the large-n limit: E[e^s 1{s <= t}] / E[e^s] = Phi(z - sigma)."""
+    from scipy.special import ndtr
+    return float(ndtr(z - sigma))

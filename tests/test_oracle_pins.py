@@ -1,0 +1,298 @@
+"""Pins of the fp64 oracle to what the Abstract of "A Mathematical Theory of
+Top-k Sparse Attention via Total Variation Distance" (arXiv 2512.07647) and
+plain mathematics fix.  CPU only.
+
+Each test checks the oracle against something other than itself:
+* hand-derived closed forms (tests/golden/closed_forms.json);
+* the definition of total variation as a supremum over events (brute force);
+* the TV-KL identity, the head-tail factorisation and the diameter bound;
+* exhaustive search over all key subsets for the minimal certified k;
+* library routines (scipy's softmax) in the special case k = n;
+* the Gaussian-score closed forms and design rule.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import softmax as sp_softmax
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _frac(x):
+    return float(Fraction(x[0], x[1]))
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_golden_closed_forms(case):
+    s = np.log(np.array(case["log_weights"], dtype=np.float64))
+    V = np.array(case["V"], dtype=np.float64)[None]
+    r = oracle.certify_scores(s[None], V, case["eps"])
+    assert int(r["k_eps"][0]) == case["k_eps"]
+    assert abs(r["tau"][0] - _frac(case["tau"])) < 1e-14
+    assert sorted(np.nonzero(r["head_mask"][0])[0].tolist()) == case["head"]
+    out = np.array([_frac(x) for x in case["out"]])
+    np.testing.assert_allclose(r["out"][0], out, rtol=0, atol=1e-14)
+    assert not r["near_boundary"][0]
+    if "attn" in case:
+        attn = np.array([_frac(x) for x in case["attn"]])
+        P = oracle.softmax(s)
+        np.testing.assert_allclose(P @ V[0], attn, atol=1e-14)
+        Ph = oracle.truncation(P, r["head_mask"][0])
+        assert abs(oracle.kl(Ph, P) - (-math.log(7 / 8))) < 1e-14
+        assert abs(oracle.diam_head_tail(V[0], r["head_mask"][0]) ** 2 - case["diam_sq"]) < 1e-12
+
+
+def _random_rows(rng, count, n, sigma):
+    return sigma * rng.standard_normal((count, n))
+
+
+@pytest.mark.parametrize("n,sigma,eps", [(64, 1.0, 0.01), (257, 3.0, 0.1), (1000, 2.0, 0.001),
+                                         (512, 8.0, 0.01), (33, 0.1, 0.3)])
+def test_tv_is_tail_mass_and_kl_identity(n, sigma, eps):
+    rng = np.random.default_rng(7 + n)
+    S = _random_rows(rng, 6, n, sigma)
+    V = rng.standard_normal((1, n, 5))
+    r = oracle.certify_scores(S, V, eps)
+    for i in range(S.shape[0]):
+        P = oracle.softmax(S[i])
+        head = r["head_mask"][i]
+        Ph = oracle.truncation(P, head)
+        tv = oracle.tv_half_l1(P, Ph)
+        assert abs(tv - r["tau"][i]) < 1e-12
+        assert r["tau"][i] <= eps
+        kl = oracle.kl(Ph, P)
+        assert abs(-math.expm1(-kl) - r["tau"][i]) < 1e-12
+        assert int(head.sum()) == int(r["k_eps"][i])
+
+
+def test_tv_matches_supremum_over_events():
+    rng = np.random.default_rng(11)
+    for n in (3, 6, 9, 11):
+        for eps in (0.05, 0.3):
+            s = 2.0 * rng.standard_normal(n)
+            r = oracle.certify_scores(s[None], rng.standard_normal((1, n, 2)), eps)
+            P = oracle.softmax(s)
+            Ph = oracle.truncation(P, r["head_mask"][0])
+            assert abs(oracle.tv_sup_events(P, Ph) - r["tau"][0]) < 1e-12
+
+
+@pytest.mark.parametrize("n,sigma,eps,dv", [(128, 1.0, 0.01, 16), (300, 4.0, 0.1, 8),
+                                            (50, 0.5, 0.2, 3)])
+def test_head_tail_factorisation_and_diameter_bound(n, sigma, eps, dv):
+    rng = np.random.default_rng(100 + n)
+    S = _random_rows(rng, 5, n, sigma)
+    V = rng.standard_normal((1, n, dv))
+    r = oracle.certify_scores(S, V, eps)
+    for i in range(S.shape[0]):
+        head = r["head_mask"][i]
+        attn = sp_softmax(S[i]) @ V[0]          # library softmax, not the oracle's
+        err = attn - r["out"][i]
+        P = oracle.softmax(S[i])
+        mu_h, mu_t = oracle.head_tail_means(P, V[0], head)
+        np.testing.assert_allclose(mu_h, r["out"][i], rtol=1e-12, atol=1e-13)
+        fac = r["tau"][i] * (mu_t - mu_h)
+        np.testing.assert_allclose(err, fac, rtol=1e-9, atol=1e-14)
+        ne = np.linalg.norm(err)
+        assert abs(ne - r["tau"][i] * np.linalg.norm(mu_t - mu_h)) <= 1e-10 * max(ne, 1e-300)
+        assert ne <= r["tau"][i] * oracle.diam_head_tail(V[0], head) * (1 + 1e-12)
+
+
+def _subset_masses(P):
+    n = P.shape[0]
+    masks = np.arange(1 << n, dtype=np.int64)
+    bits = ((masks[:, None] >> np.arange(n)) & 1).astype(np.float64)
+    return masks, bits @ P, bits.sum(1).astype(np.int64)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_bruteforce_minimal_k_and_topk_optimality(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 17))
+    sigma = float(rng.choice([0.3, 1.0, 2.0, 5.0]))
+    eps = float(rng.choice([0.001, 0.01, 0.05, 0.2, 0.5]))
+    s = sigma * rng.standard_normal(n)
+    r = oracle.certify_scores(s[None], rng.standard_normal((1, n, 3)), eps)
+    P = oracle.softmax(s)
+    masks, kept, sizes = _subset_masses(P)
+    dropped = 1.0 - kept
+    k_brute = None
+    for k in range(1, n + 1):
+        sel = sizes == k
+        if dropped[sel].min() <= eps + 1e-15:
+            k_brute = k
+            best = masks[sel][np.argmin(dropped[sel])]
+            break
+    assert k_brute == int(r["k_eps"][0])
+    head_bits = sum(1 << int(i) for i in np.nonzero(r["head_mask"][0])[0])
+    assert head_bits == int(best)
+
+
+def test_equal_scores_closed_form():
+    n, eps = 1000, 0.0123
+    s = np.zeros((1, n))
+    rng = np.random.default_rng(3)
+    V = rng.standard_normal((1, n, 4))
+    r = oracle.certify_scores(s, V, eps)
+    k = math.ceil(n * (1 - eps))   # T_k = (n - k)/n <= eps
+    assert int(r["k_eps"][0]) == k
+    assert abs(r["tau"][0] - (n - k) / n) < 1e-12
+    np.testing.assert_allclose(r["out"][0], V[0, :k].mean(0), rtol=1e-12, atol=1e-13)
+    assert r["head_mask"][0, :k].all() and not r["head_mask"][0, k:].any()
+
+
+def test_equal_scores_exact_boundary_is_flagged():
+    n, eps = 100, 0.25           # T_75 = 25/100 = eps up to rounding
+    r = oracle.certify_scores(np.zeros((1, n)), np.ones((1, n, 2)), eps)
+    assert r["near_boundary"][0]
+    assert int(r["k_eps"][0]) in (75, 76)
+
+
+def test_signed_zero_scores_tie():
+    s = np.array([[-0.0, 0.0, -0.0, 0.0]])
+    r = oracle.certify_scores(s, np.eye(4)[None], 0.3)
+    assert int(r["k_eps"][0]) == 3
+    assert r["head_mask"][0].tolist() == [True, True, True, False]
+
+
+def test_two_level_closed_form():
+    n, m, a, b = 200, 13, 2.0, -1.0
+    rng = np.random.default_rng(5)
+    pos = rng.permutation(n)[:m]
+    s = np.full(n, b)
+    s[pos] = a
+    Z = m * math.exp(a) + (n - m) * math.exp(b)
+    for eps in (0.001, 0.05, 0.3, 0.6, 0.9):
+        def T(k):
+            if k <= m:
+                return ((m - k) * math.exp(a) + (n - m) * math.exp(b)) / Z
+            return (n - k) * math.exp(b) / Z
+        k_cf = min(k for k in range(1, n + 1) if T(k) <= eps)
+        r = oracle.certify_scores(s[None], rng.standard_normal((1, n, 2)), eps)
+        assert int(r["k_eps"][0]) == k_cf
+        assert abs(r["tau"][0] - T(k_cf)) < 1e-12
+        head = np.nonzero(r["head_mask"][0])[0]
+        hi = np.sort(pos)
+        lo = np.setdiff1d(np.arange(n), pos)
+        expect = np.sort(np.concatenate([hi[:min(k_cf, m)], lo[:max(0, k_cf - m)]]))
+        assert head.tolist() == expect.tolist()
+
+
+def test_one_dominant_key():
+    n, a, b = 300, 12.0, 0.0
+    s = np.full(n, b)
+    s[17] = a
+    r = oracle.certify_scores(s[None], np.random.default_rng(1).standard_normal((1, n, 3)), 0.01)
+    assert int(r["k_eps"][0]) == 1
+    tau = (n - 1) * math.exp(b) / (math.exp(a) + (n - 1) * math.exp(b))
+    assert abs(r["tau"][0] - tau) < 1e-15
+    assert r["head_mask"][0, 17]
+
+
+def test_keep_all_reduces_to_dense_attention():
+    rng = np.random.default_rng(9)
+    n, d = 40, 6
+    s = rng.standard_normal(n)
+    V = rng.standard_normal((1, n, d))
+    P = sp_softmax(s)
+    eps = 0.5 * float(P.min())        # every key is needed
+    r = oracle.certify_scores(s[None], V, eps)
+    assert int(r["k_eps"][0]) == n and r["tau"][0] == 0.0
+    np.testing.assert_allclose(r["out"][0], P @ V[0], rtol=1e-12, atol=1e-14)
+
+
+def test_scores_and_gqa_mapping():
+    rng = np.random.default_rng(2)
+    n_q, n_kv, n, d = 8, 2, 50, 16
+    K = rng.standard_normal((n_kv, n, d)).astype(np.float32)
+    V = rng.standard_normal((n_kv, n, d)).astype(np.float32)
+    q = np.zeros((n_q, d), dtype=np.float32)
+    for h in range(n_q):
+        q[h, h] = 1.0                    # q_h = e_h picks column h of K
+    scale = np.full(n_q, 0.5, dtype=np.float32)
+    r = oracle.certify(q, K, V, 0.1, n_q, n_kv, head_scale=scale)
+    for h in range(n_q):
+        g = h // (n_q // n_kv)
+        np.testing.assert_array_equal(r["S"][h], 0.5 * K[g, :, h].astype(np.float64))
+        assert oracle.gqa_kv_head(h, n_q, n_kv) == g
+
+
+def test_bf16_decode():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x3FC0], dtype=np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, 3.3895313892515355e38, 9.183549615799121e-41, 1.5]
+    got = oracle.bf16_bits_to_f64(bits)
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[3]) == -1.0
+
+
+def test_gaussian_tail_mass_closed_form():
+    rng = np.random.default_rng(21)
+    n = 2_000_000
+    for sigma in (0.5, 1.0, 2.0):
+        s = sigma * rng.standard_normal(n)
+        w = np.exp(s - s.max())
+        for z in (-1.0, 0.0, 1.5):
+            frac = w[s <= z * sigma].sum() / w.sum()
+            assert abs(frac - oracle.gaussian_tail_fraction(sigma, z)) < 6e-3
+
+
+@pytest.mark.parametrize("sigma", [1.0, 2.0])
+@pytest.mark.parametrize("n", [4096, 65536])
+@pytest.mark.parametrize("eps", [0.01, 0.1])
+def test_gaussian_design_rule(sigma, n, eps):
+    rows = 64 if n == 4096 else 16
+    wl = workloads.logit_sweep(sigma, n, rows=rows, dv=2)
+    r = oracle.certify_scores(wl["logits"], wl["V"], eps)
+    frac = float(np.mean(r["k_eps"] / n))
+    pred = oracle.gaussian_design_rule(sigma, eps)
+    assert abs(frac - pred) <= 0.005, (frac, pred)
+
+
+@pytest.mark.parametrize("sigma", [3.0, 4.0])
+def test_gaussian_design_rule_gap_closes_with_n(sigma):
+    eps = 0.01
+    pred = oracle.gaussian_design_rule(sigma, eps)
+    gaps = []
+    for n, rows in ((4096, 64), (262144, 4)):
+        wl = workloads.logit_sweep(sigma, n, rows=rows, dv=2)
+        r = oracle.certify_scores(wl["logits"], wl["V"], eps)
+        gaps.append(abs(float(np.mean(r["k_eps"] / n)) - pred))
+    assert gaps[1] < gaps[0]
+
+
+def test_design_rule_values():
+    # Phi_c(sigma + Phi^{-1}(eps)) evaluated with the error function directly.
+    def phi(x):
+        return 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+    def phi_inv(p):
+        lo, hi = -40.0, 40.0
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            if phi(mid) < p:
+                lo = mid
+            else:
+                hi = mid
+        return 0.5 * (lo + hi)
+
+    for sigma in (1.0, 2.0, 3.0, 4.0):
+        for eps in (0.001, 0.01, 0.1):
+            want = 1.0 - phi(sigma + phi_inv(eps))
+            assert abs(oracle.gaussian_design_rule(sigma, eps) - want) < 1e-9
+
+
+def test_eps_outside_open_interval_rejected():
+    for eps in (0.0, 1.0, -0.1, 1.5):
+        with pytest.raises(ValueError):
+            oracle.certify_scores(np.zeros((1, 4)), np.ones((1, 4, 1)), eps)
