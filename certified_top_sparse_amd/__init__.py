@@ -1,0 +1,13 @@
+"""certified_top_sparse_amd -- certified Top-k attention truncation on MI355X.
+
+The compute lives in libctopk.so (hand-written HIP kernels for gfx950, C ABI
+declared in include/ctopk.h).  This package holds the kernels' sources
+(csrc/), the in-tree build script (build.py) and a ctypes binding (ctopk.py)
+whose functions carry the C names.
+"""
+from .ctopk import (  # noqa: F401
+    CTOPK_BF16, CTOPK_F32, CtopkArgs, CtopkError, EXPORTED, LIB_PATH, ctopk_certify,
+    ctopk_certify_ex, ctopk_certify_logits, ctopk_last_error_string,
+    ctopk_logits_workspace_bytes, ctopk_validate, ctopk_version, ctopk_workspace_bytes,
+    default_scale, load, make_args,
+)

@@ -1,0 +1,128 @@
+// Device-side helpers shared by the libctopk kernels (gfx950 / CDNA4).
+//
+// Selection order (Abstract of "A Mathematical Theory of Top-k Sparse
+// Attention via Total Variation Distance", arXiv 2512.07647: the head H is the
+// k largest-score keys; equal scores are ordered by index ascending, the lower
+// index entering the head first) is encoded as one 64-bit integer per key:
+//
+//   key64(s, i) = ukey(s) << 32 | (0xFFFFFFFF - i)
+//
+// where ukey is the order-preserving map of an fp32 score to uint32 (-0.0 is
+// folded onto +0.0 first, so the two compare equal).  A larger key64 means
+// "earlier in the order".  All key64 values of one row are distinct, so the
+// head is exactly { i : key64(s_i, i) >= key64 of its last member }.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ctopk {
+
+constexpr int kWave = 64;
+
+// Digit schedule of the mass-weighted radix select over key64: 5 x 11 + 9 bits.
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kLevels = 6;
+
+__device__ __forceinline__ int digit_width(int level) { return level < 5 ? 11 : 9; }
+
+__device__ __forceinline__ uint32_t ukey(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;  // -0.0 -> +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float ukey_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t key64(float s, uint32_t idx) {
+  return (static_cast<uint64_t>(ukey(s)) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ uint32_t key64_index(uint64_t k) {
+  return 0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull);
+}
+
+__device__ __forceinline__ float key64_score(uint64_t k) {
+  return ukey_to_float(static_cast<uint32_t>(k >> 32));
+}
+
+// Unnormalised softmax weight w = exp(s - m) in fp32.  The rounding error of the
+// fp32 difference (s - m) is recovered exactly (two-sum) and folded back in to
+// first order, so w carries the error of one expf rather than that of expf at
+// a rounded argument.  Every kernel uses this one definition, so the
+// selection, tau and the output all see identical weights.
+__device__ __forceinline__ float weight(float s, float m) {
+  const float d = s - m;
+  const float bv = d - s;
+  const float av = d - bv;
+  const float err = (s - av) + (-m - bv);
+  const float e = expf(d);
+  return fmaf(e, err, e);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions (xor butterflies)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sums across the 64 lanes (Hillis-Steele over shuffles).
+__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    double t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Per-row scalars handed from the selection to the output kernel.
+struct RowSel {
+  float m;        // row maximum of the fp32 scores (weight reference)
+  uint32_t pad;
+  double Z;       // sum of weights over the row (fp64)
+  uint64_t thr;   // key64 of the last head member: key i is kept iff key64 >= thr
+};
+
+// Cooperative zeroing of a byte range by all blocks of a grid (16-byte units).
+__device__ __forceinline__ void zero_slice(void* base, size_t bytes, size_t block_linear,
+                                           size_t nblocks) {
+  if (base == nullptr || bytes == 0) return;
+  const size_t units = bytes / 16;
+  uint4* p = reinterpret_cast<uint4*>(base);
+  const size_t per = (units + nblocks - 1) / nblocks;
+  const size_t lo = block_linear * per;
+  size_t hi = lo + per;
+  if (hi > units) hi = units;
+  for (size_t u = lo + threadIdx.x; u < hi; u += blockDim.x) p[u] = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace ctopk

@@ -1,0 +1,157 @@
+/*
+ * libctopk -- certified Top-k attention truncation on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, per query head h (definitions from the Abstract
+ * of "A Mathematical Theory of Top-k Sparse Attention via Total Variation
+ * Distance", arXiv 2512.07647):
+ *
+ *   s_i    = scale_h * <q_h, k_i>                 for every key i in [0, n)
+ *   P      = softmax(s)                            the attention distribution
+ *   order  = keys by score descending, index ascending among equal scores
+ *   T_k    = softmax mass of the keys after the first k of that order
+ *            (= TV(P, P_hat_k), the total-variation distance between P and its
+ *            Top-k truncation)
+ *   k_eps  = min { k in 1..n : T_k <= eps }        smallest certified head
+ *   tau    = T_{k_eps}
+ *   out_h  = sum_{i in H} P_i v_i / sum_{i in H} P_i   (H = first k_eps keys),
+ *            the renormalised head-only output Attn_k(q, K, V).
+ *
+ * Conventions shared by every entry point:
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *     never frees, retains or reads them after the enqueued work completes.
+ *   - All arrays are dense and row-major.  q is [n_q_heads, d]; K and V are
+ *     [n_kv_heads, n, d]; query head h reads KV head h / (n_q_heads / n_kv_heads)
+ *     (grouped-query attention; batch is folded into the head dimensions).
+ *   - Calls are asynchronous: work is enqueued on `stream` (NULL = the default
+ *     stream) and the call returns.  No device-to-host copy, no host sync.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     return a negative ctopk_status; ctopk_last_error_string() describes the
+ *     last error of the calling thread.  A failed kernel launch returns
+ *     CTOPK_ERR_HIP.  Faults inside kernels surface at the caller's next sync.
+ *   - No C++ exception crosses this interface.
+ *   - Inputs must be finite.  NaN or infinite scores give unspecified results.
+ *   - Inputs and outputs must not alias.
+ */
+#ifndef CTOPK_H
+#define CTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define CTOPK_API __attribute__((visibility("default")))
+#else
+#define CTOPK_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t (a pointer to the runtime's stream object). */
+typedef struct ihipStream_t* ctopk_stream_t;
+
+typedef enum {
+  CTOPK_OK = 0,
+  CTOPK_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  CTOPK_ERR_SHAPE = -2,       /* n, d, head counts or their ratio are invalid    */
+  CTOPK_ERR_EPS = -3,         /* eps is not a finite number in (0, 1)           */
+  CTOPK_ERR_ALIGN = -4,       /* an input/output pointer is not 16-byte aligned  */
+  CTOPK_ERR_UNSUPPORTED = -5, /* valid request this build does not handle        */
+  CTOPK_ERR_WORKSPACE = -6,   /* caller workspace too small                      */
+  CTOPK_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed      */
+} ctopk_status;
+
+typedef enum { CTOPK_F32 = 0, CTOPK_BF16 = 1 } ctopk_dtype;
+
+/*
+ * ctopk_certify -- the decode call.
+ *
+ * q [n_q_heads, d], K [n_kv_heads, n, d], V [n_kv_heads, n, d]: bfloat16.
+ * scale_h = float(1/sqrt(d)) for every head.  d must be 64 or 128;
+ * 1 <= n <= 2^31 - 1; n_q_heads must be a multiple of n_kv_heads.
+ * Outputs: out [n_q_heads, d] float32, k_eps [n_q_heads] int32,
+ * tau [n_q_heads] float64.
+ * Scratch memory comes from a per-device workspace that the library allocates
+ * on first use and grows as needed (hipMalloc); it is shared by all calls on a
+ * device, so concurrent calls on different streams of one device race.  Use
+ * ctopk_certify_ex with a caller workspace for concurrent streams.
+ */
+CTOPK_API int ctopk_certify(const void* q, const void* K, const void* V, int64_t n, int32_t d,
+                  int32_t n_q_heads, int32_t n_kv_heads, double eps, ctopk_stream_t stream,
+                  float* out, int32_t* k_eps, double* tau);
+
+/* Full-form arguments of ctopk_certify_ex. */
+typedef struct ctopk_args {
+  const void* q;            /* [n_q_heads, d], dtype                                   */
+  const void* K;            /* [n_kv_heads, n, d], dtype                               */
+  const void* V;            /* [n_kv_heads, n, d], dtype                               */
+  int32_t dtype;            /* ctopk_dtype of q, K and V                               */
+  int64_t n;                /* keys per head, 1 .. 2^31 - 1                            */
+  int32_t d;                /* head dimension, 64 or 128                               */
+  int32_t n_q_heads;        /* query heads (query rows)                                */
+  int32_t n_kv_heads;       /* KV heads; divides n_q_heads                             */
+  double eps;               /* TV budget, finite, 0 < eps < 1                          */
+  const float* head_scale;  /* [n_q_heads] score scale per query head; NULL: 1/sqrt(d) */
+  void* workspace;          /* caller scratch (device), or NULL for the cached one     */
+  size_t workspace_bytes;   /* size of `workspace`; >= ctopk_workspace_bytes(...)      */
+  float* out;               /* [n_q_heads, d] float32                                  */
+  int32_t* k_eps;           /* [n_q_heads]                                             */
+  double* tau;              /* [n_q_heads]                                             */
+  uint32_t* sel_mask;       /* optional [n_q_heads, ceil(n/32)]: bit (i%32) of word
+                               i/32 is set iff key i is in the head set; NULL: skip   */
+  float* scores;            /* optional [n_q_heads, n] float32 scores as computed;
+                               NULL: kept in the workspace                            */
+  double* lse;              /* optional [n_q_heads] log-sum-exp of the scores; NULL    */
+} ctopk_args;
+
+/*
+ * ctopk_certify_ex -- full form of ctopk_certify: fp32 or bf16 inputs, per-head
+ * scale, caller-owned workspace, optional selection mask, scores and lse.
+ * Rows whose group size n_q_heads/n_kv_heads is >= 64 with n <= 1024 and bf16
+ * inputs run on the all-queries (encoder-shaped) path whose QK^T uses MFMA.
+ */
+CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
+
+/* Device scratch bytes ctopk_certify_ex needs for these sizes (0 on bad sizes). */
+CTOPK_API size_t ctopk_workspace_bytes(int64_t n, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t dtype);
+
+/*
+ * ctopk_certify_logits -- selection and head-only output on given logits.
+ *
+ * logits [rows, n] float32 are the scores themselves (no scale is applied).
+ * V [n_v, n, dv] (v_dtype) holds the value rows; logits row r reads V head
+ * r / (rows / n_v), so n_v must divide rows.  dv must be 64 or 128.
+ * Outputs as for ctopk_certify_ex: out [rows, dv] float32, k_eps [rows],
+ * tau [rows] float64, optional sel_mask [rows, ceil(n/32)] and lse [rows].
+ * workspace may be NULL (cached per-device workspace) or caller memory of at
+ * least ctopk_logits_workspace_bytes(...) bytes.
+ */
+CTOPK_API int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, int64_t n,
+                         int32_t dv, int32_t rows, int32_t n_v, double eps, void* workspace,
+                         size_t workspace_bytes, ctopk_stream_t stream, float* out,
+                         int32_t* k_eps, double* tau, uint32_t* sel_mask, double* lse);
+
+/* Device scratch bytes ctopk_certify_logits needs (0 on bad sizes). */
+CTOPK_API size_t ctopk_logits_workspace_bytes(int64_t n, int32_t dv, int32_t rows, int32_t n_v);
+
+/*
+ * ctopk_validate -- the host-side argument checks of ctopk_certify_ex, alone.
+ * Makes no HIP call and touches no device memory (pointers are only tested for
+ * NULL and alignment), so it runs without a GPU.  Returns CTOPK_OK or the
+ * status ctopk_certify_ex would return for these arguments.
+ */
+CTOPK_API int ctopk_validate(const ctopk_args* a);
+
+/* Text of the last error on the calling thread ("" after success). */
+CTOPK_API const char* ctopk_last_error_string(void);
+
+/* Library version string, e.g. "libctopk 0.1 gfx950". */
+CTOPK_API const char* ctopk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CTOPK_H */

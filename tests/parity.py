@@ -1,0 +1,94 @@
+"""Comparison protocol between the device path and the fp64 oracle.
+
+* k_eps must match exactly, except on rows the oracle flags near-boundary (its
+  tail mass within 1e-6 * eps of eps at k_eps or k_eps - 1); such mismatches
+  are counted and reported.
+* tau must match to 1e-5 absolute on every row whose k_eps matches.
+* out must match per row to a relative L2 tolerance (2e-3 for bf16 inputs,
+  1e-5 for fp32).  A row whose device head set differs from the oracle's
+  (fp32 scores can swap keys whose fp64 scores differ by rounding) passes if
+  every key in the symmetric difference scores within the fp32 rounding band
+  of the cut score and the oracle's output recomputed on the device's head set
+  matches; such rows are counted.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TAU_ATOL = 1e-5
+OUT_RTOL_BF16 = 2e-3
+OUT_RTOL_F32 = 1e-5
+
+
+def unpack_mask(words: np.ndarray, n: int) -> np.ndarray:
+    w = np.ascontiguousarray(words.astype(np.int32)).view(np.uint8)
+    bits = np.unpackbits(w.reshape(words.shape[0], -1), axis=1, bitorder="little")
+    return bits[:, :n].astype(bool)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b, axis=-1)
+    num = np.linalg.norm(a - b, axis=-1)
+    return num / np.maximum(den, 1e-300)
+
+
+def compare(gpu: dict, ref: dict, S: np.ndarray, V64: np.ndarray, row_to_v: np.ndarray,
+            eps: float, out_rtol: float, rows=None, score_band=None, label=""):
+    """Check device results against the oracle on the given rows.
+
+    gpu: numpy arrays k_eps, tau, out and optionally sel_mask (bool [R, n]) for
+    all rows; ref: oracle dict for the same rows (in `rows` order); S: oracle
+    fp64 scores of those rows; V64: fp64 values [Hv, n, dv]; score_band: per
+    row tolerance on scores for the tie adjudication.
+    """
+    if rows is None:
+        rows = np.arange(len(ref["k_eps"]))
+    rows = np.asarray(rows)
+    kg = gpu["k_eps"][rows].astype(np.int64)
+    kr = ref["k_eps"].astype(np.int64)
+    near = ref["near_boundary"]
+    kmis = kg != kr
+    bad_k = kmis & ~near
+    report = {"label": label, "rows": int(len(rows)), "k_mismatch_near_boundary": int((kmis & near).sum()),
+              "set_adjudicated": 0}
+    assert not bad_k.any(), (
+        f"{label}: k_eps mismatch on rows {rows[bad_k][:10]}: gpu {kg[bad_k][:10]} ref {kr[bad_k][:10]}")
+    tg = gpu["tau"][rows]
+    tdiff = np.abs(tg - ref["tau"])
+    okrow = ~kmis
+    assert (tdiff[okrow] <= TAU_ATOL).all(), (
+        f"{label}: tau off by {tdiff[okrow].max():.3e}")
+    report["tau_max_abs_err"] = float(tdiff[okrow].max()) if okrow.any() else 0.0
+    og = gpu["out"][rows]
+    err = rel_l2(og, ref["out"])
+    report["out_max_rel_l2"] = float(err[okrow].max()) if okrow.any() else 0.0
+    badout = okrow & (err > out_rtol)
+    for j in np.nonzero(badout)[0]:
+        assert "sel_mask" in gpu, f"{label}: out rel L2 {err[j]:.3e} on row {rows[j]} (no mask to adjudicate)"
+        hg = gpu["sel_mask"][rows[j]]
+        hr = ref["head_mask"][j]
+        diff = hg ^ hr
+        assert diff.any(), f"{label}: out rel L2 {err[j]:.3e} on row {rows[j]} with identical head sets"
+        band = score_band[j] if score_band is not None else 0.0
+        s = S[j]
+        assert np.all(np.abs(s[diff] - ref["s_star"][j]) <= band), (
+            f"{label}: head sets differ away from the cut on row {rows[j]}")
+        w = np.exp(s - s.max()) * hg
+        o2 = (w @ V64[row_to_v[rows[j]]]) / w.sum()
+        e2 = rel_l2(og[j], o2)
+        assert e2 <= out_rtol, f"{label}: out rel L2 {e2:.3e} on row {rows[j]} even on the device head set"
+        report["set_adjudicated"] += 1
+    if "sel_mask" in gpu:
+        hg = gpu["sel_mask"][rows]
+        assert (hg.sum(1) == kg).all(), f"{label}: mask popcount differs from k_eps"
+    return report
+
+
+def score_band(q64: np.ndarray, K64: np.ndarray, scale: float, d: int) -> float:
+    """Bound on |s_fp32 - s_fp64| over the keys of one query head for the
+    device's fp32 dot product: 4 * d * 2^-24 * |scale| * max_i sum_j |q_j k_ij|
+    (a loose Higham-style bound)."""
+    mag = np.abs(K64) @ np.abs(q64)
+    return float(4.0 * d * 2.0 ** -24 * abs(scale) * mag.max())
