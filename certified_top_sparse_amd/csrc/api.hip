@@ -1,10 +1,10 @@
 // libctopk C ABI: argument validation, workspace layout and launch sequencing.
 //
 // Decode path (ctopk_certify / ctopk_certify_ex):
-//   K1 score_scan -> hist0 (row max, level-0 histogram) -> resolve (k_eps, tau)
-//   -> vsum (w * v over the head, selection mask) -> finalize (out)
+//   score_scan (scores, per-tile min/max) -> hist0 (level-0 partial histograms)
+//   -> resolve (lse, k_eps, tau, cut key, mask) -> vsum (w * v over the head, out)
 // Logits path (ctopk_certify_logits):
-//   rowmax -> hist0 -> resolve -> vsum -> finalize
+//   resolve (including level 0) -> vsum
 // Encoder-shaped path (all queries of a head, small n): one fused kernel.
 // Every launch goes to the caller's stream; nothing is copied to the host.
 #include <math.h>
@@ -21,6 +21,25 @@
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Stage events armed by ctopk_record_stage_events for the next call.
+constexpr int kMaxStageEvents = 8;
+thread_local hipEvent_t g_stage_ev[kMaxStageEvents];
+thread_local int g_stage_n = 0;
+
+// Records the armed event for stage boundary i (if any) on stream st.
+struct StageMarks {
+  hipEvent_t ev[kMaxStageEvents];
+  int n;
+  hipStream_t st;
+  StageMarks(hipStream_t s) : n(g_stage_n), st(s) {
+    for (int i = 0; i < n; ++i) ev[i] = g_stage_ev[i];
+    g_stage_n = 0;
+  }
+  void mark(int i) {
+    if (i < n) (void)hipEventRecord(ev[i], st);
+  }
+};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -44,34 +63,32 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr int64_t kMaxN = 2147483647LL;
 constexpr int64_t kMaxElems = 1LL << 36;  // rows * n
 
-// Scratch layout shared by both paths.
+// Scratch layout shared by both paths (every region is fully written before
+// it is read within a call, so nothing needs zeroing).
 struct Layout {
-  size_t scores = 0, blkmax = 0, hcnt = 0, hmass = 0, rowsel = 0, part = 0, total = 0;
-  size_t scores_b = 0, blkmax_b = 0, hist_b = 0;
-  int nblk = 0, nchunk = 0;
+  size_t rowsel = 0, blkstat = 0, part = 0, pcnt = 0, pmass = 0;
+  size_t scores = 0, total = 0;
+  int nblk = 0, nchunk = 0, hchunk = 0;
 };
 
-Layout layout(int64_t n, int dv, int rows, int n_v, bool decode) {
+Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   Layout L;
-  L.nblk = decode ? static_cast<int>(ctopk::ceil_div(n, ctopk::kScanTile)) : ctopk::rowmax_nblk(n);
-  L.nchunk = ctopk::vsum_nchunk(n, rows, n_v);
+  L.nblk = decode ? static_cast<int>(ctopk::ceil_div(n, ctopk::kScanTile)) : 0;
+  L.nchunk = ctopk::vsum_nchunk(n, rows, n_v, v_dtype, dv);
+  L.hchunk = decode ? ctopk::hist_nchunk(n, rows) : 0;
   size_t off = 0;
-  // hcnt and hmass are contiguous so that one zeroing range clears both.
-  L.hcnt = off;
-  off += up(static_cast<size_t>(rows) * ctopk::kBins * sizeof(uint32_t));
-  L.hmass = off;
-  off += up(static_cast<size_t>(rows) * ctopk::kBins * sizeof(double));
-  L.hist_b = off;
   L.rowsel = off;
   off += up(static_cast<size_t>(rows) * sizeof(ctopk::RowSel));
-  L.blkmax = off;
-  L.blkmax_b = static_cast<size_t>(rows) * L.nblk * sizeof(float);
-  off += up(L.blkmax_b);
+  L.blkstat = off;
+  off += up(static_cast<size_t>(rows) * L.nblk * sizeof(float2));
   L.part = off;
   off += up(static_cast<size_t>(rows) * L.nchunk * (dv + 1) * sizeof(float));
+  L.pcnt = off;
+  off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(uint32_t));
+  L.pmass = off;
+  off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(double));
   L.scores = off;
-  L.scores_b = decode ? static_cast<size_t>(rows) * static_cast<size_t>(n) * sizeof(float) : 0;
-  off += up(L.scores_b);
+  off += up(decode ? static_cast<size_t>(rows) * static_cast<size_t>(n) * sizeof(float) : 0);
   L.total = off;
   return L;
 }
@@ -175,13 +192,13 @@ size_t ctopk_workspace_bytes(int64_t n, int32_t d, int32_t n_q_heads, int32_t n_
       n_q_heads % n_kv_heads != 0 || (dtype != CTOPK_F32 && dtype != CTOPK_BF16))
     return 0;
   if (ctopk::encoder_supported(dtype, d, n, n_q_heads, n_kv_heads)) return kAlign;
-  return layout(n, d, n_q_heads, n_kv_heads, true).total;
+  return layout(n, d, n_q_heads, n_kv_heads, dtype, true).total;
 }
 
 size_t ctopk_logits_workspace_bytes(int64_t n, int32_t dv, int32_t rows, int32_t n_v) {
   if (n < 1 || n > kMaxN || (dv != 64 && dv != 128) || rows < 1 || n_v < 1 || rows % n_v != 0)
     return 0;
-  return layout(n, dv, rows, n_v, false).total;
+  return layout(n, dv, rows, n_v, CTOPK_F32, false).total;
 }
 
 int ctopk_validate(const ctopk_args* a) {
@@ -191,20 +208,23 @@ int ctopk_validate(const ctopk_args* a) {
 }
 
 int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  StageMarks marks(st);  // consumes armed events even if validation fails
   int rc = validate_args(a);
   if (rc != CTOPK_OK) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const float default_scale = static_cast<float>(1.0 / sqrt(static_cast<double>(a->d)));
 
   if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads)) {
+    marks.mark(0);
     rc = hip_check(ctopk::launch_encoder(a->q, a->K, a->V, a->d, a->head_scale, default_scale,
                                          a->n, a->n_q_heads, a->n_kv_heads, a->eps, a->out,
                                          a->k_eps, a->tau, a->sel_mask, a->scores, a->lse, st),
                    "encoder launch");
+    marks.mark(1);
     return rc == CTOPK_OK ? ok() : rc;
   }
 
-  const Layout L = layout(a->n, a->d, a->n_q_heads, a->n_kv_heads, true);
+  const Layout L = layout(a->n, a->d, a->n_q_heads, a->n_kv_heads, a->dtype, true);
   char* ws = static_cast<char*>(a->workspace);
   if (ws == nullptr) {
     void* p = nullptr;
@@ -213,32 +233,36 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
     ws = static_cast<char*>(p);
   }
   float* scores = a->scores ? a->scores : reinterpret_cast<float*>(ws + L.scores);
-  float* blkmax = reinterpret_cast<float*>(ws + L.blkmax);
-  uint32_t* hcnt = reinterpret_cast<uint32_t*>(ws + L.hcnt);
-  double* hmass = reinterpret_cast<double*>(ws + L.hmass);
-  ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
+  float2* blkstat = reinterpret_cast<float2*>(ws + L.blkstat);
   float* part = reinterpret_cast<float*>(ws + L.part);
+  uint32_t* pcnt = reinterpret_cast<uint32_t*>(ws + L.pcnt);
+  double* pmass = reinterpret_cast<double*>(ws + L.pmass);
+  ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
   const int rows = a->n_q_heads;
 
+  marks.mark(0);
   rc = hip_check(ctopk::launch_score_scan(a->q, a->K, a->dtype, a->d, a->head_scale,
                                           default_scale, a->n, rows, a->n_kv_heads, scores,
-                                          blkmax, ws + L.hcnt, L.hist_b - L.hcnt, st),
+                                          blkstat, nullptr, 0, st),
                  "score_scan launch");
   if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_hist0(scores, a->n, rows, blkmax, L.nblk, rs, hcnt, hmass, st),
+  marks.mark(1);
+  rc = hip_check(ctopk::launch_hist0(scores, a->n, rows, blkstat, L.nblk, L.hchunk, pcnt, pmass,
+                                     st),
                  "hist0 launch");
   if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, hcnt, hmass, a->eps, rs, a->k_eps,
-                                       a->tau, a->lse, st),
+  marks.mark(2);
+  rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, blkstat, L.nblk, pcnt, pmass,
+                                       L.hchunk, a->eps, rs, a->k_eps, a->tau, a->lse,
+                                       a->sel_mask, nullptr, 0, st),
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;
+  marks.mark(3);
   rc = hip_check(ctopk::launch_vsum(scores, a->n, rows, a->n_kv_heads, a->V, a->dtype, a->d, rs,
-                                    part, L.nchunk, a->sel_mask, st),
+                                    part, L.nchunk, a->out, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_finalize(part, rows, L.nchunk, a->d, a->out, st),
-                 "finalize launch");
-  if (rc != CTOPK_OK) return rc;
+  marks.mark(4);
   return ok();
 }
 
@@ -266,6 +290,8 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
                          int32_t dv, int32_t rows, int32_t n_v, double eps, void* workspace,
                          size_t workspace_bytes, ctopk_stream_t stream, float* out,
                          int32_t* k_eps, double* tau, uint32_t* sel_mask, double* lse) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  StageMarks marks(st);  // consumes armed events even if validation fails
   if (!logits || !V || !out || !k_eps || !tau)
     return fail(CTOPK_ERR_NULL, "logits, V, out, k_eps and tau must be non-NULL");
   if (v_dtype != CTOPK_F32 && v_dtype != CTOPK_BF16)
@@ -283,8 +309,7 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
   if (!aligned(logits, 4) || !aligned16(V) || !aligned(out, 4) || !aligned(k_eps, 4) ||
       !aligned(tau, 8) || (sel_mask && !aligned(sel_mask, 4)) || (lse && !aligned(lse, 8)))
     return fail(CTOPK_ERR_ALIGN, "V must be 16-byte aligned and outputs element aligned");
-  const Layout L = layout(n, dv, rows, n_v, false);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Layout L = layout(n, dv, rows, n_v, v_dtype, false);
   char* ws = static_cast<char*>(workspace);
   if (ws != nullptr) {
     if (!aligned(ws, kAlign)) return fail(CTOPK_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -297,27 +322,29 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
     if (rc != CTOPK_OK) return rc;
     ws = static_cast<char*>(p);
   }
-  float* blkmax = reinterpret_cast<float*>(ws + L.blkmax);
-  uint32_t* hcnt = reinterpret_cast<uint32_t*>(ws + L.hcnt);
-  double* hmass = reinterpret_cast<double*>(ws + L.hmass);
-  ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
   float* part = reinterpret_cast<float*>(ws + L.part);
+  ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
 
-  rc = hip_check(ctopk::launch_rowmax(logits, n, rows, blkmax, ws + L.hcnt, L.hist_b - L.hcnt, st),
-                 "rowmax launch");
-  if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_hist0(logits, n, rows, blkmax, L.nblk, rs, hcnt, hmass, st),
-                 "hist0 launch");
-  if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_resolve(logits, n, rows, hcnt, hmass, eps, rs, k_eps, tau, lse, st),
+  marks.mark(0);
+  rc = hip_check(ctopk::launch_resolve(logits, n, rows, nullptr, 0, nullptr, nullptr, 0, eps, rs,
+                                       k_eps, tau, lse, sel_mask, nullptr, 0, st),
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;
+  marks.mark(1);
   rc = hip_check(ctopk::launch_vsum(logits, n, rows, n_v, V, v_dtype, dv, rs, part, L.nchunk,
-                                    sel_mask, st),
+                                    out, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_finalize(part, rows, L.nchunk, dv, out, st), "finalize launch");
-  if (rc != CTOPK_OK) return rc;
+  marks.mark(2);
+  return ok();
+}
+
+int ctopk_record_stage_events(void* const* events, int32_t count) {
+  if (count < 0 || count > kMaxStageEvents)
+    return fail(CTOPK_ERR_SHAPE, "count must be in 0..%d, got %d", kMaxStageEvents, count);
+  if (count > 0 && events == nullptr) return fail(CTOPK_ERR_NULL, "events is NULL");
+  for (int i = 0; i < count; ++i) g_stage_ev[i] = static_cast<hipEvent_t>(events[i]);
+  g_stage_n = count;
   return ok();
 }
 

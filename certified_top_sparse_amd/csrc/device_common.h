@@ -65,6 +65,48 @@ __device__ __forceinline__ float weight(float s, float m) {
 }
 
 // ---------------------------------------------------------------------------
+// DPP lane exchanges (full-rate VALU, no LDS traffic)
+// ---------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of L consecutive lanes (L a power of two <= 64);
+// on return every lane of a group holds the group's sum.  After the two quad
+// steps all lanes of a quad agree, so the mirror patterns (which pair each
+// lane with one in the other half) complete the 8- and 16-lane sums.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (L >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (L >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Maximum over the 64 lanes, returned in every lane (DPP within rows of 16,
+// then the four row results through scalar lane reads).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// ---------------------------------------------------------------------------
 // wave64 reductions (xor butterflies)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
@@ -107,10 +149,27 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
 // Per-row scalars handed from the selection to the output kernel.
 struct RowSel {
   float m;        // row maximum of the fp32 scores (weight reference)
-  uint32_t pad;
+  float lo;       // row minimum (lower edge of the level-0 value bins)
   double Z;       // sum of weights over the row (fp64)
   uint64_t thr;   // key64 of the last head member: key i is kept iff key64 >= thr
 };
+
+// Level-0 bins of the select: kBins equal-width value bins over [lo, hi].
+// lin_bin is non-decreasing in s (IEEE subtraction and multiplication by a
+// non-negative constant are monotone, as is truncation of a non-negative
+// value), so every bin holds a contiguous range of the key64 order; any such
+// partition serves the radix descent, and equal-width bins split Gaussian-like
+// scores far more evenly than the top bits of the float encoding do.
+__device__ __forceinline__ float lin_scale(float lo, float hi) {
+  const float r = hi - lo;
+  const float inv = static_cast<float>(kBins) / r;
+  return (r > 0.0f && isfinite(inv)) ? inv : 0.0f;
+}
+
+__device__ __forceinline__ int lin_bin(float s, float lo, float inv) {
+  const float x = (s - lo) * inv;
+  return x < static_cast<float>(kBins) ? static_cast<int>(x) : kBins - 1;
+}
 
 // Cooperative zeroing of a byte range by all blocks of a grid (16-byte units).
 __device__ __forceinline__ void zero_slice(void* base, size_t bytes, size_t block_linear,

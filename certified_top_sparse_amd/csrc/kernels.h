@@ -10,49 +10,50 @@
 
 namespace ctopk {
 
-// Keys per block of the score scan; per-block maxima are emitted per tile.
-constexpr int kScanTile = 256;
-// Scores per block of the first (global) histogram pass.
-constexpr int kHistChunk = 4096;
-// Keys per block of the value stream.
+// Compute units of an MI355X.
+constexpr int kNumCUs = 256;
+// Keys per tile of the score scan; per-tile (min, max) are emitted per tile.
+constexpr int kScanTile = 128;
+// Keys per tile of the value stream (8 waves x 32 keys).
 constexpr int kVsumTile = 256;
 // Largest candidate set the resolve kernel keeps in LDS.
 constexpr int kCandCap = 8192;
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// K1: scores[h, i] = scale_h * <q_h, K[h / G, i]> and blkmax[h, tile].
-// Also zeroes `zero_bytes` at `zero_base` (the histogram scratch).
+// K1: scores[h, i] = scale_h * <q_h, K[h / G, i]> and blkstat[h, tile] =
+// (min, max) over the tile.  Also zeroes `zero_bytes` at `zero_base`.
 hipError_t launch_score_scan(const void* q, const void* K, int dtype, int d,
                              const float* head_scale, float default_scale, int64_t n,
-                             int n_q, int n_kv, float* scores, float* blkmax,
+                             int n_q, int n_kv, float* scores, float2* blkstat,
                              void* zero_base, size_t zero_bytes, hipStream_t st);
 
-// Row maxima of given logits, per chunk of keys: blkmax[row, chunk].
-int rowmax_nblk(int64_t n);
-hipError_t launch_rowmax(const float* logits, int64_t n, int rows, float* blkmax,
-                         void* zero_base, size_t zero_bytes, hipStream_t st);
+// Level 0 of the select for the decode path, many blocks per row: row
+// (min, max) from blkstat, weights w = exp(s - max), and a (count, fp64 mass)
+// histogram over kBins equal-width value bins on [min, max] per chunk of keys,
+// written to pcnt / pmass [rows, hist_nchunk, kBins].
+int hist_nchunk(int64_t n, int rows);
+hipError_t launch_hist0(const float* scores, int64_t n, int rows, const float2* blkstat,
+                        int nblk, int nchunk, uint32_t* pcnt, double* pmass, hipStream_t st);
 
-// Pass 1 of the select: row max m from blkmax, weights w = exp(s - m), and the
-// top-digit (count, mass) histogram of every row, merged with global atomics.
-hipError_t launch_hist0(const float* scores, int64_t n, int rows, const float* blkmax,
-                        int nblk, RowSel* rs, uint32_t* hcnt, double* hmass, hipStream_t st);
+// Select, one workgroup per row: level-0 histogram from the hist0 partials (or,
+// with npart == 0, from a pass over the row, after a (min, max) pass when
+// blkstat is NULL), then the radix levels.  Writes k_eps, tau, lse (optional),
+// sel_mask (optional) and RowSel.  Also zeroes `zero_bytes` at `zero_base`.
+hipError_t launch_resolve(const float* scores, int64_t n, int rows, const float2* blkstat,
+                          int nblk, const uint32_t* pcnt, const double* pmass, int npart,
+                          double eps, RowSel* rs, int32_t* k_eps, double* tau, double* lse,
+                          uint32_t* sel_mask, void* zero_base, size_t zero_bytes,
+                          hipStream_t st);
 
-// Remaining select levels, one workgroup per row: k_eps, tau, lse, thr.
-hipError_t launch_resolve(const float* scores, int64_t n, int rows, const uint32_t* hcnt,
-                          const double* hmass, double eps, RowSel* rs, int32_t* k_eps,
-                          double* tau, double* lse, hipStream_t st);
-
-// Number of key chunks the value stream splits each row into.
-int vsum_nchunk(int64_t n, int rows, int n_v);
-// K4: per-chunk partial sums of w * v over kept keys, and the selection mask.
+// Blocks per group (nchunk) and groups of the value stream.
+int vsum_groups(int rows, int n_v, int v_dtype, int dv);
+int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv);
+// K4: w * v over kept keys into part [rows, nchunk, dv + 1] (numerator and
+// weight sum per block), then a finalize kernel writes out = num / den.
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                       int v_dtype, int dv, const RowSel* rs, float* part, int nchunk,
-                       uint32_t* sel_mask, hipStream_t st);
-
-// Combine the per-chunk partials (fp64, fixed order) into out = num / den.
-hipError_t launch_finalize(const float* part, int rows, int nchunk, int dv, float* out,
-                           hipStream_t st);
+                       int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
+                       hipStream_t st);
 
 // Encoder-shaped path (all queries of a head, n <= 1024, bf16, MFMA QK^T).
 hipError_t launch_encoder(const void* q, const void* K, const void* V, int d,

@@ -3,8 +3,8 @@
 // Computes s_i = scale_h * <q_h, k_i> for every key i of a KV head and every
 // query head h of its group (the scores whose softmax is P in the Abstract of
 // "A Mathematical Theory of Top-k Sparse Attention via Total Variation
-// Distance", arXiv 2512.07647), and the maximum score of each tile of
-// kScanTile keys.
+// Distance", arXiv 2512.07647), and the (minimum, maximum) score of each tile
+// of kScanTile keys.
 //
 // Memory plan (HBM-bound: one K row of d*esize bytes feeds G dot products):
 //   * every K row is read from HBM exactly once per group of up to 8 query
@@ -13,9 +13,14 @@
 //     fully coalesced);
 //   * each lane keeps the matching 16-byte slice of every q_h in registers;
 //     bf16 pairs use v_dot2_f32_bf16 (products exact in fp32, fp32 sum);
-//   * the LPR partial dots are combined by an xor butterfly, the scores are
-//     staged in LDS and written out coalesced ([n_q_heads, n] fp32, 4*G bytes
-//     per key against d*esize bytes of K read).
+//   * one short block per tile (thousands of blocks, all loads of a wave
+//     issued before any arithmetic, no branch around a load), so blocks in
+//     different phases keep HBM busy;
+//   * the LPR partial dots are combined by DPP butterflies (full-rate VALU,
+//     no LDS round trips), the scores are staged in LDS and written out
+//     coalesced ([n_q_heads, n] fp32, 4*G bytes per key against d*esize bytes
+//     of K read);
+
 #include "kernels.h"
 
 namespace ctopk {
@@ -57,24 +62,22 @@ struct Slice<float> {
   }
 };
 
-template <typename T, int D, int GB>
+// One block per tile of kScanTile keys of one KV head and up to GB query
+// heads: 4 waves, each covering kScanTile / 4 keys with all of its K loads
+// issued before any arithmetic.
+template <typename T, int D, int GB, bool HS>
 __global__ __launch_bounds__(256) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ K, const float* __restrict__ head_scale,
     float default_scale, int64_t n, int G, int nblk, float* __restrict__ scores,
-    float* __restrict__ blkmax, void* zero_base, size_t zero_bytes) {
+    float2* __restrict__ blkstat, void* zero_base, size_t zero_bytes) {
   constexpr int EPL = Slice<T>::kElems;
   constexpr int LPR = D / EPL;
   constexpr int RPW = kWave / LPR;
   constexpr int WAVES = 4;
   constexpr int ITER = kScanTile / (WAVES * RPW);
   static_assert(GB <= LPR, "one lane per head within a row group");
+  static_assert(kScanTile % kWave == 0, "tile is a whole number of waves");
   __shared__ float s_sc[GB][kScanTile];
-  __shared__ float s_red[GB][WAVES];
-
-  const size_t nblocks = static_cast<size_t>(gridDim.x) * gridDim.y * gridDim.z;
-  const size_t blin =
-      (static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-  zero_slice(zero_base, zero_bytes, blin, nblocks);
 
   const int tile = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -84,110 +87,113 @@ __global__ __launch_bounds__(256) void score_scan_kernel(
   const int rg = lane / LPR;
   const int h0 = kvh * G + blockIdx.z * GB;
   const int nh = min(GB, G - static_cast<int>(blockIdx.z) * GB);
+  const int64_t tile0 = static_cast<int64_t>(tile) * kScanTile;
+  const int lbase = wave * (ITER * RPW);
 
+  // K rows first: they carry the block's HBM latency.  Rows past n re-read
+  // row n-1 (their scores are never written), so the loads are unconditional.
+  const T* Kb = K + static_cast<size_t>(kvh) * static_cast<size_t>(n) * D;
+  uint4 kv[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int64_t r = min(tile0 + lbase + it * RPW + rg, n - 1);
+    kv[it] = *reinterpret_cast<const uint4*>(Kb + r * D + seg * EPL);
+  }
+  // q slices (head slots past nh repeat the last head and are never written).
   uint4 qv[GB];
   float sc[GB];
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
-    if (j < nh) {
-      qv[j] = *reinterpret_cast<const uint4*>(q + static_cast<size_t>(h0 + j) * D + seg * EPL);
-      sc[j] = head_scale ? head_scale[h0 + j] : default_scale;
+    const int hj = h0 + min(j, nh - 1);
+    qv[j] = *reinterpret_cast<const uint4*>(q + static_cast<size_t>(hj) * D + seg * EPL);
+    if constexpr (HS) {
+      sc[j] = head_scale[hj];
     } else {
-      qv[j] = make_uint4(0, 0, 0, 0);
-      sc[j] = 0.0f;
+      sc[j] = default_scale;
     }
   }
+  zero_slice(zero_base, zero_bytes,
+             (static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x,
+             static_cast<size_t>(gridDim.x) * gridDim.y * gridDim.z);
 
-  const T* Kb = K + static_cast<size_t>(kvh) * static_cast<size_t>(n) * D;
-  const int64_t tile0 = static_cast<int64_t>(tile) * kScanTile;
-  const int lbase = wave * (ITER * RPW);
-
-  uint4 kv[ITER];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int64_t r = tile0 + lbase + it * RPW + rg;
-    kv[it] = make_uint4(0, 0, 0, 0);
-    if (r < n) kv[it] = *reinterpret_cast<const uint4*>(Kb + r * D + seg * EPL);
-  }
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    float acc[GB];
-#pragma unroll
-    for (int j = 0; j < GB; ++j) acc[j] = Slice<T>::dot(kv[it], qv[j]);
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) {
-#pragma unroll
-      for (int j = 0; j < GB; ++j) acc[j] += __shfl_xor(acc[j], o, kWave);
-    }
     const int lr = lbase + it * RPW + rg;
 #pragma unroll
-    for (int j = 0; j < GB; ++j)
-      if (seg == j) s_sc[j][lr] = acc[j] * sc[j];
+    for (int j = 0; j < GB; ++j) {
+      const float acc = group_sum<LPR>(Slice<T>::dot(kv[it], qv[j]));
+      if (seg == j) s_sc[j][lr] = acc * sc[j];
+    }
   }
   __syncthreads();
 
-  const int64_t i = tile0 + threadIdx.x;
+  // Wave w writes heads w, w + 4, ...: coalesced score stores and the tile's
+  // (min, max) for that head.
+  for (int j = wave; j < nh; j += WAVES) {
+    float vmax = -INFINITY, vmin = INFINITY;
+    float* srow = scores + static_cast<size_t>(h0 + j) * static_cast<size_t>(n);
 #pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    float v = -INFINITY;
-    if (j < nh && i < n) {
-      v = s_sc[j][threadIdx.x];
-      scores[static_cast<size_t>(h0 + j) * static_cast<size_t>(n) + i] = v;
+    for (int k = lane; k < kScanTile; k += kWave) {
+      const int64_t i = tile0 + k;
+      if (i < n) {
+        const float v = s_sc[j][k];
+        srow[i] = v;
+        vmax = fmaxf(vmax, v);
+        vmin = fminf(vmin, v);
+      }
     }
-    v = wave_max(v);
-    if (lane == 0) s_red[j][wave] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < nh) {
-    const int j = threadIdx.x;
-    float v = s_red[j][0];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) v = fmaxf(v, s_red[j][w]);
-    blkmax[static_cast<size_t>(h0 + j) * nblk + tile] = v;
+    vmax = wave_max_dpp(vmax);
+    vmin = -wave_max_dpp(-vmin);
+    if (lane == 0) blkstat[static_cast<size_t>(h0 + j) * nblk + tile] = make_float2(vmin, vmax);
   }
 }
 
 template <typename T, int D, int GB>
 hipError_t launch_t(const void* q, const void* K, const float* head_scale, float default_scale,
-                    int64_t n, int n_q, int n_kv, float* scores, float* blkmax, void* zb,
+                    int64_t n, int n_q, int n_kv, float* scores, float2* blkstat, void* zb,
                     size_t zbytes, hipStream_t st) {
   const int G = n_q / n_kv;
   const int nblk = static_cast<int>(ceil_div(n, kScanTile));
   dim3 grid(nblk, n_kv, static_cast<unsigned>(ceil_div(G, GB)));
-  hipLaunchKernelGGL((score_scan_kernel<T, D, GB>), grid, dim3(256), 0, st,
-                     static_cast<const T*>(q), static_cast<const T*>(K), head_scale,
-                     default_scale, n, G, nblk, scores, blkmax, zb, zbytes);
+  if (head_scale != nullptr)
+    hipLaunchKernelGGL((score_scan_kernel<T, D, GB, true>), grid, dim3(256), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(K), head_scale,
+                       default_scale, n, G, nblk, scores, blkstat, zb, zbytes);
+  else
+    hipLaunchKernelGGL((score_scan_kernel<T, D, GB, false>), grid, dim3(256), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(K), head_scale,
+                       default_scale, n, G, nblk, scores, blkstat, zb, zbytes);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_d(const void* q, const void* K, const float* hs, float ds, int64_t n, int n_q,
-                    int n_kv, float* scores, float* blkmax, void* zb, size_t zbytes,
+                    int n_kv, float* scores, float2* bs, void* zb, size_t zbytes,
                     hipStream_t st) {
   const int G = n_q / n_kv;
-  if (G == 1) return launch_t<T, D, 1>(q, K, hs, ds, n, n_q, n_kv, scores, blkmax, zb, zbytes, st);
-  if (G == 2) return launch_t<T, D, 2>(q, K, hs, ds, n, n_q, n_kv, scores, blkmax, zb, zbytes, st);
-  if (G <= 4) return launch_t<T, D, 4>(q, K, hs, ds, n, n_q, n_kv, scores, blkmax, zb, zbytes, st);
-  return launch_t<T, D, 8>(q, K, hs, ds, n, n_q, n_kv, scores, blkmax, zb, zbytes, st);
+  if (G == 1) return launch_t<T, D, 1>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
+  if (G == 2) return launch_t<T, D, 2>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
+  if (G <= 4) return launch_t<T, D, 4>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
+  return launch_t<T, D, 8>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
 }
 
 }  // namespace
 
 hipError_t launch_score_scan(const void* q, const void* K, int dtype, int d,
                              const float* head_scale, float default_scale, int64_t n, int n_q,
-                             int n_kv, float* scores, float* blkmax, void* zero_base,
+                             int n_kv, float* scores, float2* blkstat, void* zero_base,
                              size_t zero_bytes, hipStream_t st) {
   if (dtype == 1) {
     if (d == 128)
       return launch_d<uint16_t, 128>(q, K, head_scale, default_scale, n, n_q, n_kv, scores,
-                                     blkmax, zero_base, zero_bytes, st);
-    return launch_d<uint16_t, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkmax,
+                                     blkstat, zero_base, zero_bytes, st);
+    return launch_d<uint16_t, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
                                   zero_base, zero_bytes, st);
   }
   if (d == 128)
-    return launch_d<float, 128>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkmax,
+    return launch_d<float, 128>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
                                 zero_base, zero_bytes, st);
-  return launch_d<float, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkmax,
+  return launch_d<float, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
                              zero_base, zero_bytes, st);
 }
 

@@ -6,15 +6,20 @@
 //
 // where H_h = { i : key64(s_i, i) >= thr_h } comes from the select.
 //
-// Memory plan (HBM-bound): a block owns kVsumTile keys of one V head and up to
-// 8 query heads of its group.  A prologue (one thread per key, coalesced score
-// reads) evaluates membership and the weight of every (key, head) pair once,
-// writes the selection mask with wave ballots and stages the weights in LDS.
-// The main loop streams only V rows kept by at least one head of the group
-// (the union of the group's heads), each row read once with 16-byte loads by
-// LPR consecutive lanes, and accumulates w * v for every head.  Partial sums
-// per block go to scratch and are combined in fp64, in a fixed order, by
-// finalize_kernel (so results are bitwise reproducible).
+// Memory plan (HBM-bound).  A block of 8 waves owns up to 8 query heads of one
+// V head and `tpb` consecutive tiles of kVsumTile keys; each wave streams its
+// 32 keys of a tile on its own, with no block barrier inside the stream:
+//   * the V rows and the scores of a wave's keys are loaded together (each V
+//     row once, 16-byte loads by LPR consecutive lanes), so the stream never
+//     waits on a score read or on any other dependent load; keys outside a
+//     head's set get weight 0 (on these workloads the union of a group's head
+//     sets covers nearly every key, so loading every row costs little);
+//   * each (key, head) weight is computed once, by one lane, and staged in a
+//     wave-private LDS slot from which the LPR lanes of the row read all G
+//     weights;
+//   * w * v is accumulated for every head in registers.
+// Block sums go to per-(head, block) partials, and finalize_kernel adds them
+// in block order in fp64 and writes out, so results are bitwise reproducible.
 #include "kernels.h"
 
 namespace ctopk {
@@ -58,24 +63,32 @@ struct AccOf<float> {
   using type = double;
 };
 
+constexpr int kVsumThreads = 512;
+
+
+// Heads per block: 8, except fp32 values at d = 128, whose fp64 block sums
+// would not fit LDS for 8 heads.
+template <typename T, int D>
+constexpr int kGroupMax = (sizeof(typename AccOf<T>::type) == 8 && D == 128) ? 4 : 8;
+constexpr int kVsumWaves = kVsumThreads / kWave;
+
 template <typename T, int D, int GB>
-__global__ __launch_bounds__(256) void vsum_kernel(const float* __restrict__ scores, int64_t n,
-                                                   int G, const T* __restrict__ V,
-                                                   const RowSel* __restrict__ rs,
-                                                   float* __restrict__ part, int nchunk,
-                                                   int tpb, uint32_t* __restrict__ sel_mask,
-                                                   int64_t nwords) {
+__global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
+    const float* __restrict__ scores, int64_t n, int G, const T* __restrict__ V,
+    const RowSel* __restrict__ rs, float* __restrict__ part, int nchunk, int tpb) {
   using Acc = typename AccOf<T>::type;
   constexpr int EPL = VSlice<T>::kElems;
   constexpr int LPR = D / EPL;
   constexpr int RPW = kWave / LPR;
-  constexpr int WAVES = 4;
-  constexpr int NRG = WAVES * RPW;  // row groups per block
-  constexpr int ITER = kVsumTile / NRG;
-  __shared__ float s_w[GB][kVsumTile];
-  __shared__ uint32_t s_any[kVsumTile];
-  __shared__ Acc s_red[WAVES][GB * D];
-  __shared__ double s_wsum[GB][WAVES];
+  constexpr int PASS = kVsumTile / kVsumWaves;  // keys per wave per tile
+  constexpr int ITER = PASS / RPW;              // rows per lane per tile
+  constexpr int NPAIR = PASS * GB;              // (key, head) weights per wave per tile
+  constexpr int PPL = (NPAIR + kWave - 1) / kWave;  // weights per lane
+  static_assert(kVsumTile % (kVsumWaves * RPW) == 0, "whole rows per lane");
+  static_assert(GB <= LPR && kWave % GB == 0, "head groups tile the wave");
+  __shared__ Acc s_red[kVsumWaves][GB * D];
+  __shared__ double s_wsum[kVsumWaves][GB];
+  __shared__ float s_w[kVsumWaves][PASS][GB];  // wave-private weight staging
 
   const int chunk = blockIdx.x;
   const int vh = blockIdx.y;
@@ -87,74 +100,81 @@ __global__ __launch_bounds__(256) void vsum_kernel(const float* __restrict__ sco
   const int seg = lane % LPR;
   const int rg = lane / LPR;
   const T* Vb = V + static_cast<size_t>(vh) * static_cast<size_t>(n) * D;
+
+  // Weights are computed once per (key, head): pair p = lane + 64 * u covers
+  // key p / GB and head p % GB, so each lane always works for head lane % GB.
+  // That head's selection parameters are read with block-uniform addresses.
+  const int hw = lane % GB;
+  uint64_t thr = ~0ull;
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < GB; ++j) {
+    const RowSel r = rs[h0 + min(j, nh - 1)];
+    if (hw == j) {
+      thr = j < nh ? r.thr : ~0ull;
+      m = r.m;
+    }
+  }
+  const float* srow = scores + static_cast<size_t>(h0 + min(hw, nh - 1)) * static_cast<size_t>(n);
+
   Acc acc[GB][EPL];
 #pragma unroll
   for (int j = 0; j < GB; ++j)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = Acc(0);
-  double wsum[GB];
-#pragma unroll
-  for (int j = 0; j < GB; ++j) wsum[j] = 0.0;
+  double wsum = 0.0;  // weight of head hw over this lane's pairs
 
   for (int tb = 0; tb < tpb; ++tb) {
-    const int64_t tile0 = (static_cast<int64_t>(chunk) * tpb + tb) * kVsumTile;
-    if (tile0 >= n) break;
-    // Prologue: membership and weights, one thread per key.
-    {
-      const int64_t i = tile0 + t;
-      uint32_t any = 0u;
+    const int64_t p0 = (static_cast<int64_t>(chunk) * tpb + tb) * kVsumTile + wave * PASS;
+    if (p0 >= n) break;  // uniform per wave; waves do not synchronise in this loop
+    // Value rows and the pass's scores, issued together (rows past n re-read
+    // row n-1 and get weight 0).
+    uint4 u[ITER];
 #pragma unroll
-      for (int j = 0; j < GB; ++j) {
-        float w = 0.0f;
-        bool kept = false;
-        if (j < nh && i < n) {
-          const float s = scores[static_cast<size_t>(h0 + j) * static_cast<size_t>(n) + i];
-          const RowSel r = rs[h0 + j];
-          kept = key64(s, static_cast<uint32_t>(i)) >= r.thr;
-          if (kept) w = weight(s, r.m);
-        }
-        any |= kept ? 1u : 0u;
-        s_w[j][t] = w;
-        wsum[j] += static_cast<double>(w);
-        if (sel_mask != nullptr && j < nh) {
-          const uint64_t b = __ballot(kept);
-          const int64_t w0 = (tile0 + wave * kWave) / 32;
-          uint32_t* mrow = sel_mask + static_cast<size_t>(h0 + j) * static_cast<size_t>(nwords);
-          if (lane == 0 && w0 < nwords) mrow[w0] = static_cast<uint32_t>(b);
-          if (lane == 1 && w0 + 1 < nwords) mrow[w0 + 1] = static_cast<uint32_t>(b >> 32);
-        }
-      }
-      s_any[t] = any;
-    }
-    __syncthreads();
-
-    // Main loop: stream the union of kept V rows.
-#pragma unroll 4
     for (int it = 0; it < ITER; ++it) {
-      const int lr = it * NRG + wave * RPW + rg;
-      if (s_any[lr] != 0u) {
-        const int64_t r = tile0 + lr;
-        const uint4 u = *reinterpret_cast<const uint4*>(Vb + r * D + seg * EPL);
-        float v[EPL];
-        VSlice<T>::load(u, v);
+      const int64_t r = min(p0 + it * RPW + rg, n - 1);
+      u[it] = *reinterpret_cast<const uint4*>(Vb + r * D + seg * EPL);
+    }
+    float s[PPL];
 #pragma unroll
-        for (int j = 0; j < GB; ++j) {
-          const Acc w = static_cast<Acc>(s_w[j][lr]);
+    for (int q = 0; q < PPL; ++q) {
+      const int key = (lane + kWave * q) / GB;
+      s[q] = srow[min(p0 + min(key, PASS - 1), n - 1)];
+    }
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[j][e] += w * static_cast<Acc>(v[e]);
-        }
+    for (int q = 0; q < PPL; ++q) {
+      const int pair = lane + kWave * q;
+      if (pair < NPAIR) {
+        const int key = pair / GB;
+        const int64_t r = p0 + key;
+        const bool kept = r < n && key64(s[q], static_cast<uint32_t>(r)) >= thr;
+        const float w = kept ? weight(s[q], m) : 0.0f;
+        wsum += static_cast<double>(w);
+        s_w[wave][key][hw] = w;
       }
     }
-    __syncthreads();
-  }
+    // s_w is private to this wave, and one wave's LDS operations complete in
+    // order, so a wavefront-scope fence (which only stops the compiler from
+    // moving the reads above the writes) is all the ordering needed.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    const double ws = wave_sum(wsum[j]);
-    if (lane == 0) s_wsum[j][wave] = ws;
+    for (int it = 0; it < ITER; ++it) {
+      const int key = it * RPW + rg;
+      float wj[GB];
+#pragma unroll
+      for (int j = 0; j < GB; ++j) wj[j] = s_w[wave][key][j];
+      float v[EPL];
+      VSlice<T>::load(u[it], v);
+#pragma unroll
+      for (int j = 0; j < GB; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] += static_cast<Acc>(wj[j]) * static_cast<Acc>(v[e]);
+    }
   }
 
-  // Combine the RPW row groups of each wave (xor butterfly over lane / LPR),
-  // then the waves through LDS, always in the same order.
+  // Block sums: row groups of a wave (xor butterfly over lane / LPR), then the
+  // waves in order through LDS.
 #pragma unroll
   for (int o = LPR; o < kWave; o <<= 1) {
 #pragma unroll
@@ -162,100 +182,137 @@ __global__ __launch_bounds__(256) void vsum_kernel(const float* __restrict__ sco
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], o, kWave);
   }
+#pragma unroll
+  for (int o = GB; o < kWave; o <<= 1) wsum += __shfl_xor(wsum, o, kWave);
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < GB; ++j)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) s_red[wave][j * D + seg * EPL + e] = acc[j][e];
   }
+  if (lane < GB) s_wsum[wave][lane] = wsum;
   __syncthreads();
-
-  for (int idx = t; idx < GB * D; idx += blockDim.x) {
-    const int j = idx / D;
+  const size_t pstride = static_cast<size_t>(D + 1);
+  for (int idx = t; idx < GB * (D + 1); idx += kVsumThreads) {
+    const int j = idx / (D + 1);
+    const int e = idx - j * (D + 1);
     if (j < nh) {
-      const int e = idx - j * D;
-      Acc sum = Acc(0);
+      double sum = 0.0;
+      if (e < D) {
 #pragma unroll
-      for (int g = 0; g < WAVES; ++g) sum += s_red[g][idx];
-      part[(static_cast<size_t>(h0 + j) * nchunk + chunk) * (D + 1) + e] =
-          static_cast<float>(sum);
+        for (int g = 0; g < kVsumWaves; ++g) sum += static_cast<double>(s_red[g][j * D + e]);
+      } else {
+#pragma unroll
+        for (int g = 0; g < kVsumWaves; ++g) sum += s_wsum[g][j];
+      }
+      part[(static_cast<size_t>(h0 + j) * nchunk + chunk) * pstride + e] = static_cast<float>(sum);
     }
   }
-  if (t < nh) {
-    double ws = 0.0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) ws += s_wsum[t][w];
-    part[(static_cast<size_t>(h0 + t) * nchunk + chunk) * (D + 1) + D] = static_cast<float>(ws);
-  }
+
 }
 
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ part, int nchunk,
-                                                       int dv, float* __restrict__ out) {
-  __shared__ double s_den;
+// out[h, e] = sum_c part[h, c, e] / sum_c part[h, c, dv], fp64 sums in a fixed
+// order: thread (k, e) adds chunks k, k + NK, ... and the NK partial sums are
+// then added in k order.  Runs as its own kernel so that the kernel boundary
+// makes every block's partials visible (an in-kernel device-scope fence costs
+// a full L2 writeback and invalidate per block on this multi-XCD part).
+__global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict__ part,
+                                                        int nchunk, int dv,
+                                                        float* __restrict__ out) {
+  __shared__ double s_col[1024];
   const int row = blockIdx.x;
-  const int e = threadIdx.x;
-  double acc = 0.0;
-  if (e <= dv) {
-    const float* p = part + static_cast<size_t>(row) * nchunk * (dv + 1) + e;
-    for (int c = 0; c < nchunk; ++c) acc += static_cast<double>(p[static_cast<size_t>(c) * (dv + 1)]);
+  const int t = threadIdx.x;
+  const int cols = dv + 1;
+  const int NK = 1024 / cols;
+  const int k = t / cols;
+  const int e = t - k * cols;
+  double a = 0.0;
+  if (k < NK) {
+    const float* p = part + static_cast<size_t>(row) * nchunk * cols + e;
+    for (int c0 = k; c0 < nchunk; c0 += 8 * NK) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = min(c0 + u * NK, nchunk - 1);
+        v[u] = p[static_cast<size_t>(c) * cols];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u * NK < nchunk) a += static_cast<double>(v[u]);
+    }
   }
-  if (e == dv) s_den = acc;
+  s_col[t] = a;
   __syncthreads();
-  if (e < dv) out[static_cast<size_t>(row) * dv + e] = static_cast<float>(acc / s_den);
+  if (t < dv) {
+    double num = 0.0, den = 0.0;
+    for (int j = 0; j < NK; ++j) {
+      num += s_col[j * cols + t];
+      den += s_col[j * cols + dv];
+    }
+    out[static_cast<size_t>(row) * dv + t] = static_cast<float>(num / den);
+  }
 }
 
 template <typename T, int D, int GB>
 hipError_t launch_t(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                    const RowSel* rs, float* part, int nchunk, uint32_t* sel_mask,
-                    hipStream_t st) {
+                    const RowSel* rs, float* part, int nchunk, float* out, hipStream_t st) {
   const int G = rows / n_v;
   const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
   dim3 grid(nchunk, n_v, static_cast<unsigned>(ceil_div(G, GB)));
-  hipLaunchKernelGGL((vsum_kernel<T, D, GB>), grid, dim3(256), 0, st, scores, n, G,
-                     static_cast<const T*>(V), rs, part, nchunk, tpb, sel_mask, ceil_div(n, 32));
+  hipLaunchKernelGGL((vsum_kernel<T, D, GB>), grid, dim3(kVsumThreads), 0, st, scores, n, G,
+                     static_cast<const T*>(V), rs, part, nchunk, tpb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(finalize_kernel, dim3(rows), dim3(1024), 0, st, part, nchunk, D, out);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                    const RowSel* rs, float* part, int nchunk, uint32_t* sel_mask,
-                    hipStream_t st) {
+                    const RowSel* rs, float* part, int nchunk, float* out, hipStream_t st) {
   const int G = rows / n_v;
-  if (G == 1) return launch_t<T, D, 1>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
-  if (G == 2) return launch_t<T, D, 2>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
-  if (G <= 4) return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
-  return launch_t<T, D, 8>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
+  if (G == 1) return launch_t<T, D, 1>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+  if (G == 2) return launch_t<T, D, 2>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+  if constexpr (kGroupMax<T, D> == 4) {
+    return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+  } else {
+    if (G <= 4) return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+    return launch_t<T, D, 8>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                       int v_dtype, int dv, const RowSel* rs, float* part, int nchunk,
-                       uint32_t* sel_mask, hipStream_t st) {
+                       int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
+                       hipStream_t st) {
   if (v_dtype == 1) {
-    if (dv == 128) return launch_d<uint16_t, 128>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
-    return launch_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
+    if (dv == 128)
+      return launch_d<uint16_t, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+    return launch_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
   }
-  if (dv == 128) return launch_d<float, 128>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
-  return launch_d<float, 64>(scores, n, rows, n_v, V, rs, part, nchunk, sel_mask, st);
+  if (dv == 128) return launch_d<float, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+  return launch_d<float, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
 }
 
-int vsum_nchunk(int64_t n, int rows, int n_v) {
-  // Enough blocks to fill the chip (~4096), few enough partial sums to keep
-  // their traffic small next to the value rows.
-  const int64_t tiles = ceil_div(n, kVsumTile);
+int vsum_groups(int rows, int n_v, int v_dtype, int dv) {
   const int G = rows / n_v;
-  const int64_t zb = ceil_div(G, 8);
-  const int64_t base = tiles * n_v * zb;
-  int64_t tpb = 1;
-  while (tpb < 256 && base / (tpb * 2) >= 4096) tpb *= 2;
-  return static_cast<int>(ceil_div(tiles, tpb));
+  const int gmax = (v_dtype == 0 && dv == 128) ? 4 : 8;
+  const int gb = G == 1 ? 1 : (G == 2 ? 2 : (G <= 4 ? 4 : gmax));
+  return n_v * static_cast<int>(ceil_div(G, gb));
 }
 
-hipError_t launch_finalize(const float* part, int rows, int nchunk, int dv, float* out,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(rows), dim3(256), 0, st, part, nchunk, dv, out);
-  return hipGetLastError();
+int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
+  // Blocks per group: one per tile up to 128, so a short row is read by many
+  // blocks at once; beyond that blocks take several tiles, which keeps the
+  // partial sums (and the final combine) small.
+  (void)rows;
+  (void)n_v;
+  (void)v_dtype;
+  (void)dv;
+  const int64_t tiles = ceil_div(n, kVsumTile);
+  const int64_t tpb = ceil_div(tiles, 128);
+  return static_cast<int>(ceil_div(tiles, tpb));
 }
 
 }  // namespace ctopk

@@ -37,7 +37,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "ctopk_certify", "ctopk_certify_ex", "ctopk_workspace_bytes", "ctopk_certify_logits",
     "ctopk_logits_workspace_bytes", "ctopk_validate", "ctopk_last_error_string",
-    "ctopk_version",
+    "ctopk_version", "ctopk_record_stage_events",
 )
 
 
@@ -83,6 +83,9 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(
             f"libctopk.so not found at {path}; build it with "
             "`python -m certified_top_sparse_amd.build` (no CPU fallback exists)")
+    # Import torch first: its bundled HIP runtime (soname libamdhip64.so.7) is
+    # then the one libctopk binds to, so streams and memory are shared.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i32, i64, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                              ctypes.c_double, ctypes.c_size_t)
@@ -103,6 +106,8 @@ def load(path: str = LIB_PATH):
     lib.ctopk_last_error_string.restype = ctypes.c_char_p
     lib.ctopk_version.argtypes = []
     lib.ctopk_version.restype = ctypes.c_char_p
+    lib.ctopk_record_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.ctopk_record_stage_events.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -156,6 +161,13 @@ def ctopk_workspace_bytes(n, d, n_q_heads, n_kv_heads, dtype=CTOPK_BF16) -> int:
 
 def ctopk_logits_workspace_bytes(n, dv, rows, n_v) -> int:
     return int(load().ctopk_logits_workspace_bytes(n, dv, rows, n_v))
+
+
+def ctopk_record_stage_events(events) -> None:
+    """Arm the calling thread's next certify call to record the given raw
+    hipEvent_t handles (ints) at its stage boundaries."""
+    arr = (ctypes.c_void_p * max(1, len(events)))(*[ctypes.c_void_p(e) for e in events])
+    _check(load().ctopk_record_stage_events(arr, len(events)))
 
 
 def ctopk_validate(args: CtopkArgs) -> int:

@@ -144,6 +144,23 @@ CTOPK_API size_t ctopk_logits_workspace_bytes(int64_t n, int32_t dv, int32_t row
  */
 CTOPK_API int ctopk_validate(const ctopk_args* a);
 
+/*
+ * ctopk_record_stage_events -- instrumentation for benchmarks and profilers.
+ *
+ * Arms the calling thread so that its NEXT ctopk_certify, ctopk_certify_ex or
+ * ctopk_certify_logits call records events[i] (hipEvent_t handles created by
+ * the caller, count <= 8) on its stream at the path's stage boundaries, then
+ * disarms.  Decode path: [0] before the score scan, [1] after it, [2] after
+ * the level-0 histogram, [3] after the rest of the select, [4] after the value
+ * stream and its output combine.  Logits path: [0] before the select, [1]
+ * after it, [2] after the value stream and its output combine.
+ * Encoder-shaped path: [0] before and [1] after its fused kernel.
+ * Boundaries past `count` are not recorded.
+ * Recording adds no work to the kernels themselves.  Returns CTOPK_OK, or
+ * CTOPK_ERR_SHAPE for count outside 0..8 (count 0 disarms).
+ */
+CTOPK_API int ctopk_record_stage_events(void* const* events, int32_t count);
+
 /* Text of the last error on the calling thread ("" after success). */
 CTOPK_API const char* ctopk_last_error_string(void);
 
