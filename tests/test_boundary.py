@@ -1,0 +1,177 @@
+"""The C ABI boundary on the host: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching a GPU.  CPU only:
+ctopk_validate and the workspace-size functions make no HIP call, and the
+certify entry points check their arguments before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import certified_top_sparse_amd as ct
+from certified_top_sparse_amd import ctopk as cb
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "ctopk.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cb.LIB_PATH):
+        pytest.skip("libctopk.so not built")
+    return cb.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"CTOPK_API\s+[\w\s\*]+?\b(ctopk_\w+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert sorted(cb.EXPORTED) == declared_functions()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # nothing internal leaks out of the shared object
+    out = os.popen(f"nm -D --defined-only {cb.LIB_PATH}").read()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(declared_functions())
+
+
+def test_version_string(lib):
+    assert ct.ctopk_version().startswith("libctopk")
+
+
+A16 = 1 << 20  # a fake 16-byte-aligned device address (validate never dereferences it)
+
+
+def good_args(**kw):
+    a = cb.CtopkArgs()
+    a.q, a.K, a.V = A16, A16 * 2, A16 * 3
+    a.dtype = cb.CTOPK_BF16
+    a.n, a.d, a.n_q_heads, a.n_kv_heads = 32768, 128, 32, 8
+    a.eps = 0.01
+    a.out, a.k_eps, a.tau = A16 * 4, A16 * 5, A16 * 6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_valid_arguments_pass(lib):
+    assert ct.ctopk_validate(good_args()) == cb.CTOPK_OK
+    assert ct.ctopk_last_error_string() == ""
+
+
+@pytest.mark.parametrize("field", ["q", "K", "V", "out", "k_eps", "tau"])
+def test_null_pointers(lib, field):
+    assert ct.ctopk_validate(good_args(**{field: None})) == cb.CTOPK_ERR_NULL
+    assert "NULL" in ct.ctopk_last_error_string()
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"n": 0}, cb.CTOPK_ERR_SHAPE),
+    ({"n": -5}, cb.CTOPK_ERR_SHAPE),
+    ({"n": 2 ** 31}, cb.CTOPK_ERR_SHAPE),
+    ({"d": 96}, cb.CTOPK_ERR_SHAPE),
+    ({"d": 256}, cb.CTOPK_ERR_SHAPE),
+    ({"n_q_heads": 0}, cb.CTOPK_ERR_SHAPE),
+    ({"n_kv_heads": 0}, cb.CTOPK_ERR_SHAPE),
+    ({"n_q_heads": 30, "n_kv_heads": 8}, cb.CTOPK_ERR_SHAPE),
+    ({"n_q_heads": 70000, "n_kv_heads": 70000}, cb.CTOPK_ERR_UNSUPPORTED),
+    ({"n": 2 ** 31 - 1, "n_q_heads": 64, "n_kv_heads": 8}, cb.CTOPK_ERR_UNSUPPORTED),
+    ({"dtype": 7}, cb.CTOPK_ERR_UNSUPPORTED),
+])
+def test_shape_errors(lib, kw, code):
+    assert ct.ctopk_validate(good_args(**kw)) == code
+    assert ct.ctopk_last_error_string() != ""
+
+
+@pytest.mark.parametrize("eps", [0.0, 1.0, -0.5, 1.5, math.nan, math.inf, -math.inf])
+def test_eps_errors(lib, eps):
+    assert ct.ctopk_validate(good_args(eps=eps)) == cb.CTOPK_ERR_EPS
+
+
+@pytest.mark.parametrize("field,value", [("q", A16 + 8), ("K", A16 + 2), ("V", A16 + 4),
+                                         ("out", A16 + 2), ("tau", A16 + 4),
+                                         ("k_eps", A16 + 1)])
+def test_alignment_errors(lib, field, value):
+    assert ct.ctopk_validate(good_args(**{field: value})) == cb.CTOPK_ERR_ALIGN
+
+
+def test_workspace_checks(lib):
+    need = ct.ctopk_workspace_bytes(32768, 128, 32, 8, cb.CTOPK_BF16)
+    assert need > 32 * 32768 * 4  # at least the score buffer
+    assert ct.ctopk_validate(good_args(workspace=A16 * 8, workspace_bytes=need)) == cb.CTOPK_OK
+    assert ct.ctopk_validate(good_args(workspace=A16 * 8, workspace_bytes=need - 1)) == \
+        cb.CTOPK_ERR_WORKSPACE
+    assert ct.ctopk_validate(good_args(workspace=A16 * 8 + 16, workspace_bytes=need)) == \
+        cb.CTOPK_ERR_ALIGN
+
+
+def test_workspace_sizes(lib):
+    assert ct.ctopk_workspace_bytes(0, 128, 32, 8) == 0
+    assert ct.ctopk_workspace_bytes(100, 96, 32, 8) == 0
+    assert ct.ctopk_workspace_bytes(100, 128, 30, 8) == 0
+    a = ct.ctopk_workspace_bytes(1000, 128, 32, 8)
+    b = ct.ctopk_workspace_bytes(100000, 128, 32, 8)
+    assert 0 < a < b
+    assert ct.ctopk_workspace_bytes(4096, 64, 1, 1, cb.CTOPK_F32) > 0
+    assert ct.ctopk_logits_workspace_bytes(4096, 64, 1024, 1) > 0
+    assert ct.ctopk_logits_workspace_bytes(4096, 100, 1024, 1) == 0
+    assert ct.ctopk_logits_workspace_bytes(4096, 64, 1000, 3) == 0
+
+
+def test_certify_rejects_before_any_gpu_call(lib):
+    vp = ctypes.c_void_p
+    rc = lib.ctopk_certify(vp(A16), vp(A16), vp(A16), 0, 128, 32, 8, 0.01, None, vp(A16),
+                           vp(A16), vp(A16))
+    assert rc == cb.CTOPK_ERR_SHAPE
+    rc = lib.ctopk_certify(None, vp(A16), vp(A16), 100, 128, 32, 8, 0.01, None, vp(A16),
+                           vp(A16), vp(A16))
+    assert rc == cb.CTOPK_ERR_NULL
+    rc = lib.ctopk_certify(vp(A16), vp(A16), vp(A16), 100, 128, 32, 8, 2.0, None, vp(A16),
+                           vp(A16), vp(A16))
+    assert rc == cb.CTOPK_ERR_EPS
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"logits": None}, cb.CTOPK_ERR_NULL),
+    ({"n": 0}, cb.CTOPK_ERR_SHAPE),
+    ({"dv": 32}, cb.CTOPK_ERR_SHAPE),
+    ({"rows": 10, "n_v": 3}, cb.CTOPK_ERR_SHAPE),
+    ({"eps": 0.0}, cb.CTOPK_ERR_EPS),
+    ({"v_dtype": 5}, cb.CTOPK_ERR_UNSUPPORTED),
+    ({"V": A16 + 4}, cb.CTOPK_ERR_ALIGN),
+    ({"workspace": A16, "workspace_bytes": 16}, cb.CTOPK_ERR_WORKSPACE),
+])
+def test_logits_argument_errors(lib, kw, code):
+    args = {"logits": A16, "V": A16, "v_dtype": cb.CTOPK_F32, "n": 4096, "dv": 64, "rows": 8,
+            "n_v": 1, "eps": 0.01, "workspace": None, "workspace_bytes": 0}
+    args.update(kw)
+    vp = ctypes.c_void_p
+    p = (lambda x: None if x is None else vp(x))
+    rc = lib.ctopk_certify_logits(p(args["logits"]), p(args["V"]), args["v_dtype"], args["n"],
+                                  args["dv"], args["rows"], args["n_v"], args["eps"],
+                                  p(args["workspace"]), args["workspace_bytes"], None, vp(A16),
+                                  vp(A16), vp(A16), None, None)
+    assert rc == code
+
+
+def test_stage_event_arming_limits(lib):
+    arr = (ctypes.c_void_p * 9)()
+    assert lib.ctopk_record_stage_events(arr, 9) == cb.CTOPK_ERR_SHAPE
+    assert lib.ctopk_record_stage_events(None, 3) == cb.CTOPK_ERR_NULL
+    assert lib.ctopk_record_stage_events(None, 0) == cb.CTOPK_OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = cb._lib
+    cb._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="no CPU fallback"):
+            cb.load(str(tmp_path / "nope.so"))
+    finally:
+        cb._lib = saved
