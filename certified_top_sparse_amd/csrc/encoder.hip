@@ -1,17 +1,571 @@
-// Encoder-shaped path: all queries of a head against n <= 1024 keys.
+// Encoder-shaped path: every query row of a head against all n <= 512 keys of
+// that head, bf16 inputs (dense QK^T on MFMA).
+//
+// What is computed follows the Abstract of "A Mathematical Theory of Top-k
+// Sparse Attention via Total Variation Distance" (arXiv 2512.07647): per query
+// row s_i = scale * q.k_i, the head is the k largest-score keys (equal scores:
+// lower index first), k_eps is the smallest k whose discarded softmax mass is
+// at most eps, tau is that mass, and the output is the softmax average of V
+// over the head, renormalised over the head.
+//
+// One workgroup = 4 wavefronts = 64 query rows of one KV head.  Per wave: 16
+// query rows; lane (r, g) = (lane % 16, lane / 16) holds row r and the keys
+// 16 t + 4 g + e (t < NT tiles, e < 4), which is the fp32 result layout of a
+// 16x16x32 bf16 MFMA computing S^T = K Q^T.  A row's scores therefore live in
+// four lanes, 4 NT registers each, and never leave registers.
+//
+//  1. S^T = K Q^T on MFMA; K is staged through LDS in chunks that the four
+//     waves share.
+//  2. Per row: max and min, weights w = exp(s - max), Z; then the certified
+//     cut by a mass-weighted bin descent: fp64 LDS histograms of weight mass
+//     over 64 bins per row (equal-width value bins first, bins over the
+//     order-preserving integer encoding of the score below that), each level
+//     keeping the one bin that holds the cut.  It ends exactly, either by
+//     pairwise key comparison once a row has <= 32 candidates, or by index
+//     rank when all remaining candidates share one score.
+//  3. out^T = V^T P^T on MFMA, V staged transposed through LDS.  P holds the
+//     head weights split into bf16 high and low parts, so the products carry
+//     about 16 bits of weight precision; accumulation is fp32.
+#include "device_common.h"
 #include "kernels.h"
 
 namespace ctopk {
+namespace {
 
-bool encoder_supported(int dtype, int d, int64_t n, int n_q, int n_kv) {
-  (void)dtype; (void)d; (void)n; (void)n_q; (void)n_kv;
-  return false;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kEncWaves = 4;
+constexpr int kEncThreads = kEncWaves * kWave;
+constexpr int kEncRows = 16 * kEncWaves;  // query rows per workgroup
+constexpr int kEncMaxKeys = 512;
+constexpr int kEncMinGroup = 64;
+constexpr int kEncBins = 64;              // bins per row and level
+constexpr int kHistStride = kEncBins + 1; // doubles per histogram row (bank padding)
+constexpr int kLaneCand = 12;             // candidate slots per lane
+constexpr int kFinishMax = 32;            // exact finish at or below this many candidates
+// Every level below the first drops at least one candidate, so n levels suffice.
+constexpr int kMaxLevels = 2 * kEncMaxKeys;
+
+struct WaveSel {  // per-wave scratch of the select phase
+  double hist[16 * kHistStride];
+  uint64_t key[kWave * kLaneCand];
+  float w[kWave * kLaneCand];
+};
+constexpr int kEncSmem = kEncWaves * static_cast<int>(sizeof(WaveSel));
+
+template <int D>
+struct Geo {
+  static constexpr int kChunk = D == 64 ? 128 : 64;  // keys per staged chunk
+  static constexpr int kKStride = D + 8;              // bf16 per staged K row
+  static constexpr int kVStride = kChunk + 8;         // bf16 per staged V^T row (one feature)
+  static constexpr int kTiles = kChunk / 16;          // 16-key tiles per chunk
+};
+static_assert(Geo<64>::kChunk * Geo<64>::kKStride * 2 <= kEncSmem, "K stage");
+static_assert(64 * Geo<64>::kVStride * 2 <= kEncSmem, "V stage");
+static_assert(Geo<128>::kChunk * Geo<128>::kKStride * 2 <= kEncSmem, "K stage");
+static_assert(128 * Geo<128>::kVStride * 2 <= kEncSmem, "V stage");
+
+// Reductions over the four lanes (r, 0..3) of a row.
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  return fmaxf(v, __shfl_xor(v, 32, kWave));
+}
+__device__ __forceinline__ float row_min(float v) {
+  v = fminf(v, __shfl_xor(v, 16, kWave));
+  return fminf(v, __shfl_xor(v, 32, kWave));
+}
+__device__ __forceinline__ double row_sum(double v) {
+  v += __shfl_xor(v, 16, kWave);
+  return v + __shfl_xor(v, 32, kWave);
+}
+__device__ __forceinline__ int row_sum(int v) {
+  v += __shfl_xor(v, 16, kWave);
+  return v + __shfl_xor(v, 32, kWave);
+}
+__device__ __forceinline__ uint32_t row_or(uint32_t v) {
+  v |= __shfl_xor(v, 16, kWave);
+  return v | __shfl_xor(v, 32, kWave);
 }
 
-hipError_t launch_encoder(const void*, const void*, const void*, int, const float*, float, int64_t,
-                          int, int, double, float*, int32_t*, double*, uint32_t*, float*, double*,
-                          hipStream_t) {
-  return hipErrorNotSupported;
+// LDS writes of one lane become visible to the other lanes of its wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Bin of a score at one level.  Both forms are non-decreasing in s, so every
+// bin holds a contiguous range of the key order.  fmaxf also maps the -inf of
+// absent keys (weight 0) to bin 0.
+__device__ __forceinline__ int value_bin(float s, float lo, float inv) {
+  const float x = fmaxf((s - lo) * inv, 0.0f);
+  return x < static_cast<float>(kEncBins) ? static_cast<int>(x) : kEncBins - 1;
+}
+__device__ __forceinline__ int ukey_bin(float s, uint32_t ulo, float inv) {
+  const float x = static_cast<float>(ukey(s) - ulo) * inv;
+  return x < static_cast<float>(kEncBins) ? static_cast<int>(x) : kEncBins - 1;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int D, int NT>
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void encoder_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ head_scale, float default_scale,
+    int n, int G, double eps, float* __restrict__ out, int32_t* __restrict__ k_eps,
+    double* __restrict__ tau, uint32_t* __restrict__ sel_mask, float* __restrict__ scores_out,
+    double* __restrict__ lse) {
+  using Gm = Geo<D>;
+  constexpr int kChunks = NT / Gm::kTiles;
+  static_assert(NT % Gm::kTiles == 0, "tiles per chunk");
+  __shared__ __align__(16) unsigned char smem[kEncSmem];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y;
+  const int qr = blockIdx.x * kEncRows + wave * 16 + r;
+  const bool row_ok = qr < G;
+  const int64_t row = static_cast<int64_t>(h) * G + (row_ok ? qr : G - 1);
+  const float scale = head_scale ? head_scale[row] : default_scale;
+  const uint16_t* Kh = K + static_cast<size_t>(h) * n * D;
+  const uint16_t* Vh = V + static_cast<size_t>(h) * n * D;
+  // Key 16 t + 4 g + e exists iff 16 t + e < nl; tests against nl compare a
+  // constant with one register instead of materialising 4 NT key indices.
+  int nl = n - 4 * g;
+
+  // ---- 1. scores: S^T tile t = K[16t .. 16t+15] Q^T, lane (r, g) gets keys 16t + 4g + e
+  bf16x8_t qf[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    qf[c] = as_bf16x8(*reinterpret_cast<const uint4*>(q + row * D + 32 * c + 8 * g));
+
+  float s[NT][4];
+  float mx = -INFINITY, mn = INFINITY;  // lane-local, over existing keys
+  int nlq = nl;
+  // Opaque copy: the existence masks stay local to this phase instead of being
+  // kept (4 NT scalar register pairs) for later tests of the same condition.
+  asm volatile("" : "+v"(nlq));
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+  for (int cb = 0; cb < kChunks; ++cb) {
+    if (cb * Gm::kChunk >= n) {  // chunk wholly past the last key (uniform)
+#pragma unroll
+      for (int tt = 0; tt < Gm::kTiles; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[cb * Gm::kTiles + tt][e] = -INFINITY;
+      continue;
+    }
+    if (cb > 0) __syncthreads();
+    constexpr int kUnits = Gm::kChunk * D / 8;  // 16-byte units per chunk
+#pragma unroll
+    for (int u0 = 0; u0 < kUnits; u0 += kEncThreads) {
+      const int u = u0 + tid, rr = u / (D / 8), c8 = u % (D / 8);
+      const int src = min(cb * Gm::kChunk + rr, n - 1);
+      *reinterpret_cast<uint4*>(Ks + rr * Gm::kKStride + c8 * 8) =
+          *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(src) * D + c8 * 8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < Gm::kTiles; ++tt) {
+      const int t = cb * Gm::kTiles + tt;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const bf16x8_t a = as_bf16x8(
+            *reinterpret_cast<const uint4*>(Ks + (tt * 16 + r) * Gm::kKStride + 32 * c + 8 * g));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool live = 16 * t + e < nlq;
+        s[t][e] = live ? acc[e] * scale : -INFINITY;
+        mx = fmaxf(mx, s[t][e]);
+        mn = live ? fminf(mn, s[t][e]) : mn;
+      }
+    }
+  }
+  __syncthreads();  // the K stage is reused as select scratch
+
+  // ---- 2. the certified cut, per row
+  WaveSel& ws = reinterpret_cast<WaveSel*>(smem)[wave];
+  mx = row_max(mx);
+  mn = row_min(mn);
+
+  double* hrow = ws.hist + r * kHistStride;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) hrow[16 * g + j] = 0.0;
+  wave_lds_sync();
+  // Level 0: Z and the mass histogram over equal-width value bins on [mn, mx].
+  const float vrng = mx - mn;
+  float vinv = static_cast<float>(kEncBins) / vrng;
+  vinv = (vrng > 0.0f && isfinite(vinv)) ? vinv : 0.0f;
+  // Scores more than 200 below the maximum have weight 0 in fp32 (exp
+  // underflows below -104), so clamping there changes no weight; it maps the
+  // -inf of absent keys to weight 0 without a branch.
+  const float wfloor = mx - 200.0f;
+  double Z = 0.0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = s[t][e];
+      const float w = weight(fmaxf(v, wfloor), mx);
+      Z += static_cast<double>(w);
+      atomicAdd(hrow + value_bin(v, mn, vinv), static_cast<double>(w));
+    }
+  Z = row_sum(Z);
+  const double thr = eps * Z;
+
+  bool active = true;
+  double P = 0.0;            // mass of the keys below the current interval
+  float ilo = mn, ihi = mx;  // closed score interval known to hold the cut key
+  uint64_t cut = 0;
+  double R = 0.0;
+  uint64_t* klist = ws.key + lane * kLaneCand;
+  float* wlist = ws.w + lane * kLaneCand;
+
+  for (int level = 0; level < kMaxLevels; ++level) {
+    // Opaque to the optimiser: keeps per-key values derived from s (weights,
+    // encodings) from being hoisted out of the level loop into 4 NT extra
+    // registers each.
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(s[t][e]));
+    const uint32_t ulo = ukey(ilo);
+    float uinv = 0.0f;
+    if (level > 0) {  // histogram of the interval over bins of the integer encoding
+      uinv = static_cast<float>(kEncBins) /
+             (static_cast<float>(ukey(ihi) - ulo) + 1.0f);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) hrow[16 * g + j] = 0.0;
+      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = s[t][e];
+          if (active && v >= ilo && v <= ihi)
+            atomicAdd(hrow + ukey_bin(v, ulo, uinv), static_cast<double>(weight(v, mx)));
+        }
+    }
+    wave_lds_sync();
+
+    // The bin holding the cut: the largest b whose mass below is <= thr.
+    double hl[16], S = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      hl[j] = hrow[16 * g + j];
+      S += hl[j];
+    }
+    const double S0 = __shfl(S, r, kWave), S1 = __shfl(S, r + 16, kWave),
+                 S2 = __shfl(S, r + 32, kWave);
+    double Pc = P;
+    if (g > 0) Pc += S0;
+    if (g > 1) Pc += S1;
+    if (g > 2) Pc += S2;
+    int best = -1;
+    double bestP = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (Pc <= thr) {
+        best = 16 * g + j;
+        bestP = Pc;
+      }
+      Pc += hl[j];
+    }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const int ob = __shfl_xor(best, off, kWave);
+      const double oP = __shfl_xor(bestP, off, kWave);
+      if (ob > best) {
+        best = ob;
+        bestP = oP;
+      }
+    }
+
+    // Candidates: the keys of that bin.
+    int kofs = 4 * g;
+    asm volatile("" : "+v"(kofs));  // recomputed per use, not held per key
+    int cnt = 0;
+    float cmn = INFINITY, cmx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = s[t][e];
+        if (active && v >= ilo && v <= ihi &&
+            (level == 0 ? value_bin(v, mn, vinv) : ukey_bin(v, ulo, uinv)) == best) {
+          if (cnt < kLaneCand) klist[cnt] = key64(v, static_cast<uint32_t>(kofs + 16 * t + e));
+          ++cnt;
+          cmn = fminf(cmn, v);
+          cmx = fmaxf(cmx, v);
+        }
+      }
+    const int ctot = row_sum(cnt);
+    const int over = row_sum(cnt > kLaneCand ? 1 : 0);
+    cmn = row_min(cmn);
+    cmx = row_max(cmx);
+    const bool fin_list = active && over == 0 && ctot <= kFinishMax;
+    const bool fin_eq = active && !fin_list && cmn == cmx;
+
+    // Exact finish on <= 32 candidates: the cut is the largest candidate key
+    // whose strictly smaller keys carry mass <= thr.
+    if (fin_list) {
+      for (int y = 0; y < cnt; ++y) wlist[y] = weight(key64_score(klist[y]), mx);
+    }
+    // Equal scores: the candidates differ only in index; rank by index.
+    uint32_t* bm = reinterpret_cast<uint32_t*>(ws.key + r * kLaneCand);  // 16 words per row
+    if (fin_eq) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bm[4 * g + j] = 0u;
+    }
+    wave_lds_sync();
+    if (fin_list) {
+      int ng[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) ng[gg] = __shfl(cnt, r + 16 * gg, kWave);
+      uint64_t bk = 0;
+      double bR = 0.0;
+      for (int j = 0; j < cnt; ++j) {
+        const uint64_t kj = klist[j];
+        double ml = 0.0;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const uint64_t* ko = ws.key + (r + 16 * gg) * kLaneCand;
+          const float* wo = ws.w + (r + 16 * gg) * kLaneCand;
+          for (int y = 0; y < ng[gg]; ++y)
+            if (ko[y] < kj) ml += static_cast<double>(wo[y]);
+        }
+        const double Pm = bestP + ml;
+        if (Pm <= thr && kj > bk) {
+          bk = kj;
+          bR = Pm;
+        }
+      }
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const uint64_t ok = __shfl_xor(bk, off, kWave);
+        const double oR = __shfl_xor(bR, off, kWave);
+        if (ok > bk) {
+          bk = ok;
+          bR = oR;
+        }
+      }
+      cut = bk;
+      R = bR;
+    }
+    if (fin_eq) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 4 * g + 16 * t + e;
+          if (s[t][e] == cmn) atomicOr(bm + (key >> 5), 1u << (key & 31));
+        }
+    }
+    wave_lds_sync();
+    if (fin_eq) {
+      // The tail takes the tied candidates from the highest index down; j of
+      // them fit under thr beside the mass below, so the cut is the one of
+      // rank j counted from the highest index.
+      const double wc = static_cast<double>(weight(cmn, mx));
+      int j = ctot - 1;
+      if (wc > 0.0) {
+        const double qj = floor((thr - bestP) / wc);
+        j = qj < static_cast<double>(ctot - 1) ? static_cast<int>(qj) : ctot - 1;
+        if (j < 0) j = 0;
+        while (j + 1 < ctot && bestP + (j + 1) * wc <= thr) ++j;
+        while (j > 0 && bestP + j * wc > thr) --j;
+      }
+      int idx = 0;
+      if (g == 0) {
+        int rem = j;
+        for (int wd = 15; wd >= 0; --wd) {
+          uint32_t word = bm[wd];
+          const int c = __popc(word);
+          if (rem < c) {
+            for (int b = 0; b < 32; ++b) {
+              const int hb = 31 - __clz(word);
+              if (rem == 0) {
+                idx = 32 * wd + hb;
+                break;
+              }
+              word &= ~(1u << hb);
+              --rem;
+            }
+            break;
+          }
+          rem -= c;
+        }
+      }
+      idx = __shfl(idx, r, kWave);
+      cut = key64(cmn, static_cast<uint32_t>(idx));
+      R = bestP + j * wc;
+    }
+    if (active && !fin_list && !fin_eq) {  // descend into the bin
+      P = bestP;
+      ilo = cmn;
+      ihi = cmx;
+    }
+    active = active && !fin_list && !fin_eq;
+    if (__ballot(active) == 0) break;
+  }
+  const bool failed = active;  // not reached: each level drops a candidate
+
+  // ---- 3. head-only output: out^T = V^T P^T over the head keys
+  __syncthreads();  // select scratch is reused as the V^T stage
+  const float cs = key64_score(cut);
+  const int cil = static_cast<int>(key64_index(cut)) - 4 * g;  // head iff s > cs or (s == cs and 16 t + e <= cil)
+  const uint32_t gbit = 1u << (4 * g);
+  const int nw = (n + 31) >> 5;
+  f32x4_t acc[D / 16];
+#pragma unroll
+  for (int f = 0; f < D / 16; ++f) acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  double den = 0.0;
+  int kc = 0;
+  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+  for (int cb = 0; cb < kChunks; ++cb) {
+    if (cb * Gm::kChunk >= n) break;  // uniform
+    if (cb > 0) __syncthreads();
+    // Stage V rows [cb * kChunk, +kChunk) as V^T: two keys per 32-bit word.
+    constexpr int kOct = D / 8;
+    constexpr int kItems = (Gm::kChunk / 2) * kOct;
+#pragma unroll
+    for (int i0 = 0; i0 < kItems; i0 += kEncThreads) {
+      const int it = i0 + tid, fo = it % kOct, kp = it / kOct;
+      const int k0 = min(cb * Gm::kChunk + 2 * kp, n - 1);
+      const int k1 = min(cb * Gm::kChunk + 2 * kp + 1, n - 1);
+      const uint4 a = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(k0) * D + 8 * fo);
+      const uint4 b = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(k1) * D + 8 * fo);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + (8 * fo) * Gm::kVStride + 2 * kp);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        dst[(2 * f) * (Gm::kVStride / 2)] = (av[f] & 0xFFFFu) | (bv[f] << 16);
+        dst[(2 * f + 1) * (Gm::kVStride / 2)] = (av[f] >> 16) | (bv[f] & 0xFFFF0000u);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < Gm::kTiles / 2; ++st) {
+      const int t0 = cb * Gm::kTiles + 2 * st;
+      uint32_t ph[4], pl[4];
+      uint32_t bits = 0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          uint32_t hp = 0, lp = 0;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float v = s[t0 + half][e + k];
+            const bool head = v > cs || (v == cs && 16 * (t0 + half) + e + k <= cil);
+            const float w = head ? weight(v, mx) : 0.0f;
+            den += static_cast<double>(w);
+            kc += head ? 1 : 0;
+            bits |= head ? (gbit << (16 * half + e + k)) : 0u;
+            const __bf16 wh = static_cast<__bf16>(w);
+            const __bf16 wl = static_cast<__bf16>(w - static_cast<float>(wh));
+            hp |= static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wh)) << (16 * k);
+            lp |= static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wl)) << (16 * k);
+          }
+          ph[2 * half + e / 2] = hp;
+          pl[2 * half + e / 2] = lp;
+        }
+      const bf16x8_t bh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      const bf16x8_t bl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+      for (int f = 0; f < D / 16; ++f) {
+        const uint16_t* vr = Vt + (16 * f + r) * Gm::kVStride + 32 * st + 4 * g;
+        const uint2 lo2 = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi2 = *reinterpret_cast<const uint2*>(vr + 16);
+        const bf16x8_t av = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[f], 0, 0, 0);
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[f], 0, 0, 0);
+      }
+      if (sel_mask) {
+        bits = row_or(bits);
+        const int wd = cb * (Gm::kTiles / 2) + st;
+        if (row_ok && g == 0 && wd < nw) sel_mask[row * nw + wd] = bits;
+      }
+    }
+  }
+  den = row_sum(den);
+  kc = row_sum(kc);
+
+  if (!row_ok) return;
+  const float invd = static_cast<float>(1.0 / den);
+#pragma unroll
+  for (int f = 0; f < D / 16; ++f) {
+    const float4 o = make_float4(acc[f][0] * invd, acc[f][1] * invd, acc[f][2] * invd,
+                                 acc[f][3] * invd);
+    *reinterpret_cast<float4*>(out + row * D + 16 * f + 4 * g) = o;
+  }
+  if (g == 0) {
+    k_eps[row] = failed ? -1 : kc;
+    tau[row] = R / Z;
+    if (lse) lse[row] = static_cast<double>(mx) + log(Z);
+  }
+  if (scores_out) {
+    float* srow = scores_out + row * n + 4 * g;
+    asm volatile("" : "+v"(nl));
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (16 * t + e < nl) srow[16 * t + e] = s[t][e];
+      }
+  }
+}
+
+template <int D, int NT>
+hipError_t launch_t(const void* q, const void* K, const void* V, const float* head_scale,
+                    float default_scale, int n, int G, int n_kv, double eps, float* out,
+                    int32_t* k_eps, double* tau, uint32_t* sel_mask, float* scores, double* lse,
+                    hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(G, kEncRows)), static_cast<unsigned>(n_kv));
+  hipLaunchKernelGGL((encoder_kernel<D, NT>), grid, dim3(kEncThreads), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(V), head_scale, default_scale, n, G, eps, out,
+                     k_eps, tau, sel_mask, scores, lse);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const void* q, const void* K, const void* V, const float* head_scale,
+                    float default_scale, int n, int G, int n_kv, double eps, float* out,
+                    int32_t* k_eps, double* tau, uint32_t* sel_mask, float* scores, double* lse,
+                    hipStream_t st) {
+  if (n <= 128)
+    return launch_t<D, 8>(q, K, V, head_scale, default_scale, n, G, n_kv, eps, out, k_eps, tau,
+                          sel_mask, scores, lse, st);
+  if (n <= 256)
+    return launch_t<D, 16>(q, K, V, head_scale, default_scale, n, G, n_kv, eps, out, k_eps,
+                           tau, sel_mask, scores, lse, st);
+  return launch_t<D, 32>(q, K, V, head_scale, default_scale, n, G, n_kv, eps, out, k_eps, tau,
+                         sel_mask, scores, lse, st);
+}
+
+}  // namespace
+
+bool encoder_supported(int dtype, int d, int64_t n, int n_q, int n_kv) {
+  return dtype == 1 && (d == 64 || d == 128) && n >= 1 && n <= kEncMaxKeys && n_kv >= 1 &&
+         n_q % n_kv == 0 && n_q / n_kv >= kEncMinGroup;
+}
+
+hipError_t launch_encoder(const void* q, const void* K, const void* V, int d,
+                          const float* head_scale, float default_scale, int64_t n, int n_q,
+                          int n_kv, double eps, float* out, int32_t* k_eps, double* tau,
+                          uint32_t* sel_mask, float* scores, double* lse, hipStream_t st) {
+  if (!encoder_supported(1, d, n, n_q, n_kv)) return hipErrorInvalidValue;
+  const int G = n_q / n_kv;
+  if (d == 64)
+    return launch_d<64>(q, K, V, head_scale, default_scale, static_cast<int>(n), G, n_kv, eps,
+                        out, k_eps, tau, sel_mask, scores, lse, st);
+  return launch_d<128>(q, K, V, head_scale, default_scale, static_cast<int>(n), G, n_kv, eps, out,
+                       k_eps, tau, sel_mask, scores, lse, st);
 }
 
 }  // namespace ctopk
