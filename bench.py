@@ -12,8 +12,9 @@ of K and V, above the 256 MB Infinity Cache) so that K and V come from HBM.
 
 Prints one JSON line.  `value` is query-heads/s; the roofline block is for
 the dominant kernel (the score scan): algorithmic bytes = the K bytes of one
-call divided by its average duration, timed live with HIP events recorded by
-the library at its stage boundaries inside the timed region.
+call divided by its average duration, timed live with HIP events that the
+library attaches to each kernel's dispatch (ctopk_record_kernel_events), over
+the same rotating steps as the headline loop.
 """
 from __future__ import annotations
 
@@ -37,7 +38,9 @@ import workloads  # noqa: E402
 
 METRIC = "certified top-k decode query-heads/s + achieved HBM GB/s (% peak), n=32K GQA"
 PEAK_HBM_GBPS = 8000.0
-STAGES = ("score_scan", "histogram", "select", "value_stream")
+# Kernels of one decode call, in launch order (score scan, level-0 histogram,
+# select, value stream, output combine).
+KERNELS = ("score_scan", "hist0", "resolve", "vsum", "finalize")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_scan_gqa_decode_n32768_pmc.md")
 SCAN_SOURCE = os.path.join(ROOT, "certified_top_sparse_amd", "csrc", "score_scan.hip")
 
@@ -153,6 +156,78 @@ def read_traffic():
     return d.get("traffic_bytes_per_dispatch")
 
 
+def encoder_leg(lib, ct, torch, hip, steps, eps, sets=16):
+    """All-queries (encoder-shaped) workload: batch 8, 12 heads, 512 queries and
+    512 keys per head, d = 64, bf16, per-head temperature; every query row of a
+    head is one certified row.  Rotates over `sets` input sets (16 x 18.9 MB,
+    above the 256 MB Infinity Cache).  Returns per-call time and rates."""
+    wls = [workloads.encoder(rotation=r) for r in range(sets)]
+    w0 = wls[0]
+    n, d, n_q, n_kv = w0["n"], w0["d"], w0["n_q_heads"], w0["n_kv_heads"]
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    ins = [(dev(w["q"]), dev(w["K"]), dev(w["V"]), dev(w["head_scale"])) for w in wls]
+    out = torch.empty((n_q, d), dtype=torch.float32, device="cuda")
+    k_eps = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    tau = torch.empty(n_q, dtype=torch.float64, device="cuda")
+    args = [ct.make_args(q, K, V, eps, head_scale=hs, out=out, k_eps=k_eps, tau=tau)
+            for (q, K, V, hs) in ins]
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lib.ctopk_certify_ex
+
+    def step(i):
+        rc = call(ctypes.byref(args[i % sets]), sptr)
+        if rc != 0:
+            raise RuntimeError(ct.ctopk_last_error_string())
+
+    kmean = []
+    for i in range(sets):
+        step(i)
+        torch.cuda.synchronize()
+        kmean.append(float(k_eps.double().mean().item()))
+    for i in range(20):
+        step(i)
+    # kernel duration: an event pair attached to each call's one kernel
+    pairs = [(hip.event(), hip.event()) for _ in range(steps)]
+    arrs = [(ctypes.c_void_p * 2)(ctypes.c_void_p(a), ctypes.c_void_p(b)) for a, b in pairs]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        lib.ctopk_record_kernel_events(arrs[i], 2)
+        step(i)
+    torch.cuda.synchronize()
+    kern_us = float(np.mean([hip.elapsed_ms(a, b) for a, b in pairs])) * 1e3
+    for a, b in pairs:
+        hip.destroy(a)
+        hip.destroy(b)
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), sptr)
+    for i in range(steps):
+        step(i)
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), sptr)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    in_bytes = 3 * n_kv * n * d * 2
+    qk_flops = 2.0 * n_kv * (n_q // n_kv) * n * d
+    return {"workload": "encoder batch 8 x 12 heads, 512 queries x 512 keys, d=64, bf16",
+            "eps": eps, "steps": steps, "rotating_sets": sets,
+            "us_per_call": round(us, 3), "us_per_call_wall": round(wall * 1e6 / steps, 3),
+            "kernel_us": round(kern_us, 3),
+            "query_rows_per_s": round(n_q / (us * 1e-6), 1),
+            "qk_mfma_tflops": round(qk_flops / (us * 1e-6) / 1e12, 2),
+            "input_gbps": round(in_bytes / (us * 1e-6) / 1e9, 1),
+            "mean_k_over_n": round(float(np.mean(kmean)) / n, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,7 +237,9 @@ def main():
     ap.add_argument("--sets", type=int, default=6, help="rotating input sets (128 MiB each)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
-    ap.add_argument("--no-stage-events", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--encoder-steps", type=int, default=500,
+                    help="calls of the all-queries (encoder-shaped) leg; 0 skips it")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -251,16 +328,15 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = n_q * args.steps / wall
 
-    # Instrumented pass over the same steps: the library records HIP events on
-    # the call's stream at its stage boundaries (each record costs a few
-    # microseconds, so this pass is not the headline figure).
-    n_ev = len(STAGES) + 1
-    stage_us = {}
+    # Instrumented pass over the same steps: the library attaches a (start,
+    # stop) event pair to each kernel's dispatch, so each pair times one kernel.
+    n_ev = 2 * len(KERNELS)
+    kernel_us = {}
     scan_us = None
     ms_events = None
-    if not args.no_stage_events:
+    if not args.no_kernel_events:
         evs = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)]
-        arm = lib.ctopk_record_stage_events
+        arm = lib.ctopk_record_kernel_events
         ev_arrays = [(ctypes.c_void_p * n_ev)(*[ctypes.c_void_p(e) for e in row]) for row in evs]
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -269,10 +345,10 @@ def main():
             step(i)
         torch.cuda.synchronize()
         ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
-        per = np.array([[hip.elapsed_ms(row[j], row[j + 1]) for j in range(n_ev - 1)]
+        per = np.array([[hip.elapsed_ms(row[2 * j], row[2 * j + 1]) for j in range(len(KERNELS))]
                         for row in evs])
-        for j, name in enumerate(STAGES):
-            stage_us[name] = round(float(per[:, j].mean()) * 1e3, 3)
+        for j, name in enumerate(KERNELS):
+            kernel_us[name] = round(float(per[:, j].mean()) * 1e3, 3)
         scan_us = float(per[:, 0].mean()) * 1e3
         for row in evs:
             for e in row:
@@ -287,6 +363,10 @@ def main():
                     "traffic": traffic, "kernel": "score_scan_kernel<bf16,128,4>",
                     "algorithmic_bytes_per_launch": k_bytes,
                     "avg_launch_us": round(scan_us, 3)}
+
+    encoder = None
+    if args.encoder_steps > 0:
+        encoder = encoder_leg(lib, ct, torch, hip, args.encoder_steps, eps)
 
     e2e_gbps = (k_bytes + v_bytes) / (ms_per_step * 1e-3) / 1e9
     line = {
@@ -312,8 +392,9 @@ def main():
         "bytes_per_step": {"K": k_bytes, "V_union": round(v_bytes)},
         "v_union_fraction": round(v_bytes / k_bytes, 4),
         "mean_k_eps": round(float(np.mean(kmean)), 1),
-        "stage_us": stage_us,
-        "ms_per_step_with_stage_events": None if ms_events is None else round(ms_events, 5),
+        "kernel_us": kernel_us,
+        "ms_per_step_with_kernel_events": None if ms_events is None else round(ms_events, 5),
+        "encoder": encoder,
     }
     print(json.dumps(line), flush=True)
 

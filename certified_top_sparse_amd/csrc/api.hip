@@ -22,23 +22,25 @@ namespace {
 
 thread_local char g_err[512] = "";
 
-// Stage events armed by ctopk_record_stage_events for the next call.
-constexpr int kMaxStageEvents = 8;
-thread_local hipEvent_t g_stage_ev[kMaxStageEvents];
-thread_local int g_stage_n = 0;
+// Kernel events armed by ctopk_record_kernel_events for the next call, and
+// the pairs the current call is consuming.
+constexpr int kMaxKernelEvents = 16;
+thread_local hipEvent_t g_armed_ev[kMaxKernelEvents];
+thread_local int g_armed_n = 0;
+thread_local hipEvent_t g_call_ev[kMaxKernelEvents];
+thread_local int g_call_n = 0;
+thread_local int g_call_pos = 0;
 
-// Records the armed event for stage boundary i (if any) on stream st.
-struct StageMarks {
-  hipEvent_t ev[kMaxStageEvents];
-  int n;
-  hipStream_t st;
-  StageMarks(hipStream_t s) : n(g_stage_n), st(s) {
-    for (int i = 0; i < n; ++i) ev[i] = g_stage_ev[i];
-    g_stage_n = 0;
+// Moves the armed events to the call in progress (so they apply to this call
+// only, even when it fails validation) and drops what it left unused.
+struct CallEvents {
+  CallEvents() {
+    for (int i = 0; i < g_armed_n; ++i) g_call_ev[i] = g_armed_ev[i];
+    g_call_n = g_armed_n;
+    g_call_pos = 0;
+    g_armed_n = 0;
   }
-  void mark(int i) {
-    if (i < n) (void)hipEventRecord(ev[i], st);
-  }
+  ~CallEvents() { g_call_n = g_call_pos = 0; }
 };
 
 int fail(int code, const char* fmt, ...) {
@@ -184,6 +186,16 @@ int hip_check(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace ctopk {
+bool take_kernel_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (g_call_pos + 2 > g_call_n) return false;
+  *start = g_call_ev[g_call_pos];
+  *stop = g_call_ev[g_call_pos + 1];
+  g_call_pos += 2;
+  return true;
+}
+}  // namespace ctopk
+
 extern "C" {
 
 size_t ctopk_workspace_bytes(int64_t n, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
@@ -209,18 +221,16 @@ int ctopk_validate(const ctopk_args* a) {
 
 int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  StageMarks marks(st);  // consumes armed events even if validation fails
+  CallEvents events;  // consumes armed events even if validation fails
   int rc = validate_args(a);
   if (rc != CTOPK_OK) return rc;
   const float default_scale = static_cast<float>(1.0 / sqrt(static_cast<double>(a->d)));
 
   if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads)) {
-    marks.mark(0);
     rc = hip_check(ctopk::launch_encoder(a->q, a->K, a->V, a->d, a->head_scale, default_scale,
                                          a->n, a->n_q_heads, a->n_kv_heads, a->eps, a->out,
                                          a->k_eps, a->tau, a->sel_mask, a->scores, a->lse, st),
                    "encoder launch");
-    marks.mark(1);
     return rc == CTOPK_OK ? ok() : rc;
   }
 
@@ -240,29 +250,24 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
   const int rows = a->n_q_heads;
 
-  marks.mark(0);
   rc = hip_check(ctopk::launch_score_scan(a->q, a->K, a->dtype, a->d, a->head_scale,
                                           default_scale, a->n, rows, a->n_kv_heads, scores,
                                           blkstat, nullptr, 0, st),
                  "score_scan launch");
   if (rc != CTOPK_OK) return rc;
-  marks.mark(1);
   rc = hip_check(ctopk::launch_hist0(scores, a->n, rows, blkstat, L.nblk, L.hchunk, pcnt, pmass,
                                      st),
                  "hist0 launch");
   if (rc != CTOPK_OK) return rc;
-  marks.mark(2);
   rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, blkstat, L.nblk, pcnt, pmass,
                                        L.hchunk, a->eps, rs, a->k_eps, a->tau, a->lse,
                                        a->sel_mask, nullptr, 0, st),
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;
-  marks.mark(3);
   rc = hip_check(ctopk::launch_vsum(scores, a->n, rows, a->n_kv_heads, a->V, a->dtype, a->d, rs,
                                     part, L.nchunk, a->out, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
-  marks.mark(4);
   return ok();
 }
 
@@ -291,7 +296,7 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
                          size_t workspace_bytes, ctopk_stream_t stream, float* out,
                          int32_t* k_eps, double* tau, uint32_t* sel_mask, double* lse) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  StageMarks marks(st);  // consumes armed events even if validation fails
+  CallEvents events;  // consumes armed events even if validation fails
   if (!logits || !V || !out || !k_eps || !tau)
     return fail(CTOPK_ERR_NULL, "logits, V, out, k_eps and tau must be non-NULL");
   if (v_dtype != CTOPK_F32 && v_dtype != CTOPK_BF16)
@@ -325,26 +330,27 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
   float* part = reinterpret_cast<float*>(ws + L.part);
   ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
 
-  marks.mark(0);
   rc = hip_check(ctopk::launch_resolve(logits, n, rows, nullptr, 0, nullptr, nullptr, 0, eps, rs,
                                        k_eps, tau, lse, sel_mask, nullptr, 0, st),
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;
-  marks.mark(1);
   rc = hip_check(ctopk::launch_vsum(logits, n, rows, n_v, V, v_dtype, dv, rs, part, L.nchunk,
                                     out, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
-  marks.mark(2);
   return ok();
 }
 
-int ctopk_record_stage_events(void* const* events, int32_t count) {
-  if (count < 0 || count > kMaxStageEvents)
-    return fail(CTOPK_ERR_SHAPE, "count must be in 0..%d, got %d", kMaxStageEvents, count);
+int ctopk_record_kernel_events(void* const* events, int32_t count) {
+  if (count < 0 || count > kMaxKernelEvents || (count & 1))
+    return fail(CTOPK_ERR_SHAPE, "count must be even and in 0..%d, got %d", kMaxKernelEvents,
+                count);
   if (count > 0 && events == nullptr) return fail(CTOPK_ERR_NULL, "events is NULL");
-  for (int i = 0; i < count; ++i) g_stage_ev[i] = static_cast<hipEvent_t>(events[i]);
-  g_stage_n = count;
+  for (int i = 0; i < count; ++i) {
+    if (events[i] == nullptr) return fail(CTOPK_ERR_NULL, "events[%d] is NULL", i);
+    g_armed_ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_armed_n = count;
   return ok();
 }
 

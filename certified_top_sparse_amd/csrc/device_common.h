@@ -50,18 +50,28 @@ __device__ __forceinline__ float key64_score(uint64_t k) {
   return ukey_to_float(static_cast<uint32_t>(k >> 32));
 }
 
-// Unnormalised softmax weight w = exp(s - m) in fp32.  The rounding error of the
-// fp32 difference (s - m) is recovered exactly (two-sum) and folded back in to
-// first order, so w carries the error of one expf rather than that of expf at
-// a rounded argument.  Every kernel uses this one definition, so the
-// selection, tau and the output all see identical weights.
+// Unnormalised softmax weight w = exp(s - m) in fp32 (s <= m).  The fp32
+// difference d = s - m carries a rounding error err that two-sum recovers
+// exactly; d * log2(e) is split with an fma into th + tl (log2(e) itself in
+// two fp32 parts).  Then exp(s - m) = 2^th * 2^tl * e^err, and to first order
+// w = e2 * (1 + tl ln2 + err) with e2 = 2^th from the hardware base-2
+// exponential, so w carries about the error of that one instruction rather
+// than that of an exponential at a rounded argument.  Every kernel uses this
+// one definition, so the selection, tau and the output all see identical
+// weights.  Results below 2^-126 (weights under ~1e-38 of the row maximum)
+// may flush to zero.
 __device__ __forceinline__ float weight(float s, float m) {
   const float d = s - m;
   const float bv = d - s;
   const float av = d - bv;
   const float err = (s - av) + (-m - bv);
-  const float e = expf(d);
-  return fmaf(e, err, e);
+  constexpr float kLog2e = 1.44269502162933349609375f;   // log2(e) rounded to fp32
+  constexpr float kLog2eLo = 1.925963033500011079e-8f;  // log2(e) - kLog2e
+  constexpr float kLn2 = 0.693147182464599609375f;      // ln(2) rounded to fp32
+  const float th = d * kLog2e;
+  const float tl = fmaf(d, kLog2eLo, fmaf(d, kLog2e, -th));
+  const float e2 = __builtin_amdgcn_exp2f(th);
+  return fmaf(e2, fmaf(tl, kLn2, err), e2);
 }
 
 // ---------------------------------------------------------------------------

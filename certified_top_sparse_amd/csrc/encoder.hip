@@ -122,8 +122,16 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int h = blockIdx.y;
-  const int qr = blockIdx.x * kEncRows + wave * 16 + r;
+  // Workgroups are dealt to the 8 XCDs round robin by id; when the count
+  // allows, give every row tile of one head the same id mod 8, so that head's
+  // K and V are fetched into one XCD's L2 instead of eight.
+  const int tiles = (G + kEncRows - 1) / kEncRows;
+  const int nwg = static_cast<int>(gridDim.x);
+  const int lin = (nwg % 8 == 0 && (nwg / 8) % tiles == 0)
+                      ? static_cast<int>(blockIdx.x % 8) * (nwg / 8) + static_cast<int>(blockIdx.x / 8)
+                      : static_cast<int>(blockIdx.x);
+  const int h = lin / tiles;
+  const int qr = (lin % tiles) * kEncRows + wave * 16 + r;
   const bool row_ok = qr < G;
   const int64_t row = static_cast<int64_t>(h) * G + (row_ok ? qr : G - 1);
   const float scale = head_scale ? head_scale[row] : default_scale;
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int j = 0; j < 16; ++j) hrow[16 * g + j] = 0.0;
   wave_lds_sync();
-  // Level 0: Z and the mass histogram over equal-width value bins on [mn, mx].
+  // Level 0: the mass histogram over equal-width value bins on [mn, mx].
   const float vrng = mx - mn;
   float vinv = static_cast<float>(kEncBins) / vrng;
   vinv = (vrng > 0.0f && isfinite(vinv)) ? vinv : 0.0f;
@@ -203,17 +211,20 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // underflows below -104), so clamping there changes no weight; it maps the
   // -inf of absent keys to weight 0 without a branch.
   const float wfloor = mx - 200.0f;
-  double Z = 0.0;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float v = s[t][e];
-      const float w = weight(fmaxf(v, wfloor), mx);
-      Z += static_cast<double>(w);
-      atomicAdd(hrow + value_bin(v, mn, vinv), static_cast<double>(w));
+      atomicAdd(hrow + value_bin(v, mn, vinv), static_cast<double>(weight(fmaxf(v, wfloor), mx)));
     }
-  Z = row_sum(Z);
+  wave_lds_sync();
+  // Z = the histogram's total, summed in one fixed order by all lanes of a row.
+  double zp = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) zp += hrow[16 * g + j];
+  const double Z = (__shfl(zp, r, kWave) + __shfl(zp, r + 16, kWave)) +
+                   (__shfl(zp, r + 32, kWave) + __shfl(zp, r + 48, kWave));
   const double thr = eps * Z;
 
   bool active = true;
@@ -422,7 +433,6 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   f32x4_t acc[D / 16];
 #pragma unroll
   for (int f = 0; f < D / 16; ++f) acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  double den = 0.0;
   int kc = 0;
   uint16_t* Vt = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
@@ -463,7 +473,6 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
             const float v = s[t0 + half][e + k];
             const bool head = v > cs || (v == cs && 16 * (t0 + half) + e + k <= cil);
             const float w = head ? weight(v, mx) : 0.0f;
-            den += static_cast<double>(w);
             kc += head ? 1 : 0;
             bits |= head ? (gbit << (16 * half + e + k)) : 0u;
             const __bf16 wh = static_cast<__bf16>(w);
@@ -492,8 +501,8 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
   }
-  den = row_sum(den);
   kc = row_sum(kc);
+  const double den = Z - R;  // head mass
 
   if (!row_ok) return;
   const float invd = static_cast<float>(1.0 / den);
@@ -525,12 +534,11 @@ hipError_t launch_t(const void* q, const void* K, const void* V, const float* he
                     float default_scale, int n, int G, int n_kv, double eps, float* out,
                     int32_t* k_eps, double* tau, uint32_t* sel_mask, float* scores, double* lse,
                     hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(G, kEncRows)), static_cast<unsigned>(n_kv));
-  hipLaunchKernelGGL((encoder_kernel<D, NT>), grid, dim3(kEncThreads), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
-                     static_cast<const uint16_t*>(V), head_scale, default_scale, n, G, eps, out,
-                     k_eps, tau, sel_mask, scores, lse);
-  return hipGetLastError();
+  const dim3 grid(static_cast<unsigned>(ceil_div(G, kEncRows) * n_kv));
+  return launch(encoder_kernel<D, NT>, grid, dim3(kEncThreads), 0, st,
+                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
+                static_cast<const uint16_t*>(V), head_scale, default_scale, n, G, eps, out, k_eps,
+                tau, sel_mask, scores, lse);
 }
 
 template <int D>

@@ -2,6 +2,7 @@
 // C ABI is include/ctopk.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -20,6 +21,24 @@ constexpr int kVsumTile = 256;
 constexpr int kCandCap = 8192;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Instrumentation: pops the next (start, stop) event pair armed for the
+// current call on this host thread (ctopk_record_kernel_events); false if none.
+bool take_kernel_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through here.  With an armed event
+// pair the events are attached to the dispatch itself, so they time exactly
+// the kernel's execution (no marker packets in between).
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem,
+                  hipStream_t st, Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (take_kernel_events(&a, &b))
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, a, b, 0, static_cast<KArgs>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
 
 // K1: scores[h, i] = scale_h * <q_h, K[h / G, i]> and blkstat[h, tile] =
 // (min, max) over the tile.  Also zeroes `zero_bytes` at `zero_base`.

@@ -156,14 +156,12 @@ hipError_t launch_t(const void* q, const void* K, const float* head_scale, float
   const int nblk = static_cast<int>(ceil_div(n, kScanTile));
   dim3 grid(nblk, n_kv, static_cast<unsigned>(ceil_div(G, GB)));
   if (head_scale != nullptr)
-    hipLaunchKernelGGL((score_scan_kernel<T, D, GB, true>), grid, dim3(256), 0, st,
-                       static_cast<const T*>(q), static_cast<const T*>(K), head_scale,
-                       default_scale, n, G, nblk, scores, blkstat, zb, zbytes);
-  else
-    hipLaunchKernelGGL((score_scan_kernel<T, D, GB, false>), grid, dim3(256), 0, st,
-                       static_cast<const T*>(q), static_cast<const T*>(K), head_scale,
-                       default_scale, n, G, nblk, scores, blkstat, zb, zbytes);
-  return hipGetLastError();
+    return launch(score_scan_kernel<T, D, GB, true>, grid, dim3(256), 0, st,
+                  static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale,
+                  n, G, nblk, scores, blkstat, zb, zbytes);
+  return launch(score_scan_kernel<T, D, GB, false>, grid, dim3(256), 0, st,
+                static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale, n,
+                G, nblk, scores, blkstat, zb, zbytes);
 }
 
 template <typename T, int D>

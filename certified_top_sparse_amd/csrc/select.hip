@@ -514,9 +514,8 @@ int hist_nchunk(int64_t n, int rows) {
 hipError_t launch_hist0(const float* scores, int64_t n, int rows, const float2* blkstat,
                         int nblk, int nchunk, uint32_t* pcnt, double* pmass, hipStream_t st) {
   const int64_t chunk = ceil_div(n, nchunk);
-  hipLaunchKernelGGL(hist0_kernel, dim3(static_cast<unsigned>(nchunk) * rows), dim3(256), 0, st,
-                     scores, n, chunk, nchunk, blkstat, nblk, pcnt, pmass);
-  return hipGetLastError();
+  return launch(hist0_kernel, dim3(static_cast<unsigned>(nchunk) * rows), dim3(256), 0, st,
+                scores, n, chunk, nchunk, blkstat, nblk, pcnt, pmass);
 }
 
 hipError_t launch_resolve(const float* scores, int64_t n, int rows, const float2* blkstat,
@@ -524,10 +523,9 @@ hipError_t launch_resolve(const float* scores, int64_t n, int rows, const float2
                           double eps, RowSel* rs, int32_t* k_eps, double* tau, double* lse,
                           uint32_t* sel_mask, void* zero_base, size_t zero_bytes,
                           hipStream_t st) {
-  hipLaunchKernelGGL(resolve_kernel, dim3(rows), dim3(kResolveThreads), 0, st, scores, n, blkstat,
-                     nblk, pcnt, pmass, npart, eps, rs, k_eps, tau, lse, sel_mask, zero_base,
-                     zero_bytes);
-  return hipGetLastError();
+  return launch(resolve_kernel, dim3(rows), dim3(kResolveThreads), 0, st, scores, n, blkstat,
+                nblk, pcnt, pmass, npart, eps, rs, k_eps, tau, lse, sel_mask, zero_base,
+                zero_bytes);
 }
 
 }  // namespace ctopk

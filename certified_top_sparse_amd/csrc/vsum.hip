@@ -259,12 +259,10 @@ hipError_t launch_t(const float* scores, int64_t n, int rows, int n_v, const voi
   const int G = rows / n_v;
   const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
   dim3 grid(nchunk, n_v, static_cast<unsigned>(ceil_div(G, GB)));
-  hipLaunchKernelGGL((vsum_kernel<T, D, GB>), grid, dim3(kVsumThreads), 0, st, scores, n, G,
-                     static_cast<const T*>(V), rs, part, nchunk, tpb);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch(vsum_kernel<T, D, GB>, grid, dim3(kVsumThreads), 0, st, scores, n,
+                              G, static_cast<const T*>(V), rs, part, nchunk, tpb);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3(rows), dim3(1024), 0, st, part, nchunk, D, out);
-  return hipGetLastError();
+  return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, part, nchunk, D, out);
 }
 
 template <typename T, int D>

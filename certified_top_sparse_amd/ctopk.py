@@ -37,7 +37,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "ctopk_certify", "ctopk_certify_ex", "ctopk_workspace_bytes", "ctopk_certify_logits",
     "ctopk_logits_workspace_bytes", "ctopk_validate", "ctopk_last_error_string",
-    "ctopk_version", "ctopk_record_stage_events",
+    "ctopk_version", "ctopk_record_kernel_events",
 )
 
 
@@ -106,8 +106,8 @@ def load(path: str = LIB_PATH):
     lib.ctopk_last_error_string.restype = ctypes.c_char_p
     lib.ctopk_version.argtypes = []
     lib.ctopk_version.restype = ctypes.c_char_p
-    lib.ctopk_record_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
-    lib.ctopk_record_stage_events.restype = ctypes.c_int
+    lib.ctopk_record_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.ctopk_record_kernel_events.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -163,11 +163,11 @@ def ctopk_logits_workspace_bytes(n, dv, rows, n_v) -> int:
     return int(load().ctopk_logits_workspace_bytes(n, dv, rows, n_v))
 
 
-def ctopk_record_stage_events(events) -> None:
-    """Arm the calling thread's next certify call to record the given raw
-    hipEvent_t handles (ints) at its stage boundaries."""
+def ctopk_record_kernel_events(events) -> None:
+    """Arm the calling thread's next certify call to attach the raw hipEvent_t
+    handles (ints), taken in (start, stop) pairs, to its kernels in launch order."""
     arr = (ctypes.c_void_p * max(1, len(events)))(*[ctypes.c_void_p(e) for e in events])
-    _check(load().ctopk_record_stage_events(arr, len(events)))
+    _check(load().ctopk_record_kernel_events(arr, len(events)))
 
 
 def ctopk_validate(args: CtopkArgs) -> int:

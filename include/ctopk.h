@@ -108,8 +108,10 @@ typedef struct ctopk_args {
 /*
  * ctopk_certify_ex -- full form of ctopk_certify: fp32 or bf16 inputs, per-head
  * scale, caller-owned workspace, optional selection mask, scores and lse.
- * Rows whose group size n_q_heads/n_kv_heads is >= 64 with n <= 1024 and bf16
- * inputs run on the all-queries (encoder-shaped) path whose QK^T uses MFMA.
+ * bf16 inputs with d 64 or 128, n <= 512 and n_q_heads/n_kv_heads >= 64 (all
+ * queries of a head against few keys, as in an encoder) run on a fused path
+ * whose QK^T and head-only output use MFMA; it needs no workspace.  Results
+ * follow the same definitions on both paths.
  */
 CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
 
@@ -145,21 +147,22 @@ CTOPK_API size_t ctopk_logits_workspace_bytes(int64_t n, int32_t dv, int32_t row
 CTOPK_API int ctopk_validate(const ctopk_args* a);
 
 /*
- * ctopk_record_stage_events -- instrumentation for benchmarks and profilers.
+ * ctopk_record_kernel_events -- instrumentation for benchmarks and profilers.
  *
  * Arms the calling thread so that its NEXT ctopk_certify, ctopk_certify_ex or
- * ctopk_certify_logits call records events[i] (hipEvent_t handles created by
- * the caller, count <= 8) on its stream at the path's stage boundaries, then
- * disarms.  Decode path: [0] before the score scan, [1] after it, [2] after
- * the level-0 histogram, [3] after the rest of the select, [4] after the value
- * stream and its output combine.  Logits path: [0] before the select, [1]
- * after it, [2] after the value stream and its output combine.
- * Encoder-shaped path: [0] before and [1] after its fused kernel.
- * Boundaries past `count` are not recorded.
- * Recording adds no work to the kernels themselves.  Returns CTOPK_OK, or
- * CTOPK_ERR_SHAPE for count outside 0..8 (count 0 disarms).
+ * ctopk_certify_logits call attaches the event pair (events[2i],
+ * events[2i+1]) -- hipEvent_t handles created by the caller -- to the i-th
+ * kernel it launches: the events take that kernel's start and end times on
+ * the call's stream (hipExtLaunchKernel), so hipEventElapsedTime on a pair is
+ * the kernel's own duration.  Kernels in launch order: decode path: score
+ * scan, level-0 histogram, select, value stream, output combine; logits path:
+ * select, value stream, output combine; encoder-shaped path: its one fused
+ * kernel.  Kernels past count/2 pairs run without events; pairs left over are
+ * dropped when the call returns.  count must be even and at most 16 (0
+ * disarms); returns CTOPK_ERR_SHAPE otherwise, CTOPK_ERR_NULL for a NULL
+ * array or handle.
  */
-CTOPK_API int ctopk_record_stage_events(void* const* events, int32_t count);
+CTOPK_API int ctopk_record_kernel_events(void* const* events, int32_t count);
 
 /* Text of the last error on the calling thread ("" after success). */
 CTOPK_API const char* ctopk_last_error_string(void);

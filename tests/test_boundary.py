@@ -160,11 +160,14 @@ def test_logits_argument_errors(lib, kw, code):
     assert rc == code
 
 
-def test_stage_event_arming_limits(lib):
-    arr = (ctypes.c_void_p * 9)()
-    assert lib.ctopk_record_stage_events(arr, 9) == cb.CTOPK_ERR_SHAPE
-    assert lib.ctopk_record_stage_events(None, 3) == cb.CTOPK_ERR_NULL
-    assert lib.ctopk_record_stage_events(None, 0) == cb.CTOPK_OK
+def test_kernel_event_arming_limits(lib):
+    arr = (ctypes.c_void_p * 18)(*([A16] * 18))
+    assert lib.ctopk_record_kernel_events(arr, 18) == cb.CTOPK_ERR_SHAPE
+    assert lib.ctopk_record_kernel_events(arr, 3) == cb.CTOPK_ERR_SHAPE  # pairs only
+    assert lib.ctopk_record_kernel_events(None, 4) == cb.CTOPK_ERR_NULL
+    holes = (ctypes.c_void_p * 2)(A16, None)
+    assert lib.ctopk_record_kernel_events(holes, 2) == cb.CTOPK_ERR_NULL
+    assert lib.ctopk_record_kernel_events(None, 0) == cb.CTOPK_OK
 
 
 def test_missing_library_fails_loudly(tmp_path):
