@@ -19,7 +19,7 @@ Zhang, Chen; arXiv 2512.07647), Abstract.  The abstract defines:
 * the minimal k_eps with TV <= eps, and its Gaussian-score design rule
   k_eps / n ~ Phi_c(sigma + Phi^{-1}(eps)).
 
-Readings where the page leaves a step open (each is listed in the design doc):
+Readings where the page leaves a step open:
 
 * the certificate is inclusive, TV <= eps, and k ranges over 1..n;
 * keys are ordered by score descending and, among equal scores, by index
@@ -37,8 +37,8 @@ device receives.
 
 Parity status: every function here is pinned by the tests in
 ``tests/test_oracle_pins.py`` (identities, brute force, closed forms and the
-Gaussian design rule).  No value printed on the pages pins a specific
-(q, K, V) -> (k_eps, tau, out) triple; see the design doc.
+Gaussian design rule).  The pages print no worked example, so no specific
+(q, K, V) -> (k_eps, tau, out) triple is pinned by a printed value.
 """
 from __future__ import annotations
 
