@@ -74,6 +74,15 @@ __device__ __forceinline__ float weight(float s, float m) {
   return fmaf(e2, fmaf(tl, kLn2, err), e2);
 }
 
+// 16-byte load of data that is streamed once (K in the score scan, V in the
+// value stream): the non-temporal hint keeps it from displacing reused lines
+// (scores, partials) in the caches.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // ---------------------------------------------------------------------------
 // DPP lane exchanges (full-rate VALU, no LDS traffic)
 // ---------------------------------------------------------------------------

@@ -13,8 +13,10 @@ namespace ctopk {
 
 // Compute units of an MI355X.
 constexpr int kNumCUs = 256;
-// Keys per tile of the score scan; per-tile (min, max) are emitted per tile.
-constexpr int kScanTile = 128;
+// Keys per tile (one workgroup) of the score scan; its (min, max) is emitted
+// per tile.  64 keys per 4-wave group measured fastest on MI355X (more, shorter
+// workgroups keep more loads in flight across the chip).
+constexpr int kScanTile = 64;
 // Keys per tile of the value stream (8 waves x 32 keys).
 constexpr int kVsumTile = 256;
 // Largest candidate set the resolve kernel keeps in LDS.

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void score_scan_kernel(
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int64_t r = min(tile0 + lbase + it * RPW + rg, n - 1);
-    kv[it] = *reinterpret_cast<const uint4*>(Kb + r * D + seg * EPL);
+    kv[it] = load_stream16(Kb + r * D + seg * EPL);
   }
   // q slices (head slots past nh repeat the last head and are never written).
   uint4 qv[GB];

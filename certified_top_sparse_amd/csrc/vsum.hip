@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int64_t r = min(p0 + it * RPW + rg, n - 1);
-      u[it] = *reinterpret_cast<const uint4*>(Vb + r * D + seg * EPL);
+      u[it] = load_stream16(Vb + r * D + seg * EPL);
     }
     float s[PPL];
 #pragma unroll
