@@ -38,8 +38,10 @@ import workloads  # noqa: E402
 
 METRIC = "certified top-k decode query-heads/s + achieved HBM GB/s (% peak), n=32K GQA"
 PEAK_HBM_GBPS = 8000.0
-# Kernels of one decode call, in launch order (score scan, level-0 histogram,
-# select, value stream, output combine).
+# Kernels of one decode call, in launch order: score scan, level-0 histogram
+# (only for rows longer than the select holds in registers; otherwise its
+# event pair is recorded back to back and reads ~0), select, value stream,
+# output combine.
 KERNELS = ("score_scan", "hist0", "resolve", "vsum", "finalize")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_scan_gqa_decode_n32768_pmc.md")
 SCAN_SOURCE = os.path.join(ROOT, "certified_top_sparse_amd", "csrc", "score_scan.hip")

@@ -1,8 +1,9 @@
 // libctopk C ABI: argument validation, workspace layout and launch sequencing.
 //
 // Decode path (ctopk_certify / ctopk_certify_ex):
-//   score_scan (scores, per-tile min/max) -> hist0 (level-0 partial histograms)
-//   -> resolve (lse, k_eps, tau, cut key, mask) -> vsum (w * v over the head, out)
+//   score_scan (scores, per-tile min/max) -> [hist0 (level-0 partial
+//   histograms), rows longer than the select holds in registers] -> resolve
+//   (lse, k_eps, tau, cut key, mask) -> vsum (w * v over the head, out)
 // Logits path (ctopk_certify_logits):
 //   resolve (including level 0) -> vsum
 // Encoder-shaped path (all queries of a head, small n): one fused kernel.
@@ -68,7 +69,7 @@ constexpr int64_t kMaxElems = 1LL << 36;  // rows * n
 // Scratch layout shared by both paths (every region is fully written before
 // it is read within a call, so nothing needs zeroing).
 struct Layout {
-  size_t rowsel = 0, blkstat = 0, part = 0, pcnt = 0, pmass = 0;
+  size_t rowsel = 0, blkstat = 0, part = 0, pmass = 0;
   size_t scores = 0, total = 0;
   int nblk = 0, nchunk = 0, hchunk = 0;
 };
@@ -77,7 +78,7 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   Layout L;
   L.nblk = decode ? static_cast<int>(ctopk::ceil_div(n, ctopk::kScanTile)) : 0;
   L.nchunk = ctopk::vsum_nchunk(n, rows, n_v, v_dtype, dv);
-  L.hchunk = decode ? ctopk::hist_nchunk(n, rows) : 0;
+  L.hchunk = (decode && n > ctopk::resolve_register_row()) ? ctopk::hist_nchunk(n, rows) : 0;
   size_t off = 0;
   L.rowsel = off;
   off += up(static_cast<size_t>(rows) * sizeof(ctopk::RowSel));
@@ -85,8 +86,6 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   off += up(static_cast<size_t>(rows) * L.nblk * sizeof(float2));
   L.part = off;
   off += up(static_cast<size_t>(rows) * L.nchunk * (dv + 1) * sizeof(float));
-  L.pcnt = off;
-  off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(uint32_t));
   L.pmass = off;
   off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(double));
   L.scores = off;
@@ -194,6 +193,13 @@ bool take_kernel_events(hipEvent_t* start, hipEvent_t* stop) {
   g_call_pos += 2;
   return true;
 }
+void skip_kernel_events(hipStream_t st) {
+  hipEvent_t a, b;
+  if (take_kernel_events(&a, &b)) {
+    (void)hipEventRecord(a, st);
+    (void)hipEventRecord(b, st);
+  }
+}
 }  // namespace ctopk
 
 extern "C" {
@@ -245,7 +251,6 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   float* scores = a->scores ? a->scores : reinterpret_cast<float*>(ws + L.scores);
   float2* blkstat = reinterpret_cast<float2*>(ws + L.blkstat);
   float* part = reinterpret_cast<float*>(ws + L.part);
-  uint32_t* pcnt = reinterpret_cast<uint32_t*>(ws + L.pcnt);
   double* pmass = reinterpret_cast<double*>(ws + L.pmass);
   ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
   const int rows = a->n_q_heads;
@@ -255,11 +260,15 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
                                           blkstat, nullptr, 0, st),
                  "score_scan launch");
   if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_hist0(scores, a->n, rows, blkstat, L.nblk, L.hchunk, pcnt, pmass,
-                                     st),
-                 "hist0 launch");
-  if (rc != CTOPK_OK) return rc;
-  rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, blkstat, L.nblk, pcnt, pmass,
+  if (L.hchunk > 0) {  // long rows: level 0 from many blocks per row
+    rc = hip_check(ctopk::launch_hist0(scores, a->n, rows, blkstat, L.nblk, L.hchunk, pmass,
+                                       st),
+                   "hist0 launch");
+    if (rc != CTOPK_OK) return rc;
+  } else {
+    ctopk::skip_kernel_events(st);
+  }
+  rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, blkstat, L.nblk, pmass,
                                        L.hchunk, a->eps, rs, a->k_eps, a->tau, a->lse,
                                        a->sel_mask, nullptr, 0, st),
                  "resolve launch");
@@ -330,7 +339,7 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
   float* part = reinterpret_cast<float*>(ws + L.part);
   ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
 
-  rc = hip_check(ctopk::launch_resolve(logits, n, rows, nullptr, 0, nullptr, nullptr, 0, eps, rs,
+  rc = hip_check(ctopk::launch_resolve(logits, n, rows, nullptr, 0, nullptr, 0, eps, rs,
                                        k_eps, tau, lse, sel_mask, nullptr, 0, st),
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;

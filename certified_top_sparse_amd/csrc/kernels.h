@@ -27,6 +27,9 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 // Instrumentation: pops the next (start, stop) event pair armed for the
 // current call on this host thread (ctopk_record_kernel_events); false if none.
 bool take_kernel_events(hipEvent_t* start, hipEvent_t* stop);
+// For a kernel of the path that a call does not need: records its armed pair
+// (if any) back to back on st, so pairs stay aligned with the path's kernels.
+void skip_kernel_events(hipStream_t st);
 
 // Every kernel of the library is launched through here.  With an armed event
 // pair the events are attached to the dispatch itself, so they time exactly
@@ -49,20 +52,24 @@ hipError_t launch_score_scan(const void* q, const void* K, int dtype, int d,
                              int n_q, int n_kv, float* scores, float2* blkstat,
                              void* zero_base, size_t zero_bytes, hipStream_t st);
 
-// Level 0 of the select for the decode path, many blocks per row: row
-// (min, max) from blkstat, weights w = exp(s - max), and a (count, fp64 mass)
+// Level 0 of the select for long decode rows, many blocks per row: row
+// (min, max) from blkstat, weights w = exp(s - max), and an fp64 mass
 // histogram over kBins equal-width value bins on [min, max] per chunk of keys,
-// written to pcnt / pmass [rows, hist_nchunk, kBins].
+// written to pmass [rows, hist_nchunk, kBins].
 int hist_nchunk(int64_t n, int rows);
+// Rows up to this many keys are held in registers by the select's block, which
+// then builds level 0 itself (no hist0 pass and no partial histograms).
+int resolve_register_row();
 hipError_t launch_hist0(const float* scores, int64_t n, int rows, const float2* blkstat,
-                        int nblk, int nchunk, uint32_t* pcnt, double* pmass, hipStream_t st);
+                        int nblk, int nchunk, double* pmass, hipStream_t st);
 
-// Select, one workgroup per row: level-0 histogram from the hist0 partials (or,
-// with npart == 0, from a pass over the row, after a (min, max) pass when
-// blkstat is NULL), then the radix levels.  Writes k_eps, tau, lse (optional),
+// Select, one workgroup per row: level-0 mass histogram from the hist0
+// partials (or, with npart == 0, from a pass over the row, which the block
+// holds in registers when n <= resolve_register_row(); a (min, max) pass
+// first when blkstat is NULL), then the radix levels.  Writes k_eps, tau, lse (optional),
 // sel_mask (optional) and RowSel.  Also zeroes `zero_bytes` at `zero_base`.
 hipError_t launch_resolve(const float* scores, int64_t n, int rows, const float2* blkstat,
-                          int nblk, const uint32_t* pcnt, const double* pmass, int npart,
+                          int nblk, const double* pmass, int npart,
                           double eps, RowSel* rs, int32_t* k_eps, double* tau, double* lse,
                           uint32_t* sel_mask, void* zero_base, size_t zero_bytes,
                           hipStream_t st);

@@ -12,18 +12,20 @@
 // keeping R = mass and `below` = count of keys under the range:
 //   level 0: row maximum m (the log-sum-exp reference) and minimum, from the
 //            score scan's per-tile pairs or from a pass over given logits;
-//            weights w = exp(s - m); (count, fp64 mass) per kBins equal-width
-//            value bins on [min, max] -- built by many blocks per row
-//            (hist0_kernel, per-chunk partial histograms, no atomics across
-//            blocks) or inside the row's own block; Z = the bins' sum in a
-//            fixed order; lse = m + log Z;
-//   level >0 (resolve_kernel, one block per row): pick the cut bin b*, the
-//            largest non-empty bin whose lower bins hold mass <= eps*Z - R;
-//            then histogram the next 11 bits of key64 inside b*.  Once the
-//            range holds <= kCandCap keys they are copied into LDS and the
-//            radix continues from the first bit where they differ; once it
-//            holds <= 64 keys one wave finishes by comparing every pair.  key64
-//            is unique, so the search always ends on one key.
+//            weights w = exp(s - m); an fp64 mass histogram over kBins
+//            equal-width value bins on [min, max] -- built by many blocks per
+//            row for long rows (hist0_kernel, per-chunk partials, no atomics
+//            across blocks) or inside the row's own block, which then holds
+//            the row in registers; Z = the bins' sum in a fixed order;
+//            lse = m + log Z.  The cut bin b* is the largest bin of positive
+//            mass whose lower bins hold mass <= eps*Z; one pass then counts
+//            the keys of lower bins and copies b*'s keys into LDS;
+//   level >0 (resolve_kernel, one block per row): histogram (count, mass) of
+//            the next 11 bits of key64 inside the range and keep the bin
+//            holding the cut.  Once the range holds <= kCandCap keys they are
+//            in LDS and the radix continues from the first bit where they
+//            differ; once it holds <= 64 keys one wave finishes by comparing
+//            every pair.  key64 is unique, so the search always ends on one key.
 // Counts are exact integers, so k_eps is exact given the weights; masses are
 // fp64 sums of fp32 weights.  tau = R / Z uses the same weights as Z.
 #include "kernels.h"
@@ -37,6 +39,8 @@ constexpr int kResolveWaves = kResolveThreads / 64;
 constexpr int kReadBatch = 16;
 // Candidate sets this small are finished by one wave.
 constexpr int kSmallCand = 64;
+// Rows up to this length are held in registers by their block (32 per thread).
+constexpr int kResolveRegRow = 32 * kResolveThreads;
 
 // Row (min, max) from per-tile pairs, reduced identically by every block.
 __device__ float2 row_minmax(const float2* __restrict__ bs, int nblk, float2* s_red) {
@@ -66,17 +70,12 @@ __device__ float2 row_minmax(const float2* __restrict__ bs, int nblk, float2* s_
 __global__ __launch_bounds__(256) void hist0_kernel(const float* __restrict__ scores, int64_t n,
                                                     int64_t chunk, int nchunk,
                                                     const float2* __restrict__ blkstat, int nblk,
-                                                    uint32_t* __restrict__ pcnt,
                                                     double* __restrict__ pmass) {
-  __shared__ uint32_t lc[kBins];
   __shared__ double lm[kBins];
   __shared__ float2 s_red[4];
   const int row = static_cast<int>(blockIdx.x / static_cast<unsigned>(nchunk));
   const int cb = static_cast<int>(blockIdx.x % static_cast<unsigned>(nchunk));
-  for (int b = threadIdx.x; b < kBins; b += blockDim.x) {
-    lc[b] = 0u;
-    lm[b] = 0.0;
-  }
+  for (int b = threadIdx.x; b < kBins; b += blockDim.x) lm[b] = 0.0;
   const float2 mm = row_minmax(blkstat + static_cast<size_t>(row) * nblk, nblk, s_red);
   const float lo = mm.x;
   const float m = mm.y;
@@ -93,18 +92,13 @@ __global__ __launch_bounds__(256) void hist0_kernel(const float* __restrict__ sc
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (base + u * 256 + threadIdx.x < c1) {
-        const int bin = lin_bin(v[u], lo, inv);
-        atomicAdd(&lc[bin], 1u);
-        atomicAdd(&lm[bin], static_cast<double>(weight(v[u], m)));
+        atomicAdd(&lm[lin_bin(v[u], lo, inv)], static_cast<double>(weight(v[u], m)));
       }
     }
   }
   __syncthreads();
   const size_t off = (static_cast<size_t>(row) * nchunk + cb) * kBins;
-  for (int b = threadIdx.x; b < kBins; b += blockDim.x) {
-    pcnt[off + b] = lc[b];
-    pmass[off + b] = lm[b];
-  }
+  for (int b = threadIdx.x; b < kBins; b += blockDim.x) pmass[off + b] = lm[b];
 }
 
 struct ResolveShared {
@@ -126,62 +120,91 @@ struct ResolveShared {
   unsigned long long kmin, kmax;
 };
 
-// Block-wide choice of the cut bin among nb bins held in sh.hc / sh.hm.
-// Returns b* and, through S and C, the mass and count of the bins below it.
-__device__ int select_bin(ResolveShared& sh, int nb, double R, double epsZ, double& S,
-                          uint32_t& C) {
+// Wave totals of the current histogram (nb <= kBins bins in sh.hc / sh.hm):
+// thread t holds bins 2t and 2t + 1, so wave w covers bins [128 w, 128 w + 128).
+// Every lane of a wave gets the same butterfly sum; sh.wd / sh.wc hold them.
+// With by_mass the histogram holds masses only and a bin counts as non-empty
+// when its mass is positive (bins of weight-0 keys, which underflowed, lie
+// below every positive bin and never hold the cut).
+__device__ __forceinline__ uint32_t bin_count(const ResolveShared& sh, int b, int nb, bool by_mass) {
+  if (b >= nb) return 0u;
+  return by_mass ? (sh.hm[b] > 0.0 ? 1u : 0u) : sh.hc[b];
+}
+
+__device__ void hist_wave_totals(ResolveShared& sh, int nb, bool by_mass) {
+  const int t = threadIdx.x;
+  const int b0 = 2 * t;
+  const double m = (b0 < nb ? sh.hm[b0] : 0.0) + (b0 + 1 < nb ? sh.hm[b0 + 1] : 0.0);
+  const uint32_t c = bin_count(sh, b0, nb, by_mass) + bin_count(sh, b0 + 1, nb, by_mass);
+  const double wm = wave_sum(m);
+  const uint32_t wc = wave_sum_u32(c);
+  if ((t & 63) == 0) {
+    sh.wd[t >> 6] = wm;
+    sh.wc[t >> 6] = wc;
+  }
+  __syncthreads();
+}
+
+// Block-wide choice of the cut bin among nb bins held in sh.hc / sh.hm, after
+// hist_wave_totals: the largest non-empty bin whose lower bins hold mass
+// R + S <= epsZ.  Every thread scans the 16 wave totals to find the wave that
+// holds it; only that wave scans its own 128 bins.  Returns b* and, through S
+// and C, the mass and count of the bins below it (-1 if no bin qualifies; C
+// is meaningless with by_mass).
+__device__ int select_bin(ResolveShared& sh, int nb, bool by_mass, double R, double epsZ,
+                          double& S, uint32_t& C) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int b0 = 2 * t;
-  const uint32_t c0 = b0 < nb ? sh.hc[b0] : 0u;
-  const uint32_t c1 = b0 + 1 < nb ? sh.hc[b0 + 1] : 0u;
-  const double m0 = b0 < nb ? sh.hm[b0] : 0.0;
-  const double m1 = b0 + 1 < nb ? sh.hm[b0 + 1] : 0.0;
-  const double tm = m0 + m1;
-  const uint32_t tc = c0 + c1;
-  const double im = wave_incl_scan(tm, lane);
-  const uint32_t ic = wave_incl_scan_u32(tc, lane);
-  if (lane == 63) {
-    sh.wd[wave] = im;
-    sh.wc[wave] = ic;
-  }
-  if (t == 0) sh.best = -1;
-  __syncthreads();
-  double off = 0.0;
-  uint32_t offc = 0u;
-  for (int w = 0; w < wave; ++w) {
-    off += sh.wd[w];
-    offc += sh.wc[w];
-  }
-  double em = __shfl_up(im, 1, 64);
-  uint32_t ec = __shfl_up(ic, 1, 64);
-  if (lane == 0) {
-    em = 0.0;
-    ec = 0u;
-  }
-  const double ex0 = off + em;
-  const uint32_t exc0 = offc + ec;
-  const double ex1 = ex0 + m0;
-  int mine = -1;
-  if (c0 != 0u && R + ex0 <= epsZ) mine = b0;
-  if (c1 != 0u && R + ex1 <= epsZ) mine = b0 + 1;
-  if (mine >= 0) atomicMax(&sh.best, mine);
-  __syncthreads();
-  const int bs = sh.best;
-  if (bs >= 0 && (bs >> 1) == t) {
-    if (bs == b0) {
-      sh.selS = ex0;
-      sh.selC = exc0;
-    } else {
-      sh.selS = ex1;
-      sh.selC = exc0 + c0;
+  double P = 0.0, Pw = 0.0;
+  uint32_t PC = 0u, PCw = 0u;
+  int ws = -1;
+  for (int w = 0; w < kResolveWaves; ++w) {
+    const uint32_t c = sh.wc[w];
+    if (c != 0u && R + P <= epsZ) {
+      ws = w;
+      Pw = P;
+      PCw = PC;
     }
+    P += sh.wd[w];
+    PC += c;
+  }
+  if (wave == ws) {
+    const int b0 = 2 * t;
+    const uint32_t c0 = bin_count(sh, b0, nb, by_mass);
+    const uint32_t c1 = bin_count(sh, b0 + 1, nb, by_mass);
+    const double m0 = b0 < nb ? sh.hm[b0] : 0.0;
+    const double m1 = b0 + 1 < nb ? sh.hm[b0 + 1] : 0.0;
+    const double im = wave_incl_scan(m0 + m1, lane);
+    const uint32_t ic = wave_incl_scan_u32(c0 + c1, lane);
+    double em = __shfl_up(im, 1, kWave);
+    uint32_t ec = __shfl_up(ic, 1, kWave);
+    if (lane == 0) {
+      em = 0.0;
+      ec = 0u;
+    }
+    const double ex0 = Pw + em;
+    const double ex1 = ex0 + m0;
+    const uint32_t exc0 = PCw + ec;
+    int mine = -1;
+    if (c0 != 0u && R + ex0 <= epsZ) mine = b0;
+    if (c1 != 0u && R + ex1 <= epsZ) mine = b0 + 1;
+    // The wave's first non-empty bin qualifies (its prefix is Pw), so the
+    // ballot is never empty; the highest qualifying lane holds the answer.
+    const uint64_t bal = __ballot(mine >= 0);
+    const int L = 63 - __clzll(static_cast<long long>(bal));
+    if (lane == L) {
+      sh.best = mine;
+      sh.selS = mine == b0 ? ex0 : ex1;
+      sh.selC = mine == b0 ? exc0 : exc0 + c0;
+    }
+  } else if (ws < 0 && t == 0) {
+    sh.best = -1;
   }
   __syncthreads();
   S = sh.selS;
   C = sh.selC;
-  return bs;
+  return sh.best;
 }
 
 __device__ __forceinline__ bool prefix_match(uint64_t k, uint64_t prefix, int plen) {
@@ -237,18 +260,74 @@ __device__ void finish_small(ResolveShared& sh, int c, float m, double R, double
   }
 }
 
+// The elements of one row as seen by one thread of its block: element
+// i = u * kResolveThreads + t.  With PT > 0 the thread holds its PT elements
+// in registers, all loaded when the block starts (rows of n <= PT * 1024);
+// with PT == 0 every pass streams them from global memory in batches.
+template <int PT>
+struct RowElems {
+  float v[PT > 0 ? PT : 1];
+  const float* sr;
+  int64_t n;
+
+  __device__ __forceinline__ void load(const float* __restrict__ row, int64_t len) {
+    sr = row;
+    n = len;
+    if constexpr (PT > 0) {  // n <= PT * kResolveThreads: 32-bit indices
+      const int last = static_cast<int>(len) - 1;
+#pragma unroll
+      for (int u = 0; u < PT; ++u)
+        v[u] = row[min(u * kResolveThreads + static_cast<int>(threadIdx.x), last)];
+    }
+  }
+
+  // Each pass recomputes what it derives from an element (bin, weight, key):
+  // the empty asm makes the values opaque, so the compiler cannot keep such
+  // per-element results live from one pass to the next (PT registers each).
+  template <typename F>
+  __device__ __forceinline__ void for_each(F&& f) {
+    int t = threadIdx.x;
+    if constexpr (PT > 0) {
+      asm volatile("" : "+v"(t));  // indices are recomputed per pass, not kept
+#pragma unroll
+      for (int u = 0; u < PT; ++u) asm volatile("" : "+v"(v[u]));
+      const int nn = static_cast<int>(n);
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int i = u * kResolveThreads + t;
+        if (i < nn) f(static_cast<int64_t>(i), v[u]);
+        // bound the scheduler's window: it would otherwise evaluate many
+        // elements ahead and run out of registers
+        if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int64_t base = 0; base < n; base += kReadBatch * kResolveThreads) {
+        float vv[kReadBatch];
+        load_batch(sr, n, base, t, vv);
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u) {
+          const int64_t i = base + u * kResolveThreads + t;
+          if (i < n) f(i, vv[u]);
+        }
+      }
+    }
+  }
+};
+
+template <int PT>
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
     const float* __restrict__ scores, int64_t n, const float2* __restrict__ blkstat, int nblk,
-    const uint32_t* __restrict__ pcnt, const double* __restrict__ pmass, int npart, double eps,
-    RowSel* __restrict__ rs, int32_t* __restrict__ k_eps, double* __restrict__ tau,
-    double* __restrict__ lse, uint32_t* __restrict__ sel_mask, void* zero_base,
-    size_t zero_bytes) {
+    const double* __restrict__ pmass, int npart, double eps, RowSel* __restrict__ rs,
+    int32_t* __restrict__ k_eps, double* __restrict__ tau, double* __restrict__ lse,
+    uint32_t* __restrict__ sel_mask, void* zero_base, size_t zero_bytes) {
   __shared__ ResolveShared sh;
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const float* sr = scores + static_cast<size_t>(row) * static_cast<size_t>(n);
+  RowElems<PT> E;
+  E.load(sr, n);  // register rows: every load of the row is in flight from here
   zero_slice(zero_base, zero_bytes, blockIdx.x, gridDim.x);
 
   if (t == 0) {
@@ -264,15 +343,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
     mm = row_minmax(blkstat + static_cast<size_t>(row) * nblk, nblk, sh.mm);
   } else {
     float vmax = -INFINITY, vmin = INFINITY;
-    for (int64_t base = 0; base < n; base += kReadBatch * kResolveThreads) {
-      float v[kReadBatch];
-      load_batch(sr, n, base, t, v);
-#pragma unroll
-      for (int u = 0; u < kReadBatch; ++u) {
-        vmax = fmaxf(vmax, v[u]);  // clamped duplicates are row values too
-        vmin = fminf(vmin, v[u]);
-      }
-    }
+    E.for_each([&](int64_t, float s) {
+      vmax = fmaxf(vmax, s);
+      vmin = fminf(vmin, s);
+    });
     vmax = wave_max_dpp(vmax);
     vmin = -wave_max_dpp(-vmin);
     if (lane == 0) sh.mm[wave] = make_float2(vmin, vmax);
@@ -287,81 +361,123 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
   const float lo = mm.x;
   const float inv = lin_scale(lo, m);
 
-  // Level-0 histogram: sum of the partials in chunk order, or a pass over the row.
-  if (npart > 0) {
+  // Level-0 histogram of masses: sum of the partials in chunk order, or a
+  // pass over the row (one LDS atomic per key; counts come from the pass
+  // that collects the cut bin's keys).
+  if (PT == 0 && npart > 0) {
     // Partials in chunk order; eight chunks' loads are issued before any add.
     const size_t base = static_cast<size_t>(row) * npart * kBins;
     for (int b = t; b < kBins; b += kResolveThreads) {
-      uint32_t c = 0u;
       double ms = 0.0;
       for (int p0 = 0; p0 < npart; p0 += 8) {
-        uint32_t cv[8];
         double mv[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const size_t o = base + static_cast<size_t>(min(p0 + u, npart - 1)) * kBins + b;
-          cv[u] = pcnt[o];
-          mv[u] = pmass[o];
-        }
+        for (int u = 0; u < 8; ++u)
+          mv[u] = pmass[base + static_cast<size_t>(min(p0 + u, npart - 1)) * kBins + b];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (p0 + u < npart) {
-            c += cv[u];
-            ms += mv[u];
-          }
-        }
+        for (int u = 0; u < 8; ++u)
+          if (p0 + u < npart) ms += mv[u];
       }
-      sh.hc[b] = c;
       sh.hm[b] = ms;
     }
   } else {
-    for (int b = t; b < kBins; b += kResolveThreads) {
-      sh.hc[b] = 0u;
-      sh.hm[b] = 0.0;
-    }
+    for (int b = t; b < kBins; b += kResolveThreads) sh.hm[b] = 0.0;
     __syncthreads();
-    for (int64_t base = 0; base < n; base += kReadBatch * kResolveThreads) {
-      float v[kReadBatch];
-      load_batch(sr, n, base, t, v);
-#pragma unroll
-      for (int u = 0; u < kReadBatch; ++u) {
-        if (base + u * kResolveThreads + t < n) {
-          const int bin = lin_bin(v[u], lo, inv);
-          atomicAdd(&sh.hc[bin], 1u);
-          atomicAdd(&sh.hm[bin], static_cast<double>(weight(v[u], m)));
-        }
-      }
-    }
+    E.for_each([&](int64_t, float s) {
+      atomicAdd(&sh.hm[lin_bin(s, lo, inv)], static_cast<double>(weight(s, m)));
+    });
   }
   __syncthreads();
 
-  // Z = total weight, summed in a fixed order (pairs, wave tree, waves in order).
-  double z = sh.hm[2 * t] + sh.hm[2 * t + 1];
-  z = wave_sum(z);
-  if (lane == 0) sh.wd[wave] = z;
-  __syncthreads();
+  // Z = total weight: wave totals (butterflies) added in wave order.
+  hist_wave_totals(sh, kBins, true);
   double Z = 0.0;
   for (int w = 0; w < kResolveWaves; ++w) Z += sh.wd[w];
-  __syncthreads();
   const double epsZ = eps * Z;
 
   // Level 0: the value bin holding the cut.
   double S;
   uint32_t C;
-  int b0 = select_bin(sh, kBins, 0.0, epsZ, S, C);
+  int b0 = select_bin(sh, kBins, true, 0.0, epsZ, S, C);
   if (b0 < 0) {  // only with non-finite scores (unspecified results)
     b0 = 0;
     S = 0.0;
-    C = 0u;
   }
   double R = S;
-  uint64_t below = C;
-  uint32_t cnt_in = sh.hc[b0];
+  uint64_t below = 0;
   uint64_t prefix = 0;
   int plen = 0;
-  bool in_lds = false;
   bool done = false;
-  uint32_t ncand = 0;
+
+  // Copies the keys of the current range (bin b0 and the prefix) into LDS,
+  // up to kCandCap of them, with one LDS atomic per wave and step; returns
+  // how many there are.  With count_below it also adds the number of keys in
+  // lower bins to `below`.
+  auto collect = [&](bool count_below) -> uint32_t {
+    if (t == 0) {
+      sh.ncand = 0u;
+      sh.kmin = ~0ull;
+      sh.kmax = 0ull;
+    }
+    __syncthreads();
+    uint32_t nbelow = 0u;
+    unsigned long long kmn = ~0ull, kmx = 0ull;
+    E.for_each([&](int64_t i, float s) {
+      const int bin = lin_bin(s, lo, inv);
+      nbelow += bin < b0 ? 1u : 0u;
+      const uint64_t k = key64(s, static_cast<uint32_t>(i));
+      const bool in = bin == b0 && prefix_match(k, prefix, plen);
+      const uint64_t bal = __ballot(in);
+      if (bal != 0ull) {
+        const int leader = __ffsll(static_cast<long long>(bal)) - 1;
+        uint32_t base = 0u;
+        if (lane == leader) base = atomicAdd(&sh.ncand, static_cast<uint32_t>(__popcll(bal)));
+        base = __shfl(base, leader, kWave);
+        if (in) {
+          const uint32_t slot =
+              base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+          if (slot < static_cast<uint32_t>(kCandCap)) sh.cand[slot] = k;
+          kmn = k < kmn ? k : kmn;
+          kmx = k > kmx ? k : kmx;
+        }
+      }
+    });
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const unsigned long long a = __shfl_xor(kmn, o, kWave);
+      const unsigned long long c = __shfl_xor(kmx, o, kWave);
+      kmn = a < kmn ? a : kmn;
+      kmx = c > kmx ? c : kmx;
+    }
+    if (count_below) {
+      nbelow = wave_sum_u32(nbelow);
+      if (lane == 0) sh.wc[wave] = nbelow;
+    }
+    if (lane == 0 && kmn <= kmx) {
+      atomicMin(&sh.kmin, kmn);
+      atomicMax(&sh.kmax, kmx);
+    }
+    __syncthreads();
+    if (count_below) {
+      uint64_t bsum = 0;
+      for (int w = 0; w < kResolveWaves; ++w) bsum += sh.wc[w];
+      below += bsum;
+    }
+    return sh.ncand;
+  };
+
+  uint32_t cnt_in = collect(true);
+  uint32_t ncand = min(cnt_in, static_cast<uint32_t>(kCandCap));
+  bool in_lds = cnt_in <= static_cast<uint32_t>(kCandCap);
+  if (in_lds) {  // skip the leading bits all candidates share
+    const uint64_t diff = static_cast<uint64_t>(sh.kmin) ^ static_cast<uint64_t>(sh.kmax);
+    plen = diff == 0 ? 64 : __clzll(static_cast<long long>(diff));
+    // (a shift by 64 is undefined, so plen == 0 keeps the empty prefix)
+    prefix = plen == 0 ? 0ull
+                       : (plen >= 64 ? static_cast<uint64_t>(sh.kmin)
+                                     : (static_cast<uint64_t>(sh.kmin) >> (64 - plen)));
+  }
   __syncthreads();
 
   // Each pass either copies the range into LDS, finishes it with one wave, or
@@ -369,26 +485,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
   // keys, the bound only guards against non-finite scores.
   for (int guard = 0; guard < 16 && !done; ++guard) {
     if (!in_lds && cnt_in <= static_cast<uint32_t>(kCandCap)) {
-      // Copy the keys of the current range into LDS (exactly cnt_in match).
-      for (int64_t base = 0; base < n; base += kReadBatch * kResolveThreads) {
-        float v[kReadBatch];
-        load_batch(sr, n, base, t, v);
-#pragma unroll
-        for (int u = 0; u < kReadBatch; ++u) {
-          const int64_t i = base + u * kResolveThreads + t;
-          if (i < n && lin_bin(v[u], lo, inv) == b0) {
-            const uint64_t k = key64(v[u], static_cast<uint32_t>(i));
-            if (prefix_match(k, prefix, plen)) {
-              const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-              if (slot < static_cast<uint32_t>(kCandCap)) sh.cand[slot] = k;
-              atomicMin(&sh.kmin, static_cast<unsigned long long>(k));
-              atomicMax(&sh.kmax, static_cast<unsigned long long>(k));
-            }
-          }
-        }
-      }
-      __syncthreads();
-      ncand = min(sh.ncand, static_cast<uint32_t>(kCandCap));
+      cnt_in = collect(false);
+      ncand = min(cnt_in, static_cast<uint32_t>(kCandCap));
       in_lds = true;
       // Skip the leading bits all candidates share.
       const uint64_t diff = static_cast<uint64_t>(sh.kmin) ^ static_cast<uint64_t>(sh.kmax);
@@ -398,6 +496,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
         prefix = plen >= 64 ? static_cast<uint64_t>(sh.kmin)
                             : (static_cast<uint64_t>(sh.kmin) >> (64 - plen));
       }
+      __syncthreads();
     }
     if (in_lds && cnt_in <= static_cast<uint32_t>(kSmallCand)) {
       // Gather the range's keys and let wave 0 finish.
@@ -437,25 +536,20 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
         }
       }
     } else {
-      for (int64_t base = 0; base < n; base += kReadBatch * kResolveThreads) {
-        float v[kReadBatch];
-        load_batch(sr, n, base, t, v);
-#pragma unroll
-        for (int u = 0; u < kReadBatch; ++u) {
-          const int64_t i = base + u * kResolveThreads + t;
-          if (i < n && lin_bin(v[u], lo, inv) == b0) {
-            const uint64_t k = key64(v[u], static_cast<uint32_t>(i));
-            if (prefix_match(k, prefix, plen)) {
-              const int b = static_cast<int>((k >> shift) & static_cast<uint64_t>(nb - 1));
-              atomicAdd(&sh.hc[b], 1u);
-              atomicAdd(&sh.hm[b], static_cast<double>(weight(v[u], m)));
-            }
+      E.for_each([&](int64_t i, float s) {
+        if (lin_bin(s, lo, inv) == b0) {
+          const uint64_t k = key64(s, static_cast<uint32_t>(i));
+          if (prefix_match(k, prefix, plen)) {
+            const int b = static_cast<int>((k >> shift) & static_cast<uint64_t>(nb - 1));
+            atomicAdd(&sh.hc[b], 1u);
+            atomicAdd(&sh.hm[b], static_cast<double>(weight(s, m)));
           }
         }
-      }
+      });
     }
     __syncthreads();
-    int bs = select_bin(sh, nb, R, epsZ, S, C);
+    hist_wave_totals(sh, nb, false);
+    int bs = select_bin(sh, nb, false, R, epsZ, S, C);
     if (bs < 0) {  // only with non-finite scores (unspecified results)
       bs = 0;
       S = 0.0;
@@ -502,6 +596,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
 
 }  // namespace
 
+int resolve_register_row() { return kResolveRegRow; }
+
 int hist_nchunk(int64_t n, int rows) {
   // About two blocks per CU in total and at least 4096 keys per block.
   const int64_t total = n * static_cast<int64_t>(rows);
@@ -512,20 +608,25 @@ int hist_nchunk(int64_t n, int rows) {
 }
 
 hipError_t launch_hist0(const float* scores, int64_t n, int rows, const float2* blkstat,
-                        int nblk, int nchunk, uint32_t* pcnt, double* pmass, hipStream_t st) {
+                        int nblk, int nchunk, double* pmass, hipStream_t st) {
   const int64_t chunk = ceil_div(n, nchunk);
   return launch(hist0_kernel, dim3(static_cast<unsigned>(nchunk) * rows), dim3(256), 0, st,
-                scores, n, chunk, nchunk, blkstat, nblk, pcnt, pmass);
+                scores, n, chunk, nchunk, blkstat, nblk, pmass);
 }
 
 hipError_t launch_resolve(const float* scores, int64_t n, int rows, const float2* blkstat,
-                          int nblk, const uint32_t* pcnt, const double* pmass, int npart,
+                          int nblk, const double* pmass, int npart,
                           double eps, RowSel* rs, int32_t* k_eps, double* tau, double* lse,
                           uint32_t* sel_mask, void* zero_base, size_t zero_bytes,
                           hipStream_t st) {
-  return launch(resolve_kernel, dim3(rows), dim3(kResolveThreads), 0, st, scores, n, blkstat,
-                nblk, pcnt, pmass, npart, eps, rs, k_eps, tau, lse, sel_mask, zero_base,
-                zero_bytes);
+#define CTOPK_RESOLVE(PT)                                                                    \
+  launch(resolve_kernel<PT>, dim3(rows), dim3(kResolveThreads), 0, st, scores, n, blkstat, nblk, \
+         pmass, npart, eps, rs, k_eps, tau, lse, sel_mask, zero_base, zero_bytes)
+  if (npart == 0 && n <= 8 * kResolveThreads) return CTOPK_RESOLVE(8);
+  if (npart == 0 && n <= 16 * kResolveThreads) return CTOPK_RESOLVE(16);
+  if (npart == 0 && n <= kResolveRegRow) return CTOPK_RESOLVE(kResolveRegRow / kResolveThreads);
+  return CTOPK_RESOLVE(0);
+#undef CTOPK_RESOLVE
 }
 
 }  // namespace ctopk

@@ -238,6 +238,21 @@ def test_wide_dynamic_range(ct):
         _logits_case(ct, L, V, eps, "dynamic range")
 
 
+@pytest.mark.parametrize("n", [30000, 70000])
+def test_cut_bin_straddles_zero(ct, n):
+    """Thousands of scores in the first-level bin that contains 0, on both
+    sides of it: the candidates' keys share no leading bit (the sign flips), so
+    the descent starts from an empty prefix.  n = 30000 keeps the row in the
+    select's registers, n = 70000 streams it."""
+    rng = np.random.default_rng(n)
+    L = rng.uniform(-0.01, 0.01, size=(4, n)).astype(np.float32)
+    L[:, 5] = 5.0
+    L[:, 9] = -5.0
+    V = rng.standard_normal((1, n, 64)).astype(np.float32)
+    for eps in (0.3, 0.5, 0.7):
+        _logits_case(ct, L, V, eps, f"cut bin straddles zero n={n}")
+
+
 def test_single_key_rows(ct):
     L = np.array([[3.0], [-2.0]], dtype=np.float32)
     V = np.ones((1, 1, 64), dtype=np.float32)
