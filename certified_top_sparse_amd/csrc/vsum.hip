@@ -301,15 +301,15 @@ int vsum_groups(int rows, int n_v, int v_dtype, int dv) {
 }
 
 int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
-  // Blocks per group: one per tile up to 128, so a short row is read by many
-  // blocks at once; beyond that blocks take several tiles, which keeps the
-  // partial sums (and the final combine) small.
-  (void)rows;
-  (void)n_v;
-  (void)v_dtype;
-  (void)dv;
+  // Blocks per group: about one block per compute unit in total (measured
+  // fastest on MI355X: each block streams several tiles and amortises its
+  // reduction epilogue), and never more blocks than tiles.
   const int64_t tiles = ceil_div(n, kVsumTile);
-  const int64_t tpb = ceil_div(tiles, 128);
+  const int64_t groups = vsum_groups(rows, n_v, v_dtype, dv);
+  int64_t want = ceil_div(kNumCUs, groups);
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  const int64_t tpb = ceil_div(tiles, want);
   return static_cast<int>(ceil_div(tiles, tpb));
 }
 
