@@ -126,7 +126,8 @@ def certify_scores(S, V, eps: float, row_to_v=None, with_diagnostics: bool = Tru
 
     S: [R, n] scores; V: [Hv, n, dv] value rows; row r reads V[row_to_v[r]]
     (default: all rows read V[0]).  Returns a dict of float64/int64 arrays:
-    k_eps [R], tau [R], out [R, dv], lse [R], T_prev [R] (= T_{k_eps - 1}),
+    k_eps [R], tau [R], out [R, dv], out_dense [R, dv] (untruncated softmax
+    output), out_err [R] (= ||out_dense - out||_2), lse [R], T_prev [R] (= T_{k_eps - 1}),
     near_boundary [R] (bool), head_mask [R, n] (bool), and, with diagnostics,
     s_star [R] (score of the last kept key).
     """
@@ -162,10 +163,22 @@ def certify_scores(S, V, eps: float, row_to_v=None, with_diagnostics: bool = Tru
     den = np.sum(wh, axis=-1)
     out = num / den[:, None]
 
+    # Attn: the untruncated softmax output, and the output error of the
+    # truncation, ||Attn - Attn_k||_2 (the quantity the Abstract factorises
+    # as tau * ||mu_tail - mu_head||_2), here straight from its definition.
+    dense = np.empty((R, V.shape[-1]), dtype=np.float64)
+    for g in np.unique(row_to_v):
+        sel = row_to_v == g
+        dense[sel] = w[sel] @ V[g]
+    dense /= Z[:, None]
+    out_err = np.linalg.norm(dense - out, axis=-1)
+
     res = {
         "k_eps": k.astype(np.int64),
         "tau": tau,
         "out": out,
+        "out_dense": dense,
+        "out_err": out_err,
         "lse": np.log(Z) + np.max(S, axis=-1),
         "T_prev": T_prev,
         "near_boundary": near,

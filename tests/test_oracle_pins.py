@@ -106,6 +106,9 @@ def test_head_tail_factorisation_and_diameter_bound(n, sigma, eps, dv):
         np.testing.assert_allclose(err, fac, rtol=1e-9, atol=1e-14)
         ne = np.linalg.norm(err)
         assert abs(ne - r["tau"][i] * np.linalg.norm(mu_t - mu_h)) <= 1e-10 * max(ne, 1e-300)
+        # the oracle's dense output and output error against the library softmax
+        np.testing.assert_allclose(r["out_dense"][i], attn, rtol=1e-10, atol=1e-14)
+        assert abs(r["out_err"][i] - ne) <= 1e-9 * max(ne, 1e-300) + 1e-15
         assert ne <= r["tau"][i] * oracle.diam_head_tail(V[0], head) * (1 + 1e-12)
 
 
