@@ -85,7 +85,7 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   L.blkstat = off;
   off += up(static_cast<size_t>(rows) * L.nblk * sizeof(float2));
   L.part = off;
-  off += up(static_cast<size_t>(rows) * L.nchunk * (dv + 1) * sizeof(float));
+  off += up(static_cast<size_t>(rows) * L.nchunk * 2 * (dv + 1) * sizeof(float));  // head + tail
   L.pmass = off;
   off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(double));
   L.scores = off;
@@ -164,7 +164,8 @@ int validate_args(const ctopk_args* a) {
     return fail(CTOPK_ERR_ALIGN, "q, K and V must be 16-byte aligned");
   if (!aligned(a->out, 4) || !aligned(a->k_eps, 4) || !aligned(a->tau, 8) ||
       (a->scores && !aligned(a->scores, 4)) || (a->sel_mask && !aligned(a->sel_mask, 4)) ||
-      (a->lse && !aligned(a->lse, 8)) || (a->head_scale && !aligned(a->head_scale, 4)))
+      (a->lse && !aligned(a->lse, 8)) || (a->head_scale && !aligned(a->head_scale, 4)) ||
+      (a->out_err && !aligned(a->out_err, 8)) || (a->out_dense && !aligned(a->out_dense, 4)))
     return fail(CTOPK_ERR_ALIGN, "outputs must be aligned to their element size");
   if (a->workspace != nullptr) {
     if (!aligned(a->workspace, kAlign)) return fail(CTOPK_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -209,7 +210,9 @@ size_t ctopk_workspace_bytes(int64_t n, int32_t d, int32_t n_q_heads, int32_t n_
   if (n < 1 || n > kMaxN || (d != 64 && d != 128) || n_q_heads < 1 || n_kv_heads < 1 ||
       n_q_heads % n_kv_heads != 0 || (dtype != CTOPK_F32 && dtype != CTOPK_BF16))
     return 0;
-  if (ctopk::encoder_supported(dtype, d, n, n_q_heads, n_kv_heads)) return kAlign;
+  // Sized for the general path, which every call can take (the encoder-shaped
+  // path needs none, but calls asking for the output certificate use the
+  // general path on any shape).
   return layout(n, d, n_q_heads, n_kv_heads, dtype, true).total;
 }
 
@@ -232,7 +235,9 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   if (rc != CTOPK_OK) return rc;
   const float default_scale = static_cast<float>(1.0 / sqrt(static_cast<double>(a->d)));
 
-  if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads)) {
+  const bool certificate = a->out_err != nullptr || a->out_dense != nullptr;
+  if (!certificate &&
+      ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads)) {
     rc = hip_check(ctopk::launch_encoder(a->q, a->K, a->V, a->d, a->head_scale, default_scale,
                                          a->n, a->n_q_heads, a->n_kv_heads, a->eps, a->out,
                                          a->k_eps, a->tau, a->sel_mask, a->scores, a->lse, st),
@@ -274,7 +279,7 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;
   rc = hip_check(ctopk::launch_vsum(scores, a->n, rows, a->n_kv_heads, a->V, a->dtype, a->d, rs,
-                                    part, L.nchunk, a->out, st),
+                                    part, L.nchunk, a->out, a->out_dense, a->out_err, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
   return ok();
@@ -344,7 +349,7 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;
   rc = hip_check(ctopk::launch_vsum(logits, n, rows, n_v, V, v_dtype, dv, rs, part, L.nchunk,
-                                    out, st),
+                                    out, nullptr, nullptr, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
   return ok();

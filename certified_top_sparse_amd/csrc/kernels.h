@@ -78,10 +78,13 @@ hipError_t launch_resolve(const float* scores, int64_t n, int rows, const float2
 int vsum_groups(int rows, int n_v, int v_dtype, int dv);
 int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv);
 // K4: w * v over kept keys into part [rows, nchunk, dv + 1] (numerator and
-// weight sum per block), then a finalize kernel writes out = num / den.
+// weight sum per block), then a finalize kernel writes out = num / den.  With
+// dense or err non-NULL the tail is accumulated too (part [rows, nchunk,
+// 2 (dv + 1)]) and the finalize also writes the untruncated output and the
+// output error ||Attn - Attn_k||_2 per row.
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
                        int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
-                       hipStream_t st);
+                       float* dense, double* err, hipStream_t st);
 
 // Encoder-shaped path (all queries of a head, n <= 1024, bf16, MFMA QK^T).
 hipError_t launch_encoder(const void* q, const void* K, const void* V, int d,

@@ -72,7 +72,11 @@ template <typename T, int D>
 constexpr int kGroupMax = (sizeof(typename AccOf<T>::type) == 8 && D == 128) ? 4 : 8;
 constexpr int kVsumWaves = kVsumThreads / kWave;
 
-template <typename T, int D, int GB>
+// With TAIL the kernel also accumulates the tail: w * v and w over the keys
+// outside the head, so the combine can form the untruncated output and the
+// truncation's output error; partials then hold [head num | head w | tail num
+// | tail w] per (row, block).
+template <typename T, int D, int GB, bool TAIL>
 __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
     const float* __restrict__ scores, int64_t n, int G, const T* __restrict__ V,
     const RowSel* __restrict__ rs, float* __restrict__ part, int nchunk, int tpb) {
@@ -86,8 +90,9 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
   constexpr int PPL = (NPAIR + kWave - 1) / kWave;  // weights per lane
   static_assert(kVsumTile % (kVsumWaves * RPW) == 0, "whole rows per lane");
   static_assert(GB <= LPR && kWave % GB == 0, "head groups tile the wave");
-  __shared__ Acc s_red[kVsumWaves][GB * D];
-  __shared__ double s_wsum[kVsumWaves][GB];
+  constexpr int NS = TAIL ? 2 : 1;  // head sums, and tail sums with TAIL
+  __shared__ Acc s_red[NS][kVsumWaves][GB * D];
+  __shared__ double s_wsum[NS][kVsumWaves][GB];
   __shared__ float s_w[kVsumWaves][PASS][GB];  // wave-private weight staging
 
   const int chunk = blockIdx.x;
@@ -118,11 +123,17 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
   const float* srow = scores + static_cast<size_t>(h0 + min(hw, nh - 1)) * static_cast<size_t>(n);
 
   Acc acc[GB][EPL];
+  Acc acct[TAIL ? GB : 1][EPL];
 #pragma unroll
   for (int j = 0; j < GB; ++j)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = Acc(0);
-  double wsum = 0.0;  // weight of head hw over this lane's pairs
+#pragma unroll
+  for (int j = 0; j < (TAIL ? GB : 1); ++j)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acct[j][e] = Acc(0);
+  double wsum = 0.0;   // weight of head hw over this lane's pairs
+  double wsumt = 0.0;  // and of its tail (TAIL)
 
   for (int tb = 0; tb < tpb; ++tb) {
     const int64_t p0 = (static_cast<int64_t>(chunk) * tpb + tb) * kVsumTile + wave * PASS;
@@ -148,9 +159,17 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
         const int key = pair / GB;
         const int64_t r = p0 + key;
         const bool kept = r < n && key64(s[q], static_cast<uint32_t>(r)) >= thr;
-        const float w = kept ? weight(s[q], m) : 0.0f;
-        wsum += static_cast<double>(w);
-        s_w[wave][key][hw] = w;
+        if constexpr (TAIL) {
+          // staged as +w for head keys and -w for tail keys
+          const float w = r < n ? weight(s[q], m) : 0.0f;
+          wsum += kept ? static_cast<double>(w) : 0.0;
+          wsumt += kept ? 0.0 : static_cast<double>(w);
+          s_w[wave][key][hw] = kept ? w : -w;
+        } else {
+          const float w = kept ? weight(s[q], m) : 0.0f;
+          wsum += static_cast<double>(w);
+          s_w[wave][key][hw] = w;
+        }
       }
     }
     // s_w is private to this wave, and one wave's LDS operations complete in
@@ -166,10 +185,23 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
       for (int j = 0; j < GB; ++j) wj[j] = s_w[wave][key][j];
       float v[EPL];
       VSlice<T>::load(u[it], v);
+      if constexpr (TAIL) {
 #pragma unroll
-      for (int j = 0; j < GB; ++j)
+        for (int j = 0; j < GB; ++j) {
+          const Acc wh = static_cast<Acc>(fmaxf(wj[j], 0.0f));
+          const Acc wt = static_cast<Acc>(fmaxf(-wj[j], 0.0f));
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] += static_cast<Acc>(wj[j]) * static_cast<Acc>(v[e]);
+          for (int e = 0; e < EPL; ++e) {
+            acc[j][e] += wh * static_cast<Acc>(v[e]);
+            acct[j][e] += wt * static_cast<Acc>(v[e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[j][e] += static_cast<Acc>(wj[j]) * static_cast<Acc>(v[e]);
+      }
     }
   }
 
@@ -181,31 +213,49 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
     for (int j = 0; j < GB; ++j)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], o, kWave);
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int j = 0; j < GB; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acct[j][e] += __shfl_xor(acct[j][e], o, kWave);
+    }
   }
 #pragma unroll
-  for (int o = GB; o < kWave; o <<= 1) wsum += __shfl_xor(wsum, o, kWave);
+  for (int o = GB; o < kWave; o <<= 1) {
+    wsum += __shfl_xor(wsum, o, kWave);
+    if constexpr (TAIL) wsumt += __shfl_xor(wsumt, o, kWave);
+  }
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < GB; ++j)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_red[wave][j * D + seg * EPL + e] = acc[j][e];
+      for (int e = 0; e < EPL; ++e) {
+        s_red[0][wave][j * D + seg * EPL + e] = acc[j][e];
+        if constexpr (TAIL) s_red[NS - 1][wave][j * D + seg * EPL + e] = acct[j][e];
+      }
   }
-  if (lane < GB) s_wsum[wave][lane] = wsum;
+  if (lane < GB) {
+    s_wsum[0][wave][lane] = wsum;
+    if constexpr (TAIL) s_wsum[NS - 1][wave][lane] = wsumt;
+  }
   __syncthreads();
-  const size_t pstride = static_cast<size_t>(D + 1);
-  for (int idx = t; idx < GB * (D + 1); idx += kVsumThreads) {
-    const int j = idx / (D + 1);
-    const int e = idx - j * (D + 1);
+  const size_t pstride = static_cast<size_t>(NS * (D + 1));
+  for (int idx = t; idx < NS * GB * (D + 1); idx += kVsumThreads) {
+    const int part_k = idx / (GB * (D + 1));  // 0 head, 1 tail
+    const int rem = idx - part_k * GB * (D + 1);
+    const int j = rem / (D + 1);
+    const int e = rem - j * (D + 1);
     if (j < nh) {
       double sum = 0.0;
       if (e < D) {
 #pragma unroll
-        for (int g = 0; g < kVsumWaves; ++g) sum += static_cast<double>(s_red[g][j * D + e]);
+        for (int g = 0; g < kVsumWaves; ++g) sum += static_cast<double>(s_red[part_k][g][j * D + e]);
       } else {
 #pragma unroll
-        for (int g = 0; g < kVsumWaves; ++g) sum += s_wsum[g][j];
+        for (int g = 0; g < kVsumWaves; ++g) sum += s_wsum[part_k][g][j];
       }
-      part[(static_cast<size_t>(h0 + j) * nchunk + chunk) * pstride + e] = static_cast<float>(sum);
+      part[(static_cast<size_t>(h0 + j) * nchunk + chunk) * pstride + part_k * (D + 1) + e] =
+          static_cast<float>(sum);
     }
   }
 
@@ -216,13 +266,22 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
 // then added in k order.  Runs as its own kernel so that the kernel boundary
 // makes every block's partials visible (an in-kernel device-scope fence costs
 // a full L2 writeback and invalidate per block on this multi-XCD part).
+// With tail sums (ns == 2) it also writes the untruncated output
+// (num_head + num_tail) / (w_head + w_tail) and the output error
+// ||Attn - Attn_k||_2 = tau * ||mu_tail - mu_head||_2, tau = w_tail / (w_head +
+// w_tail) (the head-tail factorisation in the Abstract of "A Mathematical
+// Theory of Top-k Sparse Attention via Total Variation Distance", arXiv
+// 2512.07647).
 __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict__ part,
-                                                        int nchunk, int dv,
-                                                        float* __restrict__ out) {
+                                                        int nchunk, int dv, int ns,
+                                                        float* __restrict__ out,
+                                                        float* __restrict__ dense,
+                                                        double* __restrict__ err) {
   __shared__ double s_col[1024];
+  __shared__ double s_e2[16];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
-  const int cols = dv + 1;
+  const int cols = ns * (dv + 1);
   const int NK = 1024 / cols;
   const int k = t / cols;
   const int e = t - k * cols;
@@ -243,39 +302,73 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict_
   }
   s_col[t] = a;
   __syncthreads();
+  double e2 = 0.0;
+  double wt_tau = 0.0;
   if (t < dv) {
-    double num = 0.0, den = 0.0;
+    double num = 0.0, den = 0.0, numt = 0.0, dent = 0.0;
     for (int j = 0; j < NK; ++j) {
       num += s_col[j * cols + t];
       den += s_col[j * cols + dv];
+      if (ns == 2) {
+        numt += s_col[j * cols + dv + 1 + t];
+        dent += s_col[j * cols + 2 * dv + 1];
+      }
     }
-    out[static_cast<size_t>(row) * dv + t] = static_cast<float>(num / den);
+    const double mh = num / den;
+    out[static_cast<size_t>(row) * dv + t] = static_cast<float>(mh);
+    if (ns == 2) {
+      if (dense != nullptr)
+        dense[static_cast<size_t>(row) * dv + t] = static_cast<float>((num + numt) / (den + dent));
+      const double diff = dent > 0.0 ? numt / dent - mh : 0.0;
+      e2 = diff * diff;
+      wt_tau = dent / (den + dent);
+    }
+  }
+  if (ns == 2 && err != nullptr) {  // uniform: the whole block reduces ||mu_t - mu_h||^2
+    e2 = wave_sum(e2);
+    if ((t & 63) == 0) s_e2[t >> 6] = e2;
+    __syncthreads();
+    if (t == 0) {
+      double s2 = 0.0;
+      for (int w = 0; w < 16; ++w) s2 += s_e2[w];
+      err[row] = wt_tau * sqrt(s2);
+    }
   }
 }
 
 template <typename T, int D, int GB>
 hipError_t launch_t(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                    const RowSel* rs, float* part, int nchunk, float* out, hipStream_t st) {
+                    const RowSel* rs, float* part, int nchunk, float* out, float* dense,
+                    double* err, hipStream_t st) {
   const int G = rows / n_v;
   const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
   dim3 grid(nchunk, n_v, static_cast<unsigned>(ceil_div(G, GB)));
-  const hipError_t e = launch(vsum_kernel<T, D, GB>, grid, dim3(kVsumThreads), 0, st, scores, n,
-                              G, static_cast<const T*>(V), rs, part, nchunk, tpb);
+  const bool tail = dense != nullptr || err != nullptr;
+  const hipError_t e =
+      tail ? launch(vsum_kernel<T, D, GB, true>, grid, dim3(kVsumThreads), 0, st, scores, n, G,
+                    static_cast<const T*>(V), rs, part, nchunk, tpb)
+           : launch(vsum_kernel<T, D, GB, false>, grid, dim3(kVsumThreads), 0, st, scores, n, G,
+                    static_cast<const T*>(V), rs, part, nchunk, tpb);
   if (e != hipSuccess) return e;
-  return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, part, nchunk, D, out);
+  return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, part, nchunk, D, tail ? 2 : 1,
+                out, dense, err);
 }
 
 template <typename T, int D>
 hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                    const RowSel* rs, float* part, int nchunk, float* out, hipStream_t st) {
+                    const RowSel* rs, float* part, int nchunk, float* out, float* dense,
+                    double* err, hipStream_t st) {
   const int G = rows / n_v;
-  if (G == 1) return launch_t<T, D, 1>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
-  if (G == 2) return launch_t<T, D, 2>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+  if (G == 1)
+    return launch_t<T, D, 1>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+  if (G == 2)
+    return launch_t<T, D, 2>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
   if constexpr (kGroupMax<T, D> == 4) {
-    return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+    return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
   } else {
-    if (G <= 4) return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
-    return launch_t<T, D, 8>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+    if (G <= 4)
+      return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+    return launch_t<T, D, 8>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
   }
 }
 
@@ -283,14 +376,16 @@ hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const voi
 
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
                        int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
-                       hipStream_t st) {
+                       float* dense, double* err, hipStream_t st) {
   if (v_dtype == 1) {
     if (dv == 128)
-      return launch_d<uint16_t, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
-    return launch_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+      return launch_d<uint16_t, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err,
+                                     st);
+    return launch_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
   }
-  if (dv == 128) return launch_d<float, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
-  return launch_d<float, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
+  if (dv == 128)
+    return launch_d<float, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+  return launch_d<float, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
 }
 
 int vsum_groups(int rows, int n_v, int v_dtype, int dv) {

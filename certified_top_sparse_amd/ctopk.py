@@ -62,6 +62,8 @@ class CtopkArgs(ctypes.Structure):
         ("sel_mask", ctypes.c_void_p),
         ("scores", ctypes.c_void_p),
         ("lse", ctypes.c_void_p),
+        ("out_err", ctypes.c_void_p),
+        ("out_dense", ctypes.c_void_p),
     ]
 
 
@@ -195,7 +197,8 @@ def ctopk_certify(q, K, V, eps, out=None, k_eps=None, tau=None, stream=None):
 
 
 def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=None,
-              tau=None, sel_mask=None, scores=None, lse=None) -> CtopkArgs:
+              tau=None, sel_mask=None, scores=None, lse=None, out_err=None,
+              out_dense=None) -> CtopkArgs:
     n_q, d = q.shape
     n_kv, n, _ = K.shape
     a = CtopkArgs()
@@ -207,18 +210,21 @@ def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=
     a.workspace = None if workspace is None else workspace.data_ptr()
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     for f, t in (("out", out), ("k_eps", k_eps), ("tau", tau), ("sel_mask", sel_mask),
-                 ("scores", scores), ("lse", lse)):
+                 ("scores", scores), ("lse", lse), ("out_err", out_err),
+                 ("out_dense", out_dense)):
         setattr(a, f, None if t is None else t.data_ptr())
     return a
 
 
 def ctopk_certify_ex(q, K, V, eps, *, head_scale=None, workspace=None, want_mask=False,
-                     want_scores=False, want_lse=False, stream=None):
+                     want_scores=False, want_lse=False, want_err=False, want_dense=False,
+                     stream=None):
     """Full form: q [Hq, d], K/V [Hkv, n, d] in bf16 or fp32, optional per-head
     scale [Hq] fp32 and caller workspace (uint8 tensor).
 
     Returns a dict with out, k_eps, tau and, on request, sel_mask
-    [Hq, ceil(n/32)] int32 bit words, scores [Hq, n] fp32 and lse [Hq] fp64."""
+    [Hq, ceil(n/32)] int32 bit words, scores [Hq, n] fp32, lse [Hq] fp64,
+    out_err [Hq] fp64 (||Attn - Attn_k||_2) and out_dense [Hq, d] fp32 (Attn)."""
     import torch
     lib = load()
     for name, t in (("q", q), ("K", K), ("V", V)):
@@ -239,13 +245,18 @@ def ctopk_certify_ex(q, K, V, eps, *, head_scale=None, workspace=None, want_mask
         res["scores"] = torch.empty((n_q, n), dtype=torch.float32, device=dev)
     if want_lse:
         res["lse"] = torch.empty(n_q, dtype=torch.float64, device=dev)
+    if want_err:
+        res["out_err"] = torch.empty(n_q, dtype=torch.float64, device=dev)
+    if want_dense:
+        res["out_dense"] = torch.empty((n_q, d), dtype=torch.float32, device=dev)
     if head_scale is not None:
         _require_cuda_contig("head_scale", head_scale)
         if head_scale.dtype != torch.float32 or head_scale.numel() != n_q:
             raise ValueError("head_scale must be float32 with one entry per query head")
     a = make_args(q, K, V, eps, head_scale=head_scale, workspace=workspace, out=res["out"],
                   k_eps=res["k_eps"], tau=res["tau"], sel_mask=res.get("sel_mask"),
-                  scores=res.get("scores"), lse=res.get("lse"))
+                  scores=res.get("scores"), lse=res.get("lse"), out_err=res.get("out_err"),
+                  out_dense=res.get("out_dense"))
     _check(lib.ctopk_certify_ex(ctypes.byref(a), _stream(stream)))
     return res
 

@@ -103,6 +103,12 @@ typedef struct ctopk_args {
   float* scores;            /* optional [n_q_heads, n] float32 scores as computed;
                                NULL: kept in the workspace                            */
   double* lse;              /* optional [n_q_heads] log-sum-exp of the scores; NULL    */
+  /* Output-level certificate (head-tail factorisation in the Abstract): when
+     either pointer is non-NULL the value pass also accumulates the tail.      */
+  double* out_err;          /* optional [n_q_heads] ||Attn - Attn_k||_2 = tau *
+                               ||mu_tail - mu_head||_2 (fp64); NULL: skip          */
+  float* out_dense;         /* optional [n_q_heads, d] untruncated softmax output
+                               Attn (fp32); NULL: skip                              */
 } ctopk_args;
 
 /*
@@ -110,12 +116,14 @@ typedef struct ctopk_args {
  * scale, caller-owned workspace, optional selection mask, scores and lse.
  * bf16 inputs with d 64 or 128, n <= 512 and n_q_heads/n_kv_heads >= 64 (all
  * queries of a head against few keys, as in an encoder) run on a fused path
- * whose QK^T and head-only output use MFMA; it needs no workspace.  Results
- * follow the same definitions on both paths.
+ * whose QK^T and head-only output use MFMA; it needs no workspace.  Calls that
+ * ask for out_err or out_dense take the general path.  Results follow the same
+ * definitions on both paths.
  */
 CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
 
-/* Device scratch bytes ctopk_certify_ex needs for these sizes (0 on bad sizes). */
+/* Device scratch bytes ctopk_certify_ex needs for these sizes (0 on bad sizes);
+ * enough for every call with these sizes, whichever path it takes. */
 CTOPK_API size_t ctopk_workspace_bytes(int64_t n, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
                              int32_t dtype);
 

@@ -96,7 +96,8 @@ def test_eps_errors(lib, eps):
 
 @pytest.mark.parametrize("field,value", [("q", A16 + 8), ("K", A16 + 2), ("V", A16 + 4),
                                          ("out", A16 + 2), ("tau", A16 + 4),
-                                         ("k_eps", A16 + 1)])
+                                         ("k_eps", A16 + 1), ("out_err", A16 + 4),
+                                         ("out_dense", A16 + 2)])
 def test_alignment_errors(lib, field, value):
     assert ct.ctopk_validate(good_args(**{field: value})) == cb.CTOPK_ERR_ALIGN
 
@@ -109,6 +110,15 @@ def test_workspace_checks(lib):
         cb.CTOPK_ERR_WORKSPACE
     assert ct.ctopk_validate(good_args(workspace=A16 * 8 + 16, workspace_bytes=need)) == \
         cb.CTOPK_ERR_ALIGN
+
+
+def test_struct_layout_matches_header():
+    # the binding's mirror of ctopk_args must keep the header's field order
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct ctopk_args {"):text.index("} ctopk_args;")]
+    body = body[body.index("{") + 1:]
+    names = re.findall(r"\b(\w+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert names == [f for f, _ in cb.CtopkArgs._fields_]
 
 
 def test_workspace_sizes(lib):

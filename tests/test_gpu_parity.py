@@ -190,6 +190,63 @@ def test_determinism(ct):
 
 
 # ---------------------------------------------------------------------------
+# output-level certificate: ||Attn - Attn_k||_2 and the untruncated output
+# ---------------------------------------------------------------------------
+def _certificate_case(ct, wl, eps, label, rtol, same_path=True):
+    _say(f"certificate {label} eps={eps} n={wl['n']} Hq={wl['n_q_heads']} d={wl['d']}")
+    q, K, V = dev(wl["q"]), dev(wl["K"]), dev(wl["V"])
+    hs = dev(wl["head_scale"])
+    plain = ct.ctopk_certify_ex(q, K, V, eps, head_scale=hs)
+    res = ct.ctopk_certify_ex(q, K, V, eps, head_scale=hs, want_err=True, want_dense=True)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in res.items()}
+    p = {k: v.cpu().numpy() for k, v in plain.items()}
+    if same_path:  # asking for the certificate leaves the certified result unchanged
+        assert np.array_equal(g["k_eps"], p["k_eps"])
+        assert np.array_equal(g["out"], p["out"])
+    n_q, n_kv = wl["n_q_heads"], wl["n_kv_heads"]
+    G = n_q // n_kv
+    q64, K64, V64 = oracle.as_f64(wl["q"]), oracle.as_f64(wl["K"]), oracle.as_f64(wl["V"])
+    sc = np.asarray(wl["head_scale"], dtype=np.float32).astype(np.float64)
+    S = np.stack([sc[h] * (K64[h // G] @ q64[h]) for h in range(n_q)])
+    ref = oracle.certify_scores(S, V64, eps, np.arange(n_q) // G)
+    kok = g["k_eps"] == ref["k_eps"]
+    assert kok.sum() >= n_q - int(ref["near_boundary"].sum())
+    dense_err = rel_l2(g["out_dense"], ref["out_dense"])
+    assert dense_err.max() <= rtol, f"dense output rel L2 {dense_err.max():.3e}"
+    e_ref = ref["out_err"][kok]
+    e_gpu = g["out_err"][kok]
+    rel = np.abs(e_gpu - e_ref) / np.maximum(e_ref, 1e-12)
+    assert rel.max() <= rtol, f"output error off by {rel.max():.3e} (relative)"
+    print(f"{label}: dense rel L2 max {dense_err.max():.2e}, ||Attn - Attn_k|| rel err max "
+          f"{rel.max():.2e}, mean ||Attn - Attn_k|| {e_ref.mean():.3e}", flush=True)
+
+
+@pytest.mark.parametrize("eps", [0.01, 0.1])
+def test_certificate_gqa_decode(ct, eps):
+    _certificate_case(ct, workloads.gqa_decode(n=6000), eps, "gqa_decode n=6000", 1e-3)
+
+
+def test_certificate_gqa_decode_full(ct):
+    _certificate_case(ct, workloads.gqa_decode(), 0.01, "gqa_decode n=32768 (full)", 1e-3)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_certificate_fp32(ct, d, G):
+    wl = workloads.gqa_decode(n=2500, n_q=2 * G, n_kv=2, d=d, planted=3)
+    wl = dict(wl, q=workloads.bf16_to_f32(wl["q"]), K=workloads.bf16_to_f32(wl["K"]),
+              V=workloads.bf16_to_f32(wl["V"]), dtype="f32")
+    _certificate_case(ct, wl, 0.05, f"fp32 d={d} G={G}", 1e-5)
+
+
+def test_certificate_on_encoder_shape(ct):
+    # all-queries shapes take the general path when the certificate is asked for
+    wl = workloads.encoder(batch=1, heads=2)
+    _certificate_case(ct, wl, 0.01, "encoder shape 1x2x512x64", 1e-3, same_path=False)
+
+
+# ---------------------------------------------------------------------------
 # adversarial select inputs
 # ---------------------------------------------------------------------------
 def _logits_case(ct, L, V, eps, label, n_v=1, out_rtol=OUT_RTOL_F32):
