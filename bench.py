@@ -43,6 +43,9 @@ PEAK_HBM_GBPS = 8000.0
 # event pair is recorded back to back and reads ~0), select, value stream,
 # output combine.
 KERNELS = ("score_scan", "hist0", "resolve", "vsum", "finalize")
+# Rows of at most this many keys are resolved in registers, without the
+# separate level-0 histogram kernel (whose event pair then times no kernel).
+REGISTER_ROW_KEYS = 32768
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_scan_gqa_decode_n32768_pmc.md")
 SCAN_SOURCE = os.path.join(ROOT, "certified_top_sparse_amd", "csrc", "score_scan.hip")
 
@@ -351,6 +354,8 @@ def main():
                         for row in evs])
         for j, name in enumerate(KERNELS):
             kernel_us[name] = round(float(per[:, j].mean()) * 1e3, 3)
+        if n <= REGISTER_ROW_KEYS:  # no level-0 histogram kernel is launched
+            kernel_us["hist0"] = None
         scan_us = float(per[:, 0].mean()) * 1e3
         for row in evs:
             for e in row:

@@ -35,38 +35,46 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kEncWaves = 4;
+constexpr int kEncWaves = 8;              // 4 row groups x 2 key halves
 constexpr int kEncThreads = kEncWaves * kWave;
-constexpr int kEncRows = 16 * kEncWaves;  // query rows per workgroup
+constexpr int kEncRows = 64;              // query rows per workgroup
 constexpr int kEncMaxKeys = 512;
 constexpr int kEncMinGroup = 64;
 constexpr int kEncBins = 64;              // bins per row and level
 constexpr int kHistStride = kEncBins + 1; // doubles per histogram row (bank padding)
-constexpr int kLaneCand = 12;             // candidate slots per lane
+constexpr int kLaneCand = 8;              // candidate slots per lane
+constexpr int kLaneSlots = kLaneCand + 1; // plus one slot that takes every other write
 constexpr int kFinishMax = 32;            // exact finish at or below this many candidates
 // Every level below the first drops at least one candidate, so n levels suffice.
 constexpr int kMaxLevels = 2 * kEncMaxKeys;
 
-struct WaveSel {  // per-wave scratch of the select phase
+struct GroupSel {  // select scratch of one row group (two waves), aliased with the stages
   double hist[16 * kHistStride];
-  uint64_t key[kWave * kLaneCand];
-  float w[kWave * kLaneCand];
+  uint64_t key[2 * kWave * kLaneSlots];
+  float w[2 * kWave * kLaneCand];
 };
-constexpr int kEncSmem = kEncWaves * static_cast<int>(sizeof(WaveSel));
+struct GroupXchg {  // per-row values the two waves of a row group exchange
+  float f[2][16][4];   // max, min, candidate min, candidate max
+  int i[2][16][4];     // candidate count, overflow flag, head count
+  uint64_t k[2][16];   // best key
+  double d[2][16];     // its lower mass
+  int lcnt[2][kWave];  // candidates per lane
+  uint32_t bm[16][16]; // candidate bitmap per row (tied scores)
+};
+constexpr int kEncSmem = 4 * static_cast<int>(sizeof(GroupSel));
 
 template <int D>
 struct Geo {
-  static constexpr int kChunk = D == 64 ? 128 : 64;  // keys per staged chunk
+  static constexpr int kChunk = D == 64 ? 128 : 64;  // keys per staged chunk and half
   static constexpr int kKStride = D + 8;              // bf16 per staged K row
-  static constexpr int kVStride = kChunk + 8;         // bf16 per staged V^T row (one feature)
-  static constexpr int kTiles = kChunk / 16;          // 16-key tiles per chunk
 };
-static_assert(Geo<64>::kChunk * Geo<64>::kKStride * 2 <= kEncSmem, "K stage");
-static_assert(64 * Geo<64>::kVStride * 2 <= kEncSmem, "V stage");
-static_assert(Geo<128>::kChunk * Geo<128>::kKStride * 2 <= kEncSmem, "K stage");
-static_assert(128 * Geo<128>::kVStride * 2 <= kEncSmem, "V stage");
+static_assert(2 * Geo<64>::kChunk * Geo<64>::kKStride * 2 <= kEncSmem, "K stage");
+static_assert(2 * 64 * (Geo<64>::kChunk + 8) * 2 <= kEncSmem, "V stage");
+static_assert(2 * Geo<128>::kChunk * Geo<128>::kKStride * 2 <= kEncSmem, "K stage");
+static_assert(2 * 128 * (Geo<128>::kChunk + 8) * 2 <= kEncSmem, "V stage");
+static_assert(4 * 16 * 128 * 4 <= kEncSmem, "half combine");
 
-// Reductions over the four lanes (r, 0..3) of a row.
+// Reductions over the four lanes (r, 0..3) of a row within one wave.
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16, kWave));
   return fmaxf(v, __shfl_xor(v, 32, kWave));
@@ -75,10 +83,6 @@ __device__ __forceinline__ float row_min(float v) {
   v = fminf(v, __shfl_xor(v, 16, kWave));
   return fminf(v, __shfl_xor(v, 32, kWave));
 }
-__device__ __forceinline__ double row_sum(double v) {
-  v += __shfl_xor(v, 16, kWave);
-  return v + __shfl_xor(v, 32, kWave);
-}
 __device__ __forceinline__ int row_sum(int v) {
   v += __shfl_xor(v, 16, kWave);
   return v + __shfl_xor(v, 32, kWave);
@@ -86,12 +90,6 @@ __device__ __forceinline__ int row_sum(int v) {
 __device__ __forceinline__ uint32_t row_or(uint32_t v) {
   v |= __shfl_xor(v, 16, kWave);
   return v | __shfl_xor(v, 32, kWave);
-}
-
-// LDS writes of one lane become visible to the other lanes of its wave.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
 }
 
 // Bin of a score at one level.  Both forms are non-decreasing in s, so every
@@ -108,6 +106,14 @@ __device__ __forceinline__ int ukey_bin(float s, uint32_t ulo, float inv) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// weight as bf16 high part (low half-word) and bf16 residual (high half-word)
+__device__ __forceinline__ uint32_t pack_weight(float w) {
+  const __bf16 wh = static_cast<__bf16>(w);
+  const __bf16 wl = static_cast<__bf16>(w - static_cast<float>(wh));
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wh)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wl)) << 16);
+}
+
 template <int D, int NT>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void encoder_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
@@ -116,11 +122,19 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
     double* __restrict__ tau, uint32_t* __restrict__ sel_mask, float* __restrict__ scores_out,
     double* __restrict__ lse) {
   using Gm = Geo<D>;
-  constexpr int kChunks = NT / Gm::kTiles;
-  static_assert(NT % Gm::kTiles == 0, "tiles per chunk");
+  constexpr int NTH = NT / 2;                             // tiles per key half
+  constexpr int H = 16 * NTH;                             // keys per half
+  constexpr int CK = H < Gm::kChunk ? H : Gm::kChunk;     // keys per staged chunk
+  constexpr int TPC = CK / 16;                            // tiles per chunk
+  constexpr int NCH = H / CK;                             // chunks per half
+  constexpr int KS = Gm::kKStride;
+  constexpr int VS = CK + 8;                              // bf16 per staged V^T row
+  static_assert(H % CK == 0 && TPC % 2 == 0, "chunking");
   __shared__ __align__(16) unsigned char smem[kEncSmem];
+  __shared__ GroupXchg xs[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave >> 1, kh = wave & 1;  // row group, key half
   const int r = lane & 15, g = lane >> 4;
   // Workgroups are dealt to the 8 XCDs round robin by id; when the count
   // allows, give every row tile of one head the same id mod 8, so that head's
@@ -131,56 +145,53 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
                       ? static_cast<int>(blockIdx.x % 8) * (nwg / 8) + static_cast<int>(blockIdx.x / 8)
                       : static_cast<int>(blockIdx.x);
   const int h = lin / tiles;
-  const int qr = (lin % tiles) * kEncRows + wave * 16 + r;
+  const int qr = (lin % tiles) * kEncRows + rg * 16 + r;
   const bool row_ok = qr < G;
   const int64_t row = static_cast<int64_t>(h) * G + (row_ok ? qr : G - 1);
   const float scale = head_scale ? head_scale[row] : default_scale;
   const uint16_t* Kh = K + static_cast<size_t>(h) * n * D;
   const uint16_t* Vh = V + static_cast<size_t>(h) * n * D;
-  // Key 16 t + 4 g + e exists iff 16 t + e < nl; tests against nl compare a
-  // constant with one register instead of materialising 4 NT key indices.
-  int nl = n - 4 * g;
+  GroupXchg& xg = xs[rg];
+  const int kbase = kh * H;  // this wave's keys: kbase + 16 t + 4 g + e, t < NTH
+  // Key kbase + 16 t + 4 g + e exists iff 16 t + e < nl; tests against nl compare a
+  // constant with one register instead of materialising per-key indices.
+  int nl = n - kbase - 4 * g;
 
-  // ---- 1. scores: S^T tile t = K[16t .. 16t+15] Q^T, lane (r, g) gets keys 16t + 4g + e
+  // ---- 1. scores: S^T tile t = K[16t .. 16t+15] Q^T on MFMA
   bf16x8_t qf[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
     qf[c] = as_bf16x8(*reinterpret_cast<const uint4*>(q + row * D + 32 * c + 8 * g));
 
-  float s[NT][4];
+  float s[NTH][4];
   float mx = -INFINITY, mn = INFINITY;  // lane-local, over existing keys
   int nlq = nl;
-  // Opaque copy: the existence masks stay local to this phase instead of being
-  // kept (4 NT scalar register pairs) for later tests of the same condition.
-  asm volatile("" : "+v"(nlq));
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
+  asm volatile("" : "+v"(nlq));  // existence masks stay local to this phase
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);  // [2 halves][CK][KS]
 #pragma unroll
-  for (int cb = 0; cb < kChunks; ++cb) {
-    if (cb * Gm::kChunk >= n) {  // chunk wholly past the last key (uniform)
+  for (int cc = 0; cc < NCH; ++cc) {
+    if (cc > 0) __syncthreads();
+    constexpr int kUnitsH = CK * D / 8;  // 16-byte units per half chunk
 #pragma unroll
-      for (int tt = 0; tt < Gm::kTiles; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[cb * Gm::kTiles + tt][e] = -INFINITY;
-      continue;
-    }
-    if (cb > 0) __syncthreads();
-    constexpr int kUnits = Gm::kChunk * D / 8;  // 16-byte units per chunk
-#pragma unroll
-    for (int u0 = 0; u0 < kUnits; u0 += kEncThreads) {
-      const int u = u0 + tid, rr = u / (D / 8), c8 = u % (D / 8);
-      const int src = min(cb * Gm::kChunk + rr, n - 1);
-      *reinterpret_cast<uint4*>(Ks + rr * Gm::kKStride + c8 * 8) =
-          *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(src) * D + c8 * 8);
+    for (int u0 = 0; u0 < 2 * kUnitsH; u0 += kEncThreads) {
+      const int u = u0 + tid;
+      if (2 * kUnitsH % kEncThreads == 0 || u < 2 * kUnitsH) {
+        const int hh = u / kUnitsH, rem = u % kUnitsH;
+        const int rr = rem / (D / 8), c8 = rem % (D / 8);
+        const int src = min(hh * H + cc * CK + rr, n - 1);
+        *reinterpret_cast<uint4*>(Ks + (hh * CK + rr) * KS + c8 * 8) =
+            *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(src) * D + c8 * 8);
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int tt = 0; tt < Gm::kTiles; ++tt) {
-      const int t = cb * Gm::kTiles + tt;
+    for (int tt = 0; tt < TPC; ++tt) {
+      const int t = cc * TPC + tt;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        const bf16x8_t a = as_bf16x8(
-            *reinterpret_cast<const uint4*>(Ks + (tt * 16 + r) * Gm::kKStride + 32 * c + 8 * g));
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
+            Ks + (kh * CK + tt * 16 + r) * KS + 32 * c + 8 * g));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], acc, 0, 0, 0);
       }
 #pragma unroll
@@ -192,18 +203,26 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
   }
-  __syncthreads();  // the K stage is reused as select scratch
 
-  // ---- 2. the certified cut, per row
-  WaveSel& ws = reinterpret_cast<WaveSel*>(smem)[wave];
+  // ---- 2. the certified cut, per row (both waves of a row group agree on it)
   mx = row_max(mx);
   mn = row_min(mn);
-
-  double* hrow = ws.hist + r * kHistStride;
+  if (g == 0) {
+    xg.f[kh][r][0] = mx;
+    xg.f[kh][r][1] = mn;
+  }
+  __syncthreads();  // the K stage is free: it becomes the select scratch
+  GroupSel& gs = reinterpret_cast<GroupSel*>(smem)[rg];
+  double* hrow = gs.hist + r * kHistStride;
+  mx = fmaxf(xg.f[0][r][0], xg.f[1][r][0]);
+  mn = fminf(xg.f[0][r][1], xg.f[1][r][1]);
+  if (kh == 0) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) hrow[16 * g + j] = 0.0;
-  wave_lds_sync();
-  // Level 0: the mass histogram over equal-width value bins on [mn, mx].
+    for (int j = 0; j < 16; ++j) hrow[16 * g + j] = 0.0;
+  }
+  __syncthreads();
+  // Level 0: the mass histogram over equal-width value bins on [mn, mx], and
+  // every weight kept, packed, for the output pass.
   const float vrng = mx - mn;
   float vinv = static_cast<float>(kEncBins) / vrng;
   vinv = (vrng > 0.0f && isfinite(vinv)) ? vinv : 0.0f;
@@ -211,15 +230,20 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // underflows below -104), so clamping there changes no weight; it maps the
   // -inf of absent keys to weight 0 without a branch.
   const float wfloor = mx - 200.0f;
+  // Packed weights are kept for the output pass when registers allow.
+  constexpr bool kKeepW = NTH <= 8;
+  uint32_t pw[kKeepW ? NTH : 1][4];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NTH; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float v = s[t][e];
-      atomicAdd(hrow + value_bin(v, mn, vinv), static_cast<double>(weight(fmaxf(v, wfloor), mx)));
+      const float w = weight(fmaxf(v, wfloor), mx);
+      atomicAdd(hrow + value_bin(v, mn, vinv), static_cast<double>(w));
+      if constexpr (kKeepW) pw[t][e] = pack_weight(w);
     }
-  wave_lds_sync();
-  // Z = the histogram's total, summed in one fixed order by all lanes of a row.
+  __syncthreads();
+  // Z = the histogram's total, summed in one fixed order by every lane of a row.
   double zp = 0.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) zp += hrow[16 * g + j];
@@ -232,35 +256,35 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   float ilo = mn, ihi = mx;  // closed score interval known to hold the cut key
   uint64_t cut = 0;
   double R = 0.0;
-  uint64_t* klist = ws.key + lane * kLaneCand;
-  float* wlist = ws.w + lane * kLaneCand;
+  uint64_t* klist = gs.key + (kh * kWave + lane) * kLaneSlots;
+  float* wlist = gs.w + (kh * kWave + lane) * kLaneCand;
 
   for (int level = 0; level < kMaxLevels; ++level) {
-    // Opaque to the optimiser: keeps per-key values derived from s (weights,
-    // encodings) from being hoisted out of the level loop into 4 NT extra
-    // registers each.
+    // Opaque to the optimiser: keeps per-key values derived from s from being
+    // hoisted out of the level loop.
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NTH; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(s[t][e]));
     const uint32_t ulo = ukey(ilo);
     float uinv = 0.0f;
     if (level > 0) {  // histogram of the interval over bins of the integer encoding
-      uinv = static_cast<float>(kEncBins) /
-             (static_cast<float>(ukey(ihi) - ulo) + 1.0f);
+      uinv = static_cast<float>(kEncBins) / (static_cast<float>(ukey(ihi) - ulo) + 1.0f);
+      if (kh == 0) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) hrow[16 * g + j] = 0.0;
-      wave_lds_sync();
+        for (int j = 0; j < 16; ++j) hrow[16 * g + j] = 0.0;
+      }
+      __syncthreads();
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NTH; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v = s[t][e];
           if (active && v >= ilo && v <= ihi)
             atomicAdd(hrow + ukey_bin(v, ulo, uinv), static_cast<double>(weight(v, mx)));
         }
+      __syncthreads();
     }
-    wave_lds_sync();
 
     // The bin holding the cut: the largest b whose mass below is <= thr.
     double hl[16], S = 0.0;
@@ -295,58 +319,88 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
 
-    // Candidates: the keys of that bin.
-    int kofs = 4 * g;
+    // Candidates: the keys of that bin.  Branch-free: every key is written,
+    // those outside the bin (and any past kLaneCand) into the lane's spare
+    // slot; entries hold (index, score bits).
+    int kofs = kbase + 4 * g;
     asm volatile("" : "+v"(kofs));  // recomputed per use, not held per key
     int cnt = 0;
     float cmn = INFINITY, cmx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NTH; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float v = s[t][e];
-        if (active && v >= ilo && v <= ihi &&
-            (level == 0 ? value_bin(v, mn, vinv) : ukey_bin(v, ulo, uinv)) == best) {
-          if (cnt < kLaneCand) klist[cnt] = key64(v, static_cast<uint32_t>(kofs + 16 * t + e));
-          ++cnt;
-          cmn = fminf(cmn, v);
-          cmx = fmaxf(cmx, v);
-        }
+        const bool in = active && v >= ilo && v <= ihi &&
+                        (level == 0 ? value_bin(v, mn, vinv) : ukey_bin(v, ulo, uinv)) == best;
+        klist[in ? min(cnt, kLaneCand) : kLaneCand] =
+            (static_cast<uint64_t>(kofs + 16 * t + e) << 32) | __float_as_uint(v);
+        cnt += in ? 1 : 0;
+        cmn = fminf(cmn, in ? v : INFINITY);
+        cmx = fmaxf(cmx, in ? v : -INFINITY);
       }
-    const int ctot = row_sum(cnt);
-    const int over = row_sum(cnt > kLaneCand ? 1 : 0);
-    cmn = row_min(cmn);
-    cmx = row_max(cmx);
+    xg.lcnt[kh][lane] = cnt;
+    {
+      const int c = row_sum(cnt);
+      const int o = row_sum(cnt > kLaneCand ? 1 : 0);
+      const float a = row_min(cmn), b = row_max(cmx);
+      if (g == 0) {
+        xg.i[kh][r][0] = c;
+        xg.i[kh][r][1] = o;
+        xg.f[kh][r][2] = a;
+        xg.f[kh][r][3] = b;
+      }
+    }
+    __syncthreads();
+    const int ctot = xg.i[0][r][0] + xg.i[1][r][0];
+    const int over = xg.i[0][r][1] + xg.i[1][r][1];
+    cmn = fminf(xg.f[0][r][2], xg.f[1][r][2]);
+    cmx = fmaxf(xg.f[0][r][3], xg.f[1][r][3]);
     const bool fin_list = active && over == 0 && ctot <= kFinishMax;
     const bool fin_eq = active && !fin_list && cmn == cmx;
 
     // Exact finish on <= 32 candidates: the cut is the largest candidate key
     // whose strictly smaller keys carry mass <= thr.
-    if (fin_list) {
-      for (int y = 0; y < cnt; ++y) wlist[y] = weight(key64_score(klist[y]), mx);
+    if (fin_list) {  // entries become (key64, weight)
+      for (int y = 0; y < cnt; ++y) {
+        const uint64_t en = klist[y];
+        const float v = __uint_as_float(static_cast<uint32_t>(en));
+        klist[y] = key64(v, static_cast<uint32_t>(en >> 32));
+        wlist[y] = weight(v, mx);
+      }
     }
     // Equal scores: the candidates differ only in index; rank by index.
-    uint32_t* bm = reinterpret_cast<uint32_t*>(ws.key + r * kLaneCand);  // 16 words per row
-    if (fin_eq) {
+    if (fin_eq && kh == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bm[4 * g + j] = 0u;
+      for (int j = 0; j < 4; ++j) xg.bm[r][4 * g + j] = 0u;
     }
-    wave_lds_sync();
+    __syncthreads();
     if (fin_list) {
-      int ng[4];
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) ng[gg] = __shfl(cnt, r + 16 * gg, kWave);
       uint64_t bk = 0;
       double bR = 0.0;
       for (int j = 0; j < cnt; ++j) {
         const uint64_t kj = klist[j];
         double ml = 0.0;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const uint64_t* ko = ws.key + (r + 16 * gg) * kLaneCand;
-          const float* wo = ws.w + (r + 16 * gg) * kLaneCand;
-          for (int y = 0; y < ng[gg]; ++y)
-            if (ko[y] < kj) ml += static_cast<double>(wo[y]);
+        for (int li = 0; li < 8; ++li) {  // the row's 8 lanes: 4 per wave
+          const int hh = li >> 2, gg = li & 3;
+          const int slot = hh * kWave + r + 16 * gg;
+          const uint64_t* ko = gs.key + slot * kLaneSlots;
+          const float* wo = gs.w + slot * kLaneCand;
+          const int ny = xg.lcnt[hh][r + 16 * gg];
+          for (int y = 0; y < ny; y += 4) {  // four entries' loads in flight
+            uint64_t k4[4];
+            float w4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int yy = min(y + u, ny - 1);
+              k4[u] = ko[yy];
+              w4[u] = wo[yy];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (y + u < ny && k4[u] < kj) ml += static_cast<double>(w4[u]);
+          }
         }
         const double Pm = bestP + ml;
         if (Pm <= thr && kj > bk) {
@@ -363,19 +417,28 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
           bR = oR;
         }
       }
-      cut = bk;
-      R = bR;
+      if (g == 0) {
+        xg.k[kh][r] = bk;
+        xg.d[kh][r] = bR;
+      }
     }
     if (fin_eq) {
+      int kb = kbase + 4 * g;
+      asm volatile("" : "+v"(kb));  // per-key bits are recomputed, not kept across levels
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NTH; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = 4 * g + 16 * t + e;
-          if (s[t][e] == cmn) atomicOr(bm + (key >> 5), 1u << (key & 31));
+          const int key = kb + 16 * t + e;
+          if (s[t][e] == cmn) atomicOr(&xg.bm[r][key >> 5], 1u << (key & 31));
         }
     }
-    wave_lds_sync();
+    __syncthreads();
+    if (fin_list) {
+      const uint64_t k0 = xg.k[0][r], k1 = xg.k[1][r];
+      cut = k1 > k0 ? k1 : k0;
+      R = k1 > k0 ? xg.d[1][r] : xg.d[0][r];
+    }
     if (fin_eq) {
       // The tail takes the tied candidates from the highest index down; j of
       // them fit under thr beside the mass below, so the cut is the one of
@@ -393,7 +456,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       if (g == 0) {
         int rem = j;
         for (int wd = 15; wd >= 0; --wd) {
-          uint32_t word = bm[wd];
+          uint32_t word = xg.bm[r][wd];
           const int c = __popc(word);
           if (rem < c) {
             for (int b = 0; b < 32; ++b) {
@@ -420,74 +483,79 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       ihi = cmx;
     }
     active = active && !fin_list && !fin_eq;
-    if (__ballot(active) == 0) break;
+    // block-uniform exit; also orders this level's reads before the next
+    // level's histogram reset
+    if (__syncthreads_or(active ? 1 : 0) == 0) break;
   }
   const bool failed = active;  // not reached: each level drops a candidate
 
-  // ---- 3. head-only output: out^T = V^T P^T over the head keys
-  __syncthreads();  // select scratch is reused as the V^T stage
+  // ---- 3. head-only output: out^T = V^T P^T over this wave's key half
+  __syncthreads();  // select scratch becomes the V^T stage
   const float cs = key64_score(cut);
-  const int cil = static_cast<int>(key64_index(cut)) - 4 * g;  // head iff s > cs or (s == cs and 16 t + e <= cil)
+  // head iff s > cs or (s == cs and 16 t + e <= cil)
+  const int cil = static_cast<int>(key64_index(cut)) - kbase - 4 * g;
   const uint32_t gbit = 1u << (4 * g);
   const int nw = (n + 31) >> 5;
   f32x4_t acc[D / 16];
 #pragma unroll
   for (int f = 0; f < D / 16; ++f) acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   int kc = 0;
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem);  // [2 halves][D][VS]
 #pragma unroll
-  for (int cb = 0; cb < kChunks; ++cb) {
-    if (cb * Gm::kChunk >= n) break;  // uniform
-    if (cb > 0) __syncthreads();
-    // Stage V rows [cb * kChunk, +kChunk) as V^T: two keys per 32-bit word.
+  for (int cc = 0; cc < NCH; ++cc) {
+    if (cc > 0) __syncthreads();
+    // Stage V rows of chunk cc of both halves as V^T: two keys per 32-bit word.
     constexpr int kOct = D / 8;
-    constexpr int kItems = (Gm::kChunk / 2) * kOct;
+    constexpr int kItemsH = (CK / 2) * kOct;
 #pragma unroll
-    for (int i0 = 0; i0 < kItems; i0 += kEncThreads) {
-      const int it = i0 + tid, fo = it % kOct, kp = it / kOct;
-      const int k0 = min(cb * Gm::kChunk + 2 * kp, n - 1);
-      const int k1 = min(cb * Gm::kChunk + 2 * kp + 1, n - 1);
-      const uint4 a = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(k0) * D + 8 * fo);
-      const uint4 b = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(k1) * D + 8 * fo);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-      uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + (8 * fo) * Gm::kVStride + 2 * kp);
+    for (int i0 = 0; i0 < 2 * kItemsH; i0 += kEncThreads) {
+      const int it = i0 + tid;
+      if (2 * kItemsH % kEncThreads == 0 || it < 2 * kItemsH) {
+        const int hh = it / kItemsH, rem = it % kItemsH;
+        const int fo = rem % kOct, kp = rem / kOct;
+        const int k0 = min(hh * H + cc * CK + 2 * kp, n - 1);
+        const int k1 = min(hh * H + cc * CK + 2 * kp + 1, n - 1);
+        const uint4 a = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(k0) * D + 8 * fo);
+        const uint4 b = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(k1) * D + 8 * fo);
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+        uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + (hh * D + 8 * fo) * VS + 2 * kp);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        dst[(2 * f) * (Gm::kVStride / 2)] = (av[f] & 0xFFFFu) | (bv[f] << 16);
-        dst[(2 * f + 1) * (Gm::kVStride / 2)] = (av[f] >> 16) | (bv[f] & 0xFFFF0000u);
+        for (int f = 0; f < 4; ++f) {
+          dst[(2 * f) * (VS / 2)] = (av[f] & 0xFFFFu) | (bv[f] << 16);
+          dst[(2 * f + 1) * (VS / 2)] = (av[f] >> 16) | (bv[f] & 0xFFFF0000u);
+        }
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int st = 0; st < Gm::kTiles / 2; ++st) {
-      const int t0 = cb * Gm::kTiles + 2 * st;
+    for (int st = 0; st < TPC / 2; ++st) {
+      const int t0 = cc * TPC + 2 * st;
       uint32_t ph[4], pl[4];
       uint32_t bits = 0;
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
-          uint32_t hp = 0, lp = 0;
+          uint32_t p2[2];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const float v = s[t0 + half][e + k];
             const bool head = v > cs || (v == cs && 16 * (t0 + half) + e + k <= cil);
-            const float w = head ? weight(v, mx) : 0.0f;
             kc += head ? 1 : 0;
             bits |= head ? (gbit << (16 * half + e + k)) : 0u;
-            const __bf16 wh = static_cast<__bf16>(w);
-            const __bf16 wl = static_cast<__bf16>(w - static_cast<float>(wh));
-            hp |= static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wh)) << (16 * k);
-            lp |= static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wl)) << (16 * k);
+            if constexpr (kKeepW)
+              p2[k] = head ? pw[t0 + half][e + k] : 0u;
+            else
+              p2[k] = head ? pack_weight(weight(v, mx)) : 0u;
           }
-          ph[2 * half + e / 2] = hp;
-          pl[2 * half + e / 2] = lp;
+          ph[2 * half + e / 2] = (p2[0] & 0xFFFFu) | (p2[1] << 16);
+          pl[2 * half + e / 2] = (p2[0] >> 16) | (p2[1] & 0xFFFF0000u);
         }
       const bf16x8_t bh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
       const bf16x8_t bl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
       for (int f = 0; f < D / 16; ++f) {
-        const uint16_t* vr = Vt + (16 * f + r) * Gm::kVStride + 32 * st + 4 * g;
+        const uint16_t* vr = Vt + (kh * D + 16 * f + r) * VS + 32 * st + 4 * g;
         const uint2 lo2 = *reinterpret_cast<const uint2*>(vr);
         const uint2 hi2 = *reinterpret_cast<const uint2*>(vr + 16);
         const bf16x8_t av = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
@@ -496,36 +564,47 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
       if (sel_mask) {
         bits = row_or(bits);
-        const int wd = cb * (Gm::kTiles / 2) + st;
+        const int wd = kbase / 32 + cc * (TPC / 2) + st;
         if (row_ok && g == 0 && wd < nw) sel_mask[row * nw + wd] = bits;
       }
     }
   }
   kc = row_sum(kc);
-  const double den = Z - R;  // head mass
-
-  if (!row_ok) return;
-  const float invd = static_cast<float>(1.0 / den);
+  if (g == 0) xg.i[kh][r][2] = kc;
+  // Add the two halves: the upper half's wave hands its sums over through LDS.
+  __syncthreads();
+  float* comb = reinterpret_cast<float*>(smem) + rg * 16 * D;  // [16 rows][D]
+  if (kh == 1) {
 #pragma unroll
-  for (int f = 0; f < D / 16; ++f) {
-    const float4 o = make_float4(acc[f][0] * invd, acc[f][1] * invd, acc[f][2] * invd,
-                                 acc[f][3] * invd);
-    *reinterpret_cast<float4*>(out + row * D + 16 * f + 4 * g) = o;
+    for (int f = 0; f < D / 16; ++f)
+      *reinterpret_cast<float4*>(comb + r * D + 16 * f + 4 * g) =
+          make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
   }
-  if (g == 0) {
-    k_eps[row] = failed ? -1 : kc;
-    tau[row] = R / Z;
-    if (lse) lse[row] = static_cast<double>(mx) + log(Z);
-  }
-  if (scores_out) {
-    float* srow = scores_out + row * n + 4 * g;
+  __syncthreads();
+  if (scores_out && row_ok) {
+    float* srow = scores_out + row * n + kbase + 4 * g;
     asm volatile("" : "+v"(nl));
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NTH; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (16 * t + e < nl) srow[16 * t + e] = s[t][e];
       }
+  }
+  if (kh == 1 || !row_ok) return;
+  const double den = Z - R;  // head mass
+  const float invd = static_cast<float>(1.0 / den);
+#pragma unroll
+  for (int f = 0; f < D / 16; ++f) {
+    const float4 o = *reinterpret_cast<const float4*>(comb + r * D + 16 * f + 4 * g);
+    *reinterpret_cast<float4*>(out + row * D + 16 * f + 4 * g) =
+        make_float4((acc[f][0] + o.x) * invd, (acc[f][1] + o.y) * invd, (acc[f][2] + o.z) * invd,
+                    (acc[f][3] + o.w) * invd);
+  }
+  if (g == 0) {
+    k_eps[row] = failed ? -1 : xg.i[0][r][2] + xg.i[1][r][2];
+    tau[row] = R / Z;
+    if (lse) lse[row] = static_cast<double>(mx) + log(Z);
   }
 }
 

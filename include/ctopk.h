@@ -165,8 +165,10 @@ CTOPK_API int ctopk_validate(const ctopk_args* a);
  * the kernel's own duration.  Kernels in launch order: decode path: score
  * scan, level-0 histogram, select, value stream, output combine (rows of at
  * most 32768 keys need no separate histogram kernel: its pair is then recorded
- * back to back on the stream and times ~0); logits path: select, value stream,
- * output combine; encoder-shaped path: its one fused kernel.  Kernels past count/2 pairs run without events; pairs left over are
+ * back to back on the stream and measures only the stream's own gap between
+ * the two records, not a kernel); logits path: select, value stream, output
+ * combine; encoder-shaped path: its one fused kernel.  Kernels past count/2
+ * pairs run without events; pairs left over are
  * dropped when the call returns.  count must be even and at most 16 (0
  * disarms); returns CTOPK_ERR_SHAPE otherwise, CTOPK_ERR_NULL for a NULL
  * array or handle.
