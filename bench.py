@@ -42,7 +42,12 @@ PEAK_HBM_GBPS = 8000.0
 # (only for rows longer than the select holds in registers; otherwise its
 # event pair is recorded back to back and reads ~0), select, value stream,
 # output combine.
-KERNELS = ("score_scan", "hist0", "resolve", "vsum", "finalize")
+# Kernel names per decode plan, in launch order (ctopk_plan).
+KERNELS_BY_PLAN = {
+    2: ("score_scan", "hist0", "resolve", "vsum", "finalize"),
+    3: ("score_scan", "hist0", "select_dense", "tail", "finalize"),
+}
+PLAN_NAMES = {1: "encoder", 2: "decode", 3: "decode_overlap"}
 # Rows of at most this many keys are resolved in registers, without the
 # separate level-0 histogram kernel (whose event pair then times no kernel).
 REGISTER_ROW_KEYS = 32768
@@ -304,6 +309,10 @@ def main():
     torch.cuda.synchronize()
     del src, dst
 
+    plan_args = ct.make_args(Q[0], Kd[0], Vd[0], args.eps, out=out, k_eps=k_eps, tau=tau)
+    plan = ct.ctopk_plan(plan_args)
+    KERNELS = KERNELS_BY_PLAN[plan]
+
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
     qp = [ctypes.c_void_p(t.data_ptr()) for t in Q]
@@ -399,6 +408,7 @@ def main():
         "bytes_per_step": {"K": k_bytes, "V_union": round(v_bytes)},
         "v_union_fraction": round(v_bytes / k_bytes, 4),
         "mean_k_eps": round(float(np.mean(kmean)), 1),
+        "plan": PLAN_NAMES.get(plan, plan),
         "kernel_us": kernel_us,
         "ms_per_step_with_kernel_events": None if ms_events is None else round(ms_events, 5),
         "encoder": encoder,

@@ -72,6 +72,7 @@ struct Layout {
   size_t rowsel = 0, blkstat = 0, part = 0, pmass = 0;
   size_t scores = 0, total = 0;
   int nblk = 0, nchunk = 0, hchunk = 0;
+  int dchunk = 0;  // dense-stream chunks of the overlapped decode path (0: not taken)
 };
 
 Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
@@ -79,13 +80,17 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   L.nblk = decode ? static_cast<int>(ctopk::ceil_div(n, ctopk::kScanTile)) : 0;
   L.nchunk = ctopk::vsum_nchunk(n, rows, n_v, v_dtype, dv);
   L.hchunk = (decode && n > ctopk::resolve_register_row()) ? ctopk::hist_nchunk(n, rows) : 0;
+  L.dchunk = decode ? ctopk::select_dense_nchunk(n, rows, n_v, v_dtype, dv) : 0;
+  // partial slots per row: head + tail per value-stream chunk, or dense +
+  // head per dense chunk
+  const size_t pslots = 2 * static_cast<size_t>(L.nchunk > L.dchunk ? L.nchunk : L.dchunk);
   size_t off = 0;
   L.rowsel = off;
   off += up(static_cast<size_t>(rows) * sizeof(ctopk::RowSel));
   L.blkstat = off;
   off += up(static_cast<size_t>(rows) * L.nblk * sizeof(float2));
   L.part = off;
-  off += up(static_cast<size_t>(rows) * L.nchunk * 2 * (dv + 1) * sizeof(float));  // head + tail
+  off += up(static_cast<size_t>(rows) * pslots * (dv + 1) * sizeof(float));
   L.pmass = off;
   off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(double));
   L.scores = off;
@@ -178,6 +183,17 @@ int validate_args(const ctopk_args* a) {
   return CTOPK_OK;
 }
 
+// The plan of a validated call (ctopk_plan_id).
+int plan_of(const ctopk_args* a) {
+  const bool certificate = a->out_err != nullptr || a->out_dense != nullptr;
+  if (certificate) return CTOPK_PLAN_DECODE;
+  if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads))
+    return CTOPK_PLAN_ENCODER;
+  if (ctopk::select_dense_nchunk(a->n, a->n_q_heads, a->n_kv_heads, a->dtype, a->d) > 0)
+    return CTOPK_PLAN_DECODE_OVERLAP;
+  return CTOPK_PLAN_DECODE;
+}
+
 int hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(CTOPK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -228,16 +244,22 @@ int ctopk_validate(const ctopk_args* a) {
   return rc;
 }
 
+int ctopk_plan(const ctopk_args* a) {
+  const int rc = validate_args(a);
+  if (rc != CTOPK_OK) return rc;
+  ok();
+  return plan_of(a);
+}
+
 int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   CallEvents events;  // consumes armed events even if validation fails
   int rc = validate_args(a);
   if (rc != CTOPK_OK) return rc;
   const float default_scale = static_cast<float>(1.0 / sqrt(static_cast<double>(a->d)));
+  const int plan = plan_of(a);
 
-  const bool certificate = a->out_err != nullptr || a->out_dense != nullptr;
-  if (!certificate &&
-      ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads)) {
+  if (plan == CTOPK_PLAN_ENCODER) {
     rc = hip_check(ctopk::launch_encoder(a->q, a->K, a->V, a->d, a->head_scale, default_scale,
                                          a->n, a->n_q_heads, a->n_kv_heads, a->eps, a->out,
                                          a->k_eps, a->tau, a->sel_mask, a->scores, a->lse, st),
@@ -272,6 +294,23 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
     if (rc != CTOPK_OK) return rc;
   } else {
     ctopk::skip_kernel_events(st);
+  }
+  if (plan == CTOPK_PLAN_DECODE_OVERLAP) {
+    // The select beside the dense value stream in one launch, then the tail
+    // pass and the combine.
+    float* dpart = part;
+    float* hpart = part + static_cast<size_t>(rows) * L.dchunk * (a->d + 1);
+    rc = hip_check(ctopk::launch_select_dense(scores, a->n, rows, blkstat, L.nblk, a->eps, rs,
+                                              a->k_eps, a->tau, a->lse, a->sel_mask,
+                                              a->n_kv_heads, a->V, a->dtype, a->d, dpart,
+                                              L.dchunk, st),
+                   "select launch");
+    if (rc != CTOPK_OK) return rc;
+    rc = hip_check(ctopk::launch_tail_fix(scores, a->n, rows, a->n_kv_heads, a->V, a->dtype,
+                                          a->d, rs, a->k_eps, dpart, hpart, L.dchunk, a->out, st),
+                   "tail pass launch");
+    if (rc != CTOPK_OK) return rc;
+    return ok();
   }
   rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, blkstat, L.nblk, pmass,
                                        L.hchunk, a->eps, rs, a->k_eps, a->tau, a->lse,

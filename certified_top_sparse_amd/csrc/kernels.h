@@ -21,6 +21,9 @@ constexpr int kScanTile = 64;
 constexpr int kVsumTile = 256;
 // Largest candidate set the resolve kernel keeps in LDS.
 constexpr int kCandCap = 8192;
+// Most keys per chunk of the tail pass of the overlapped decode plan (its key
+// list lives in LDS).
+constexpr int kFixKeys = 2048;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -86,7 +89,29 @@ hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const 
                        int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
                        float* dense, double* err, hipStream_t st);
 
-// Encoder-shaped path (all queries of a head, n <= 1024, bf16, MFMA QK^T).
+// Chunks per group for about `blocks` workgroups in total (whole tiles of
+// kVsumTile keys per chunk, never more chunks than tiles).
+int stream_nchunk(int64_t n, int groups, int blocks);
+
+// Decode rows the select holds in registers can run beside a dense value
+// stream: select_dense_nchunk gives that stream's chunks per group (0 when
+// the shape does not qualify: rows of 16K..32K keys, at least half of the
+// compute units left beside the rows' workgroups, and chunks of at most
+// kFixKeys keys).  launch_select_dense runs the select (as launch_resolve with
+// register rows) and writes the dense partials dpart [rows, nchunk, dv + 1]
+// (sum of w v and of w over every key of a chunk); launch_tail_fix turns them
+// into head partials in part (same layout) and runs the finalize (out).
+int select_dense_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv);
+hipError_t launch_select_dense(const float* scores, int64_t n, int rows, const float2* blkstat,
+                               int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                               double* lse, uint32_t* sel_mask, int n_v, const void* V,
+                               int v_dtype, int dv, float* dpart, int nchunk, hipStream_t st);
+hipError_t launch_tail_fix(const float* scores, int64_t n, int rows, int n_v, const void* V,
+                           int v_dtype, int dv, const RowSel* rs, const int32_t* k_eps,
+                           const float* dpart, float* part, int nchunk, float* out,
+                           hipStream_t st);
+
+// Encoder-shaped path (all queries of a head, n <= 512, bf16, MFMA QK^T).
 hipError_t launch_encoder(const void* q, const void* K, const void* V, int d,
                           const float* head_scale, float default_scale, int64_t n, int n_q,
                           int n_kv, double eps, float* out, int32_t* k_eps, double* tau,

@@ -29,6 +29,7 @@
 // Counts are exact integers, so k_eps is exact given the weights; masses are
 // fp64 sums of fp32 weights.  tau = R / Z uses the same weights as Z.
 #include "kernels.h"
+#include "vsum_body.h"
 
 namespace ctopk {
 namespace {
@@ -314,14 +315,14 @@ struct RowElems {
   }
 };
 
+// The select of one row by one workgroup of kResolveThreads threads.
 template <int PT>
-__global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
-    const float* __restrict__ scores, int64_t n, const float2* __restrict__ blkstat, int nblk,
-    const double* __restrict__ pmass, int npart, double eps, RowSel* __restrict__ rs,
-    int32_t* __restrict__ k_eps, double* __restrict__ tau, double* __restrict__ lse,
-    uint32_t* __restrict__ sel_mask, void* zero_base, size_t zero_bytes) {
-  __shared__ ResolveShared sh;
-  const int row = blockIdx.x;
+__device__ __forceinline__ void resolve_row(
+    ResolveShared& sh, int row, const float* __restrict__ scores, int64_t n,
+    const float2* __restrict__ blkstat, int nblk, const double* __restrict__ pmass, int npart,
+    double eps, RowSel* __restrict__ rs, int32_t* __restrict__ k_eps, double* __restrict__ tau,
+    double* __restrict__ lse, uint32_t* __restrict__ sel_mask, void* zero_base,
+    size_t zero_bytes) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -594,7 +595,119 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
   }
 }
 
+template <int PT>
+__global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
+    const float* __restrict__ scores, int64_t n, const float2* __restrict__ blkstat, int nblk,
+    const double* __restrict__ pmass, int npart, double eps, RowSel* __restrict__ rs,
+    int32_t* __restrict__ k_eps, double* __restrict__ tau, double* __restrict__ lse,
+    uint32_t* __restrict__ sel_mask, void* zero_base, size_t zero_bytes) {
+  __shared__ ResolveShared sh;
+  resolve_row<PT>(sh, static_cast<int>(blockIdx.x), scores, n, blkstat, nblk, pmass, npart, eps,
+                  rs, k_eps, tau, lse, sel_mask, zero_base, zero_bytes);
+}
+
+// The select of every row and, on the compute units it leaves idle, the
+// dense value stream: workgroups [0, rows) each select one row; the others
+// each sum w v over one chunk of keys for GB query heads of one V head, with
+// weights exp(s - m) from the row maximum alone (no cut needed).  One launch
+// places both, so they run side by side.
+template <typename T, int D, int GB>
+union SelectDenseSmem {
+  ResolveShared r;
+  StreamSmem<T, D, GB, kStreamDense, kResolveWaves> v;
+};
+
+template <typename T, int D, int GB>
+__global__ __launch_bounds__(kResolveThreads) void select_dense_kernel(
+    const float* __restrict__ scores, int64_t n, const float2* __restrict__ blkstat, int nblk,
+    double eps, RowSel* __restrict__ rs, int32_t* __restrict__ k_eps, double* __restrict__ tau,
+    double* __restrict__ lse, uint32_t* __restrict__ sel_mask, int rows, int G,
+    const T* __restrict__ V, float* __restrict__ dpart, int nchunk, int tpb, int nz) {
+  __shared__ SelectDenseSmem<T, D, GB> sm;
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < rows) {
+    resolve_row<kResolveRegRow / kResolveThreads>(sm.r, b, scores, n, blkstat, nblk, nullptr, 0,
+                                                  eps, rs, k_eps, tau, lse, sel_mask, nullptr, 0);
+    return;
+  }
+  const int db = b - rows;
+  const int grp = db / nchunk;
+  value_stream_block<T, D, GB, kStreamDense, kResolveWaves>(sm.v, scores, n, G, V, nullptr,
+                                                            blkstat, nblk, dpart, nchunk, tpb,
+                                                            db % nchunk, grp / nz, grp % nz);
+}
+
+template <typename T, int D, int GB>
+hipError_t select_dense_t(const float* scores, int64_t n, int rows, const float2* blkstat,
+                          int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                          double* lse, uint32_t* sel_mask, int n_v, const void* V, float* dpart,
+                          int nchunk, hipStream_t st) {
+  const int G = rows / n_v;
+  const int nz = static_cast<int>(ceil_div(G, GB));
+  const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
+  const unsigned grid = static_cast<unsigned>(rows + n_v * nz * nchunk);
+  return launch(select_dense_kernel<T, D, GB>, dim3(grid), dim3(kResolveThreads), 0, st, scores,
+                n, blkstat, nblk, eps, rs, k_eps, tau, lse, sel_mask, rows, G,
+                static_cast<const T*>(V), dpart, nchunk, tpb, nz);
+}
+
+template <typename T, int D>
+hipError_t select_dense_d(const float* scores, int64_t n, int rows, const float2* blkstat,
+                          int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                          double* lse, uint32_t* sel_mask, int n_v, const void* V, float* dpart,
+                          int nchunk, hipStream_t st) {
+  const int G = rows / n_v;
+#define CTOPK_SD(GB)                                                                            \
+  select_dense_t<T, D, GB>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse, sel_mask, \
+                           n_v, V, dpart, nchunk, st)
+  if (G == 1) return CTOPK_SD(1);
+  if (G == 2) return CTOPK_SD(2);
+  if constexpr (kGroupMax<T, D> == 4) {
+    return CTOPK_SD(4);
+  } else {
+    if (G <= 4) return CTOPK_SD(4);
+    return CTOPK_SD(8);
+  }
+#undef CTOPK_SD
+}
+
 }  // namespace
+
+int select_dense_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
+  // Rows held in registers by the widest register-row select, and at least
+  // half the compute units left beside the select's workgroups: the dense
+  // stream then takes at most about twice as long as a stream over the whole
+  // chip, which the select's own time covers.
+  if (n <= 16 * kResolveThreads || n > kResolveRegRow) return 0;
+  const int spare = kNumCUs - rows;
+  if (spare < kNumCUs / 2) return 0;
+  const int groups = vsum_groups(rows, n_v, v_dtype, dv);
+  const int64_t tiles = ceil_div(n, kVsumTile);
+  int64_t want = spare / groups;  // at most `spare` workgroups in total
+  if (want > tiles) want = tiles;
+  if (want < 1) return 0;
+  const int64_t tpb = ceil_div(tiles, want);
+  if (tpb * kVsumTile > kFixKeys) return 0;  // the tail pass lists a chunk in LDS
+  return static_cast<int>(ceil_div(tiles, tpb));
+}
+
+hipError_t launch_select_dense(const float* scores, int64_t n, int rows, const float2* blkstat,
+                               int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                               double* lse, uint32_t* sel_mask, int n_v, const void* V,
+                               int v_dtype, int dv, float* dpart, int nchunk, hipStream_t st) {
+  if (v_dtype == 1) {
+    if (dv == 128)
+      return select_dense_d<uint16_t, 128>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau,
+                                           lse, sel_mask, n_v, V, dpart, nchunk, st);
+    return select_dense_d<uint16_t, 64>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
+                                        sel_mask, n_v, V, dpart, nchunk, st);
+  }
+  if (dv == 128)
+    return select_dense_d<float, 128>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
+                                      sel_mask, n_v, V, dpart, nchunk, st);
+  return select_dense_d<float, 64>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
+                                   sel_mask, n_v, V, dpart, nchunk, st);
+}
 
 int resolve_register_row() { return kResolveRegRow; }
 

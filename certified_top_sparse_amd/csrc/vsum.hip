@@ -6,259 +6,233 @@
 //
 // where H_h = { i : key64(s_i, i) >= thr_h } comes from the select.
 //
-// Memory plan (HBM-bound).  A block of 8 waves owns up to 8 query heads of one
-// V head and `tpb` consecutive tiles of kVsumTile keys; each wave streams its
-// 32 keys of a tile on its own, with no block barrier inside the stream:
-//   * the V rows and the scores of a wave's keys are loaded together (each V
-//     row once, 16-byte loads by LPR consecutive lanes), so the stream never
-//     waits on a score read or on any other dependent load; keys outside a
-//     head's set get weight 0 (on these workloads the union of a group's head
-//     sets covers nearly every key, so loading every row costs little);
-//   * each (key, head) weight is computed once, by one lane, and staged in a
-//     wave-private LDS slot from which the LPR lanes of the row read all G
-//     weights;
-//   * w * v is accumulated for every head in registers.
-// Block sums go to per-(head, block) partials, and finalize_kernel adds them
-// in block order in fp64 and writes out, so results are bitwise reproducible.
-#include "kernels.h"
+// Two ways to the same sums (HBM-bound either way):
+//   * after the select: vsum_kernel streams V once with each key's head
+//     weights (the stream body is in vsum_body.h);
+//   * beside the select (select.hip): a dense stream (every key, weights from
+//     the row maximum alone) runs in the select's own launch on the compute
+//     units the select leaves idle; tail_fix_kernel then turns each chunk's
+//     dense sums into head sums (dense minus the tail, or the head directly,
+//     per head group) and the finalize below combines them.
+// Chunk sums go to per-(head, chunk) partials, and finalize_kernel adds them
+// in chunk order in fp64 and writes out, so results are bitwise reproducible.
+
+#include "vsum_body.h"
 
 namespace ctopk {
 namespace {
 
-template <typename T>
-struct VSlice;
-
-template <>
-struct VSlice<uint16_t> {  // bf16: 8 values per 16 bytes
-  static constexpr int kElems = 8;
-  __device__ static __forceinline__ void load(const uint4& u, float* v) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = __uint_as_float(w[e] << 16);
-      v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-    }
-  }
-};
-
-template <>
-struct VSlice<float> {  // fp32: 4 values per 16 bytes
-  static constexpr int kElems = 4;
-  __device__ static __forceinline__ void load(const uint4& u, float* v) {
-    v[0] = __uint_as_float(u.x);
-    v[1] = __uint_as_float(u.y);
-    v[2] = __uint_as_float(u.z);
-    v[3] = __uint_as_float(u.w);
-  }
-};
-
-// bf16 values accumulate in fp32 (tolerance is set by the bf16 inputs); fp32
-// values accumulate in fp64 so the fp32 output keeps ~1e-7 relative accuracy.
-template <typename T>
-struct AccOf {
-  using type = float;
-};
-template <>
-struct AccOf<float> {
-  using type = double;
-};
-
 constexpr int kVsumThreads = 512;
-
-
-// Heads per block: 8, except fp32 values at d = 128, whose fp64 block sums
-// would not fit LDS for 8 heads.
-template <typename T, int D>
-constexpr int kGroupMax = (sizeof(typename AccOf<T>::type) == 8 && D == 128) ? 4 : 8;
 constexpr int kVsumWaves = kVsumThreads / kWave;
 
 // With TAIL the kernel also accumulates the tail: w * v and w over the keys
 // outside the head, so the combine can form the untruncated output and the
 // truncation's output error; partials then hold [head num | head w | tail num
-// | tail w] per (row, block).
+// | tail w] per (row, chunk).
 template <typename T, int D, int GB, bool TAIL>
 __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
     const float* __restrict__ scores, int64_t n, int G, const T* __restrict__ V,
     const RowSel* __restrict__ rs, float* __restrict__ part, int nchunk, int tpb) {
+  constexpr int MODE = TAIL ? kStreamHeadTail : kStreamHead;
+  __shared__ StreamSmem<T, D, GB, MODE, kVsumWaves> sm;
+  value_stream_block<T, D, GB, MODE, kVsumWaves>(sm, scores, n, G, V, rs, nullptr, 0, part,
+                                                 nchunk, tpb, static_cast<int>(blockIdx.x),
+                                                 static_cast<int>(blockIdx.y),
+                                                 static_cast<int>(blockIdx.z));
+}
+
+// Turns one chunk's dense sums into head sums, for the head group's mode
+// (group_tail_mode): each thread classifies its keys of the chunk (at most
+// kFixKeys) against every head's cut; the keys the mode needs are listed in
+// LDS in key order (a deterministic compaction), their V rows gathered, and
+//   tail mode: part = dense - sum over tail keys of w v (and of w);
+//   head mode: part = sum over head keys of w v (the dense sums go unused).
+// Writes part [rows, nchunk, D + 1] in the layout finalize_kernel reads.
+constexpr int kFixThreads = 512;
+constexpr int kFixWaves = kFixThreads / kWave;
+
+template <typename T, int D, int GB>
+__global__ __launch_bounds__(kFixThreads) void tail_fix_kernel(
+    const float* __restrict__ scores, int64_t n, int G, const T* __restrict__ V,
+    const RowSel* __restrict__ rs, const int32_t* __restrict__ k_eps,
+    const float* __restrict__ dpart, float* __restrict__ part, int nchunk, int tpb) {
   using Acc = typename AccOf<T>::type;
   constexpr int EPL = VSlice<T>::kElems;
   constexpr int LPR = D / EPL;
   constexpr int RPW = kWave / LPR;
-  constexpr int PASS = kVsumTile / kVsumWaves;  // keys per wave per tile
-  constexpr int ITER = PASS / RPW;              // rows per lane per tile
-  constexpr int NPAIR = PASS * GB;              // (key, head) weights per wave per tile
-  constexpr int PPL = (NPAIR + kWave - 1) / kWave;  // weights per lane
-  static_assert(kVsumTile % (kVsumWaves * RPW) == 0, "whole rows per lane");
-  static_assert(GB <= LPR && kWave % GB == 0, "head groups tile the wave");
-  constexpr int NS = TAIL ? 2 : 1;  // head sums, and tail sums with TAIL
-  __shared__ Acc s_red[NS][kVsumWaves][GB * D];
-  __shared__ double s_wsum[NS][kVsumWaves][GB];
-  __shared__ float s_w[kVsumWaves][PASS][GB];  // wave-private weight staging
+  constexpr int KPT = kFixKeys / kFixThreads;  // keys per thread
+  constexpr int STEP = kFixWaves * RPW;        // rows per workgroup and slot
+  // V rows in flight per lane: as many as the accumulators leave registers for
+  constexpr int kAccRegs = GB * EPL * static_cast<int>(sizeof(Acc)) / 4;
+  constexpr int ITER = kAccRegs <= 16 ? 16 : (sizeof(Acc) == 4 ? 8 : 4);
+  constexpr int NDP = (GB * (D + 1) + kFixThreads - 1) / kFixThreads;  // partials per thread
+  static_assert(kFixKeys % kFixThreads == 0, "whole keys per thread");
+  __shared__ int s_idx[kFixKeys];
+  __shared__ float s_w[kFixKeys][GB];
+  __shared__ uint32_t s_cnt[KPT][kFixWaves];
+  __shared__ Acc s_red[kFixWaves][GB * D];
+  __shared__ double s_ws[kFixWaves][GB];
 
   const int chunk = blockIdx.x;
   const int vh = blockIdx.y;
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t / kWave;
-  const int h0 = vh * G + blockIdx.z * GB;
+  const int h0 = vh * G + static_cast<int>(blockIdx.z) * GB;
   const int nh = min(GB, G - static_cast<int>(blockIdx.z) * GB);
-  const int seg = lane % LPR;
-  const int rg = lane / LPR;
-  const T* Vb = V + static_cast<size_t>(vh) * static_cast<size_t>(n) * D;
+  const uint32_t vmask = (1u << nh) - 1u;
+  const int64_t c0 = static_cast<int64_t>(chunk) * tpb * kVsumTile;
+  // keys of this chunk (the host keeps tpb * kVsumTile <= kFixKeys and c0 < n)
+  const int len = static_cast<int>(min(n - c0, static_cast<int64_t>(tpb) * kVsumTile));
 
-  // Weights are computed once per (key, head): pair p = lane + 64 * u covers
-  // key p / GB and head p % GB, so each lane always works for head lane % GB.
-  // That head's selection parameters are read with block-uniform addresses.
-  const int hw = lane % GB;
-  uint64_t thr = ~0ull;
-  float m = 0.0f;
+  // Every load that does not depend on another is issued first: the chunk's
+  // dense partials (needed last), the heads' cuts and the keys' scores.
+  float dp[NDP];
+#pragma unroll
+  for (int k = 0; k < NDP; ++k) {
+    const int idx = min(t + k * kFixThreads, GB * (D + 1) - 1);
+    const int j = min(idx / (D + 1), nh - 1);
+    dp[k] = dpart[(static_cast<size_t>(h0 + j) * nchunk + chunk) * (D + 1) + idx % (D + 1)];
+  }
+  float sv[KPT][GB];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int64_t key = c0 + min(t + u * kFixThreads, len - 1);
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+      sv[u][j] = scores[static_cast<size_t>(h0 + min(j, nh - 1)) * static_cast<size_t>(n) + key];
+  }
+  uint64_t thr[GB];
+  float m[GB];
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
     const RowSel r = rs[h0 + min(j, nh - 1)];
-    if (hw == j) {
-      thr = j < nh ? r.thr : ~0ull;
-      m = r.m;
-    }
+    thr[j] = r.thr;
+    m[j] = r.m;
   }
-  const float* srow = scores + static_cast<size_t>(h0 + min(hw, nh - 1)) * static_cast<size_t>(n);
+  const bool tail_mode = group_tail_mode(k_eps, h0, nh, n);  // workgroup-uniform
 
+  // Classify (bit j of hb: the key is in head j's head set) and list the
+  // keys the mode needs: local key i = u * 512 + 64 w + lane goes after every
+  // key of smaller (u, w) and the lower lanes of its wave.
+  uint32_t hb[KPT];
+  bool sel[KPT];
+  uint64_t bal[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int i = t + u * kFixThreads;
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+      if (key64(sv[u][j], static_cast<uint32_t>(c0 + i)) >= thr[j]) bits |= 1u << j;
+    hb[u] = bits & vmask;
+    sel[u] = i < len && (tail_mode ? hb[u] != vmask : hb[u] != 0u);
+    bal[u] = __ballot(sel[u]);
+    if (lane == 0) s_cnt[u][wave] = static_cast<uint32_t>(__popcll(bal[u]));
+  }
+  __syncthreads();
+  double ws[GB];
+#pragma unroll
+  for (int j = 0; j < GB; ++j) ws[j] = 0.0;
+  uint32_t base = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < kFixWaves; ++w) {
+      const uint32_t c = s_cnt[u][w];
+      before += w < wave ? c : 0u;
+      all += c;
+    }
+    if (sel[u]) {
+      const uint32_t slot =
+          base + before +
+          __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal[u] >> 32),
+                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[u]), 0u));
+      s_idx[slot] = t + u * kFixThreads;
+#pragma unroll
+      for (int j = 0; j < GB; ++j) {
+        const bool in_head = ((hb[u] >> j) & 1u) != 0u;
+        const bool take = j < nh && (tail_mode ? !in_head : in_head);
+        const float w = take ? weight(sv[u][j], m[j]) : 0.0f;
+        s_w[slot][j] = w;
+        ws[j] += static_cast<double>(w);
+      }
+    }
+    base += all;
+  }
+  const int L = static_cast<int>(base);
+  __syncthreads();
+
+  // Gather the listed V rows: entry e = k * STEP + RPW * wave + rg.
+  const int seg = lane % LPR;
+  const int rg = lane / LPR;
+  const T* Vb = V + static_cast<size_t>(vh) * static_cast<size_t>(n) * D;
   Acc acc[GB][EPL];
-  Acc acct[TAIL ? GB : 1][EPL];
 #pragma unroll
   for (int j = 0; j < GB; ++j)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = Acc(0);
-#pragma unroll
-  for (int j = 0; j < (TAIL ? GB : 1); ++j)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acct[j][e] = Acc(0);
-  double wsum = 0.0;   // weight of head hw over this lane's pairs
-  double wsumt = 0.0;  // and of its tail (TAIL)
-
-  for (int tb = 0; tb < tpb; ++tb) {
-    const int64_t p0 = (static_cast<int64_t>(chunk) * tpb + tb) * kVsumTile + wave * PASS;
-    if (p0 >= n) break;  // uniform per wave; waves do not synchronise in this loop
-    // Value rows and the pass's scores, issued together (rows past n re-read
-    // row n-1 and get weight 0).
+  for (int k0 = 0; k0 * STEP < L; k0 += ITER) {
     uint4 u[ITER];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-      const int64_t r = min(p0 + it * RPW + rg, n - 1);
-      u[it] = load_stream16(Vb + r * D + seg * EPL);
+      const int e = min((k0 + it) * STEP + RPW * wave + rg, L - 1);
+      const int64_t r = c0 + s_idx[e];
+      u[it] = *reinterpret_cast<const uint4*>(Vb + r * D + seg * EPL);
     }
-    float s[PPL];
-#pragma unroll
-    for (int q = 0; q < PPL; ++q) {
-      const int key = (lane + kWave * q) / GB;
-      s[q] = srow[min(p0 + min(key, PASS - 1), n - 1)];
-    }
-#pragma unroll
-    for (int q = 0; q < PPL; ++q) {
-      const int pair = lane + kWave * q;
-      if (pair < NPAIR) {
-        const int key = pair / GB;
-        const int64_t r = p0 + key;
-        const bool kept = r < n && key64(s[q], static_cast<uint32_t>(r)) >= thr;
-        if constexpr (TAIL) {
-          // staged as +w for head keys and -w for tail keys
-          const float w = r < n ? weight(s[q], m) : 0.0f;
-          wsum += kept ? static_cast<double>(w) : 0.0;
-          wsumt += kept ? 0.0 : static_cast<double>(w);
-          s_w[wave][key][hw] = kept ? w : -w;
-        } else {
-          const float w = kept ? weight(s[q], m) : 0.0f;
-          wsum += static_cast<double>(w);
-          s_w[wave][key][hw] = w;
-        }
-      }
-    }
-    // s_w is private to this wave, and one wave's LDS operations complete in
-    // order, so a wavefront-scope fence (which only stops the compiler from
-    // moving the reads above the writes) is all the ordering needed.
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-      const int key = it * RPW + rg;
-      float wj[GB];
-#pragma unroll
-      for (int j = 0; j < GB; ++j) wj[j] = s_w[wave][key][j];
+      const int e = (k0 + it) * STEP + RPW * wave + rg;
+      const int ec = min(e, L - 1);
       float v[EPL];
       VSlice<T>::load(u[it], v);
-      if constexpr (TAIL) {
 #pragma unroll
-        for (int j = 0; j < GB; ++j) {
-          const Acc wh = static_cast<Acc>(fmaxf(wj[j], 0.0f));
-          const Acc wt = static_cast<Acc>(fmaxf(-wj[j], 0.0f));
+      for (int j = 0; j < GB; ++j) {
+        const Acc w = e < L ? static_cast<Acc>(s_w[ec][j]) : Acc(0);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            acc[j][e] += wh * static_cast<Acc>(v[e]);
-            acct[j][e] += wt * static_cast<Acc>(v[e]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < GB; ++j)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[j][e] += static_cast<Acc>(wj[j]) * static_cast<Acc>(v[e]);
+        for (int e2 = 0; e2 < EPL; ++e2) acc[j][e2] += w * static_cast<Acc>(v[e2]);
       }
     }
   }
 
-  // Block sums: row groups of a wave (xor butterfly over lane / LPR), then the
-  // waves in order through LDS.
+  // Workgroup sums in a fixed order, then the chunk's head partial.
 #pragma unroll
-  for (int o = LPR; o < kWave; o <<= 1) {
+  for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll
     for (int j = 0; j < GB; ++j)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], o, kWave);
-    if constexpr (TAIL) {
-#pragma unroll
-      for (int j = 0; j < GB; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acct[j][e] += __shfl_xor(acct[j][e], o, kWave);
-    }
-  }
-#pragma unroll
-  for (int o = GB; o < kWave; o <<= 1) {
-    wsum += __shfl_xor(wsum, o, kWave);
-    if constexpr (TAIL) wsumt += __shfl_xor(wsumt, o, kWave);
-  }
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < GB; ++j)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        s_red[0][wave][j * D + seg * EPL + e] = acc[j][e];
-        if constexpr (TAIL) s_red[NS - 1][wave][j * D + seg * EPL + e] = acct[j][e];
-      }
+      for (int e = 0; e < EPL; ++e) s_red[wave][j * D + seg * EPL + e] = acc[j][e];
   }
-  if (lane < GB) {
-    s_wsum[0][wave][lane] = wsum;
-    if constexpr (TAIL) s_wsum[NS - 1][wave][lane] = wsumt;
+#pragma unroll
+  for (int j = 0; j < GB; ++j) {
+    const double s = wave_sum(ws[j]);
+    if (lane == 0) s_ws[wave][j] = s;
   }
   __syncthreads();
-  const size_t pstride = static_cast<size_t>(NS * (D + 1));
-  for (int idx = t; idx < NS * GB * (D + 1); idx += kVsumThreads) {
-    const int part_k = idx / (GB * (D + 1));  // 0 head, 1 tail
-    const int rem = idx - part_k * GB * (D + 1);
-    const int j = rem / (D + 1);
-    const int e = rem - j * (D + 1);
-    if (j < nh) {
+#pragma unroll
+  for (int k = 0; k < NDP; ++k) {
+    const int idx = t + k * kFixThreads;
+    const int j = idx / (D + 1);
+    const int e = idx - j * (D + 1);
+    if (idx < GB * (D + 1) && j < nh) {
       double sum = 0.0;
       if (e < D) {
 #pragma unroll
-        for (int g = 0; g < kVsumWaves; ++g) sum += static_cast<double>(s_red[part_k][g][j * D + e]);
+        for (int w = 0; w < kFixWaves; ++w) sum += static_cast<double>(s_red[w][j * D + e]);
       } else {
 #pragma unroll
-        for (int g = 0; g < kVsumWaves; ++g) sum += s_wsum[part_k][g][j];
+        for (int w = 0; w < kFixWaves; ++w) sum += s_ws[w][j];
       }
-      part[(static_cast<size_t>(h0 + j) * nchunk + chunk) * pstride + part_k * (D + 1) + e] =
-          static_cast<float>(sum);
+      const size_t off = (static_cast<size_t>(h0 + j) * nchunk + chunk) * (D + 1) + e;
+      part[off] = static_cast<float>(tail_mode ? static_cast<double>(dp[k]) - sum : sum);
     }
   }
-
 }
 
 // out[h, e] = sum_c part[h, c, e] / sum_c part[h, c, dv], fp64 sums in a fixed
@@ -372,7 +346,54 @@ hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const voi
   }
 }
 
+template <typename T, int D, int GB>
+hipError_t fix_t(const float* scores, int64_t n, int rows, int n_v, const void* V,
+                 const RowSel* rs, const int32_t* k_eps, const float* dpart, float* part,
+                 int nchunk, float* out, hipStream_t st) {
+  const int G = rows / n_v;
+  const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
+  dim3 grid(nchunk, n_v, static_cast<unsigned>(ceil_div(G, GB)));
+  const hipError_t e = launch(tail_fix_kernel<T, D, GB>, grid, dim3(kFixThreads), 0, st, scores,
+                              n, G, static_cast<const T*>(V), rs, k_eps, dpart, part, nchunk, tpb);
+  if (e != hipSuccess) return e;
+  return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, static_cast<const float*>(part),
+                nchunk, D, 1, out, static_cast<float*>(nullptr), static_cast<double*>(nullptr));
+}
+
+template <typename T, int D>
+hipError_t fix_d(const float* scores, int64_t n, int rows, int n_v, const void* V,
+                 const RowSel* rs, const int32_t* k_eps, const float* dpart, float* part,
+                 int nchunk, float* out, hipStream_t st) {
+  const int G = rows / n_v;
+#define CTOPK_FIX(GB) \
+  fix_t<T, D, GB>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st)
+  if (G == 1) return CTOPK_FIX(1);
+  if (G == 2) return CTOPK_FIX(2);
+  if constexpr (kGroupMax<T, D> == 4) {
+    return CTOPK_FIX(4);
+  } else {
+    if (G <= 4) return CTOPK_FIX(4);
+    return CTOPK_FIX(8);
+  }
+#undef CTOPK_FIX
+}
+
 }  // namespace
+
+hipError_t launch_tail_fix(const float* scores, int64_t n, int rows, int n_v, const void* V,
+                           int v_dtype, int dv, const RowSel* rs, const int32_t* k_eps,
+                           const float* dpart, float* part, int nchunk, float* out,
+                           hipStream_t st) {
+  if (v_dtype == 1) {
+    if (dv == 128)
+      return fix_d<uint16_t, 128>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out,
+                                  st);
+    return fix_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st);
+  }
+  if (dv == 128)
+    return fix_d<float, 128>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st);
+  return fix_d<float, 64>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st);
+}
 
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
                        int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
@@ -395,17 +416,20 @@ int vsum_groups(int rows, int n_v, int v_dtype, int dv) {
   return n_v * static_cast<int>(ceil_div(G, gb));
 }
 
-int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
-  // Blocks per group: about one block per compute unit in total (measured
-  // fastest on MI355X: each block streams several tiles and amortises its
-  // reduction epilogue), and never more blocks than tiles.
+int stream_nchunk(int64_t n, int groups, int blocks) {
   const int64_t tiles = ceil_div(n, kVsumTile);
-  const int64_t groups = vsum_groups(rows, n_v, v_dtype, dv);
-  int64_t want = ceil_div(kNumCUs, groups);
+  int64_t want = ceil_div(blocks, groups);
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   const int64_t tpb = ceil_div(tiles, want);
   return static_cast<int>(ceil_div(tiles, tpb));
+}
+
+int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
+  // Blocks per group: about one block per compute unit in total (measured
+  // fastest on MI355X: each block streams several tiles and amortises its
+  // reduction epilogue), and never more blocks than tiles.
+  return stream_nchunk(n, vsum_groups(rows, n_v, v_dtype, dv), kNumCUs);
 }
 
 }  // namespace ctopk

@@ -26,6 +26,9 @@ CTOPK_ERR_WORKSPACE = -6
 CTOPK_ERR_HIP = -7
 CTOPK_F32 = 0
 CTOPK_BF16 = 1
+CTOPK_PLAN_ENCODER = 1
+CTOPK_PLAN_DECODE = 2
+CTOPK_PLAN_DECODE_OVERLAP = 3
 
 STATUS_NAMES = {
     0: "CTOPK_OK", -1: "CTOPK_ERR_NULL", -2: "CTOPK_ERR_SHAPE", -3: "CTOPK_ERR_EPS",
@@ -37,7 +40,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "ctopk_certify", "ctopk_certify_ex", "ctopk_workspace_bytes", "ctopk_certify_logits",
     "ctopk_logits_workspace_bytes", "ctopk_validate", "ctopk_last_error_string",
-    "ctopk_version", "ctopk_record_kernel_events",
+    "ctopk_version", "ctopk_record_kernel_events", "ctopk_plan",
 )
 
 
@@ -104,6 +107,8 @@ def load(path: str = LIB_PATH):
     lib.ctopk_logits_workspace_bytes.restype = sz
     lib.ctopk_validate.argtypes = [ctypes.POINTER(CtopkArgs)]
     lib.ctopk_validate.restype = ctypes.c_int
+    lib.ctopk_plan.argtypes = [ctypes.POINTER(CtopkArgs)]
+    lib.ctopk_plan.restype = ctypes.c_int
     lib.ctopk_last_error_string.argtypes = []
     lib.ctopk_last_error_string.restype = ctypes.c_char_p
     lib.ctopk_version.argtypes = []
@@ -175,6 +180,12 @@ def ctopk_record_kernel_events(events) -> None:
 def ctopk_validate(args: CtopkArgs) -> int:
     """Host-only argument check; returns the status code (no exception)."""
     return int(load().ctopk_validate(ctypes.byref(args)))
+
+
+def ctopk_plan(args: CtopkArgs) -> int:
+    """Host-only: the plan (CTOPK_PLAN_*) ctopk_certify_ex takes for these
+    arguments, or the negative status of their validation."""
+    return int(load().ctopk_plan(ctypes.byref(args)))
 
 
 def ctopk_certify(q, K, V, eps, out=None, k_eps=None, tau=None, stream=None):

@@ -122,6 +122,35 @@ typedef struct ctopk_args {
  */
 CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
 
+/*
+ * Execution plans of ctopk_certify_ex, named by the kernels each launches (in
+ * launch order):
+ *   CTOPK_PLAN_ENCODER: one fused kernel (MFMA scores, select, MFMA head-only
+ *     output);
+ *   CTOPK_PLAN_DECODE: score scan; level-0 histogram (only for rows of more
+ *     than 32768 keys); select; value stream over the head; combine;
+ *   CTOPK_PLAN_DECODE_OVERLAP: score scan; one launch in which the select runs
+ *     beside a dense value stream (sum of w v over every key, which needs only
+ *     the row maximum); tail pass (per chunk of keys: the dense sums minus the
+ *     tail keys' w v or, for head groups whose heads are short, the head keys'
+ *     w v directly); combine.  Taken for decode rows of 16385..32768 keys when
+ *     at least half of the compute units (128) remain beside one workgroup per
+ *     query row and the dense stream's chunks hold at most 2048 keys, and
+ *     never for calls that ask for out_err or out_dense.
+ */
+typedef enum {
+  CTOPK_PLAN_ENCODER = 1,
+  CTOPK_PLAN_DECODE = 2,
+  CTOPK_PLAN_DECODE_OVERLAP = 3
+} ctopk_plan_id;
+
+/*
+ * ctopk_plan -- the plan ctopk_certify_ex takes for these arguments: a
+ * ctopk_plan_id, or (negative) the status ctopk_validate returns for them.
+ * Host only, like ctopk_validate: no HIP call, no device memory touched.
+ */
+CTOPK_API int ctopk_plan(const ctopk_args* a);
+
 /* Device scratch bytes ctopk_certify_ex needs for these sizes (0 on bad sizes);
  * enough for every call with these sizes, whichever path it takes. */
 CTOPK_API size_t ctopk_workspace_bytes(int64_t n, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
@@ -162,13 +191,14 @@ CTOPK_API int ctopk_validate(const ctopk_args* a);
  * events[2i+1]) -- hipEvent_t handles created by the caller -- to the i-th
  * kernel it launches: the events take that kernel's start and end times on
  * the call's stream (hipExtLaunchKernel), so hipEventElapsedTime on a pair is
- * the kernel's own duration.  Kernels in launch order: decode path: score
- * scan, level-0 histogram, select, value stream, output combine (rows of at
- * most 32768 keys need no separate histogram kernel: its pair is then recorded
- * back to back on the stream and measures only the stream's own gap between
- * the two records, not a kernel); logits path: select, value stream, output
- * combine; encoder-shaped path: its one fused kernel.  Kernels past count/2
- * pairs run without events; pairs left over are
+ * the kernel's own duration.  Kernels in launch order are those of the call's
+ * plan (ctopk_plan); the decode plans take the score scan's pair, then the
+ * level-0 histogram's (when the plan launches none, its pair is recorded back
+ * to back on the stream and measures only the stream's own gap between the
+ * two records, not a kernel), then one pair per remaining kernel (three in
+ * either decode plan).  Logits
+ * path: select, value stream, output combine.  Kernels past count/2 pairs run
+ * without events; pairs left over are
  * dropped when the call returns.  count must be even and at most 16 (0
  * disarms); returns CTOPK_ERR_SHAPE otherwise, CTOPK_ERR_NULL for a NULL
  * array or handle.

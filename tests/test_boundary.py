@@ -188,3 +188,32 @@ def test_missing_library_fails_loudly(tmp_path):
             cb.load(str(tmp_path / "nope.so"))
     finally:
         cb._lib = saved
+
+
+@pytest.mark.parametrize("kw,plan", [
+    ({}, cb.CTOPK_PLAN_DECODE_OVERLAP),                           # n = 32768, 32 query rows
+    ({"n": 16385}, cb.CTOPK_PLAN_DECODE_OVERLAP),                 # smallest overlapped row
+    ({"n": 16384}, cb.CTOPK_PLAN_DECODE),                         # below the register-row band
+    ({"n": 32769}, cb.CTOPK_PLAN_DECODE),                         # above it
+    ({"dtype": cb.CTOPK_F32}, cb.CTOPK_PLAN_DECODE_OVERLAP),
+    ({"d": 64, "n_q_heads": 8, "n_kv_heads": 8}, cb.CTOPK_PLAN_DECODE_OVERLAP),
+    ({"n_q_heads": 64, "n_kv_heads": 8}, cb.CTOPK_PLAN_DECODE_OVERLAP),
+    # 128 CUs left, but 16 head groups share them: chunks of 4096 keys, more
+    # than the tail pass lists
+    ({"n_q_heads": 128, "n_kv_heads": 16}, cb.CTOPK_PLAN_DECODE),
+    ({"n_q_heads": 136, "n_kv_heads": 136}, cb.CTOPK_PLAN_DECODE),  # fewer than half left
+    ({"n_q_heads": 192, "n_kv_heads": 24}, cb.CTOPK_PLAN_DECODE),
+    ({"out_err": A16 * 7}, cb.CTOPK_PLAN_DECODE),                 # certificate: serial stream
+    ({"out_dense": A16 * 7}, cb.CTOPK_PLAN_DECODE),
+    ({"n": 512, "d": 64, "n_q_heads": 512, "n_kv_heads": 8}, cb.CTOPK_PLAN_ENCODER),
+    ({"n": 512, "d": 64, "n_q_heads": 512, "n_kv_heads": 8, "out_err": A16 * 7},
+     cb.CTOPK_PLAN_DECODE),
+])
+def test_plan_choice(lib, kw, plan):
+    assert ct.ctopk_plan(good_args(**kw)) == plan
+
+
+def test_plan_reports_validation_status(lib):
+    assert ct.ctopk_plan(good_args(eps=1.5)) == cb.CTOPK_ERR_EPS
+    assert ct.ctopk_plan(good_args(q=None)) == cb.CTOPK_ERR_NULL
+    assert ct.ctopk_plan(good_args(n_kv_heads=5)) == cb.CTOPK_ERR_SHAPE

@@ -190,9 +190,57 @@ def test_determinism(ct):
 
 
 # ---------------------------------------------------------------------------
+# overlapped plan: the select beside a dense value stream, then the tail
+# correction (dense minus tail, or the head directly, per chunk)
+# ---------------------------------------------------------------------------
+def plan_of(ct, wl):
+    q, K, V = dev(wl["q"][:1]), dev(wl["K"][:1, :1]), dev(wl["V"][:1, :1])
+    a = ct.make_args(q, K, V, 0.01, out=q, k_eps=q, tau=q)
+    a.n, a.n_q_heads, a.n_kv_heads = wl["n"], wl["n_q_heads"], wl["n_kv_heads"]
+    a.d = wl["d"]
+    return ct.ctopk_plan(a)
+
+
+def as_f32(wl):
+    return dict(wl, q=workloads.bf16_to_f32(wl["q"]), K=workloads.bf16_to_f32(wl["K"]),
+                V=workloads.bf16_to_f32(wl["V"]), dtype="f32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_overlap_shapes(ct, d, dtype, G):
+    # every head-group width (1, 2, 4, 8, and 16 as two groups of 8); n is not
+    # a multiple of the 256-key tile
+    wl = workloads.gqa_decode(n=20000, n_q=2 * G, n_kv=2, d=d, planted=5, temp_range=(0.5, 2.0))
+    if dtype == "f32":
+        wl = as_f32(wl)
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_OVERLAP
+    check_decode(ct, wl, 0.05, f"overlap d={d} {dtype} G={G}")
+
+
+@pytest.mark.parametrize("eps", [0.001, 0.3, 0.9])
+def test_overlap_eps(ct, eps):
+    # small eps: short tails (chunks subtract the tail from the dense sums);
+    # large eps: small heads (chunks sum the head directly)
+    wl = workloads.gqa_decode(n=24577, temp_range=(0.5, 4.0))
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_OVERLAP
+    check_decode(ct, wl, eps, "overlap gqa_decode n=24577")
+
+
+def test_overlap_smallest_row(ct):
+    wl = workloads.gqa_decode(n=16385, n_q=64, n_kv=8, d=64)
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_OVERLAP
+    check_decode(ct, wl, 0.01, "overlap gqa_decode n=16385 Hq=64")
+    wl = workloads.gqa_decode(n=16384, n_q=64, n_kv=8, d=64)
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE
+    check_decode(ct, wl, 0.01, "serial gqa_decode n=16384 Hq=64")
+
+
+# ---------------------------------------------------------------------------
 # output-level certificate: ||Attn - Attn_k||_2 and the untruncated output
 # ---------------------------------------------------------------------------
-def _certificate_case(ct, wl, eps, label, rtol, same_path=True):
+def _certificate_case(ct, wl, eps, label, rtol, same_path=True, same_select=True):
     _say(f"certificate {label} eps={eps} n={wl['n']} Hq={wl['n_q_heads']} d={wl['d']}")
     q, K, V = dev(wl["q"]), dev(wl["K"]), dev(wl["V"])
     hs = dev(wl["head_scale"])
@@ -201,9 +249,13 @@ def _certificate_case(ct, wl, eps, label, rtol, same_path=True):
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy() for k, v in res.items()}
     p = {k: v.cpu().numpy() for k, v in plain.items()}
-    if same_path:  # asking for the certificate leaves the certified result unchanged
+    if same_select:  # the certificate does not change the select
         assert np.array_equal(g["k_eps"], p["k_eps"])
+        assert np.array_equal(g["tau"], p["tau"])
+    if same_path:  # nor, on one plan, the output
         assert np.array_equal(g["out"], p["out"])
+    else:  # the plain call's plan may sum the head in another order
+        assert rel_l2(p["out"], g["out"]).max() <= rtol
     n_q, n_kv = wl["n_q_heads"], wl["n_kv_heads"]
     G = n_q // n_kv
     q64, K64, V64 = oracle.as_f64(wl["q"]), oracle.as_f64(wl["K"]), oracle.as_f64(wl["V"])
@@ -228,7 +280,9 @@ def test_certificate_gqa_decode(ct, eps):
 
 
 def test_certificate_gqa_decode_full(ct):
-    _certificate_case(ct, workloads.gqa_decode(), 0.01, "gqa_decode n=32768 (full)", 1e-3)
+    # the plain call runs the overlapped plan, the certificate the serial one
+    _certificate_case(ct, workloads.gqa_decode(), 0.01, "gqa_decode n=32768 (full)", 1e-3,
+                      same_path=False)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -243,7 +297,8 @@ def test_certificate_fp32(ct, d, G):
 def test_certificate_on_encoder_shape(ct):
     # all-queries shapes take the general path when the certificate is asked for
     wl = workloads.encoder(batch=1, heads=2)
-    _certificate_case(ct, wl, 0.01, "encoder shape 1x2x512x64", 1e-3, same_path=False)
+    _certificate_case(ct, wl, 0.01, "encoder shape 1x2x512x64", 1e-3, same_path=False,
+                      same_select=False)
 
 
 # ---------------------------------------------------------------------------

@@ -115,9 +115,10 @@ def _decode_common(rng, n_q, n_kv, n, d, planted, temp_range):
 
 
 def gqa_decode(n: int = 32768, n_q: int = 32, n_kv: int = 8, d: int = 128,
-               planted: int = 16, rotation: int = 0):
-    """bf16 GQA decode step (batch 1)."""
-    return _decode_common(_rng(2, rotation), n_q, n_kv, n, d, planted, None)
+               planted: int = 16, rotation: int = 0, temp_range=None):
+    """bf16 GQA decode step (batch 1); temp_range (lo, hi) multiplies each query
+    head's 1/sqrt(d) scale by a uniform draw from it (None: plain 1/sqrt(d))."""
+    return _decode_common(_rng(2, rotation), n_q, n_kv, n, d, planted, temp_range)
 
 
 def long_decode(n: int = 131072, batch: int = 4, n_q: int = 32, n_kv: int = 8,
