@@ -11,10 +11,11 @@ HBM before timing.  Steps rotate over R independent input sets (R * 128 MiB
 of K and V, above the 256 MB Infinity Cache) so that K and V come from HBM.
 
 Prints one JSON line.  `value` is query-heads/s; the roofline block is for
-the dominant kernel (the score scan): algorithmic bytes = the K bytes of one
-call divided by its average duration, timed live with HIP events that the
-library attaches to each kernel's dispatch (ctopk_record_kernel_events), over
-the same rotating steps as the headline loop.
+the dominant kernel (the one with the longest average duration):
+algorithmic bytes of one launch (kernel_bytes) divided by its average
+duration, timed live with HIP events that the library attaches to each
+kernel's dispatch (ctopk_record_kernel_events), over the same rotating steps
+as the headline loop; `rooflines` gives the same figures for every kernel.
 """
 from __future__ import annotations
 
@@ -38,11 +39,9 @@ import workloads  # noqa: E402
 
 METRIC = "certified top-k decode query-heads/s + achieved HBM GB/s (% peak), n=32K GQA"
 PEAK_HBM_GBPS = 8000.0
-# Kernels of one decode call, in launch order: score scan, level-0 histogram
-# (only for rows longer than the select holds in registers; otherwise its
-# event pair is recorded back to back and reads ~0), select, value stream,
-# output combine.
-# Kernel names per decode plan, in launch order (ctopk_plan).
+# Kernel names per decode plan, in launch order (ctopk_plan).  The level-0
+# histogram runs only for rows longer than the select holds in registers;
+# otherwise its event pair is recorded back to back and times no kernel.
 KERNELS_BY_PLAN = {
     2: ("score_scan", "hist0", "resolve", "vsum", "finalize"),
     3: ("score_scan", "hist0", "select_dense", "tail", "finalize"),
@@ -51,8 +50,18 @@ PLAN_NAMES = {1: "encoder", 2: "decode", 3: "decode_overlap"}
 # Rows of at most this many keys are resolved in registers, without the
 # separate level-0 histogram kernel (whose event pair then times no kernel).
 REGISTER_ROW_KEYS = 32768
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_scan_gqa_decode_n32768_pmc.md")
-SCAN_SOURCE = os.path.join(ROOT, "certified_top_sparse_amd", "csrc", "score_scan.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_gqa_decode_n32768.md")
+CSRC = os.path.join(ROOT, "certified_top_sparse_amd", "csrc")
+_COMMON = ("kernels.h", "device_common.h")
+# Sources each kernel is built from: a counter figure applies only while they
+# are unchanged.
+KERNEL_SOURCES = {
+    "score_scan": ("score_scan.hip",) + _COMMON,
+    "select_dense": ("select.hip", "vsum_body.h") + _COMMON,
+    "resolve": ("select.hip", "vsum_body.h") + _COMMON,
+    "tail": ("vsum.hip", "vsum_body.h") + _COMMON,
+    "vsum": ("vsum.hip", "vsum_body.h") + _COMMON,
+}
 
 
 # ---------------------------------------------------------------------------
@@ -144,26 +153,68 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def sources_digest(names):
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per score-scan dispatch from the committed rocprofv3 --pmc
-    summary, if it was taken on the current score-scan source."""
+def read_traffic(kernel):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 --pmc
+    summary, if it was taken on the kernel's current sources."""
     try:
         with open(PMC_SUMMARY) as f:
             text = f.read()
     except OSError:
         return None
     m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
-    if not m:
+    if not m or kernel not in KERNEL_SOURCES:
         return None
-    d = json.loads(m.group(1))
-    if d.get("score_scan_source_sha256_16") != source_digest(SCAN_SOURCE):
+    entry = json.loads(m.group(1)).get("kernels", {}).get(kernel)
+    if not entry or entry.get("sources_sha256_16") != sources_digest(KERNEL_SOURCES[kernel]):
         return None
-    return d.get("traffic_bytes_per_dispatch")
+    return entry.get("traffic_bytes_per_dispatch")
+
+
+def read_stream_gbps(torch, bufs, reps=60):
+    """Achievable read rate on this machine: a plain library reduction over the
+    same rotating 64 MiB K buffers the decode steps read (timed with events)."""
+    views = [b.view(torch.int32).view(-1) for b in bufs]
+    for v in views:
+        torch.sum(v)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        torch.sum(views[i % len(views)])
+    b.record()
+    torch.cuda.synchronize()
+    return sum(v.numel() * 4 for v in views) / len(views) * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def group_heads(G):
+    """Query heads per workgroup of the value passes (bf16 values)."""
+    return 1 if G == 1 else (2 if G == 2 else (4 if G <= 4 else 8))
+
+
+def tail_pass_rows(bits, k, n_kv, G, n):
+    """V rows the tail pass gathers: per head group, the keys outside some
+    head's set (tail mode: the tails together hold no more keys than the
+    largest head) or inside some head's set (head mode)."""
+    gb = group_heads(G)
+    rows = 0
+    for g in range(n_kv):
+        for z in range(0, G, gb):
+            hs = slice(g * G + z, g * G + min(G, z + gb))
+            kk = k[hs].astype(np.int64)
+            hb = bits[hs]
+            if (n - kk).sum() <= kk.max():
+                rows += int((~hb).any(axis=0).sum())
+            else:
+                rows += int(hb.any(axis=0).sum())
+    return rows
 
 
 def encoder_leg(lib, ct, torch, hip, steps, eps, sets=16):
@@ -291,6 +342,7 @@ def main():
     # Union of the group's head sets per input set: the V rows the path must read.
     G = n_q // n_kv
     union_rows = []
+    tail_rows = []
     kmean = []
     for r in range(args.sets):
         res = ct.ctopk_certify_ex(Q[r], Kd[r], Vd[r], args.eps, want_mask=True)
@@ -298,9 +350,20 @@ def main():
         words = res["sel_mask"].cpu().numpy().astype(np.int32).view(np.uint8)
         bits = np.unpackbits(words.reshape(n_q, -1), axis=1, bitorder="little")[:, :n].astype(bool)
         union_rows.append(int(bits.reshape(n_kv, G, n).any(axis=1).sum()))
-        kmean.append(float(res["k_eps"].double().mean().item()))
+        kr = res["k_eps"].cpu().numpy()
+        tail_rows.append(tail_pass_rows(bits, kr, n_kv, G, n))
+        kmean.append(float(kr.astype(np.float64).mean()))
     k_bytes = n_kv * n * d * 2
     v_bytes = float(np.mean(union_rows)) * d * 2
+    score_bytes = n_q * n * 4
+    # Algorithmic bytes of one launch of each kernel: what it must read.
+    kernel_bytes = {
+        "score_scan": k_bytes,                                   # K
+        "resolve": score_bytes,                                  # the scores
+        "vsum": v_bytes + score_bytes,                           # head-union V rows, scores
+        "select_dense": k_bytes + 2 * score_bytes,               # all of V, scores twice
+        "tail": float(np.mean(tail_rows)) * d * 2 + score_bytes,  # gathered V rows, scores
+    }
 
     # A plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters.
     src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
@@ -346,7 +409,6 @@ def main():
     # stop) event pair to each kernel's dispatch, so each pair times one kernel.
     n_ev = 2 * len(KERNELS)
     kernel_us = {}
-    scan_us = None
     ms_events = None
     if not args.no_kernel_events:
         evs = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)]
@@ -365,26 +427,28 @@ def main():
             kernel_us[name] = round(float(per[:, j].mean()) * 1e3, 3)
         if n <= REGISTER_ROW_KEYS:  # no level-0 histogram kernel is launched
             kernel_us["hist0"] = None
-        scan_us = float(per[:, 0].mean()) * 1e3
         for row in evs:
             for e in row:
                 hip.destroy(e)
 
-    roofline = None
-    if scan_us:
-        achieved = k_bytes / (scan_us * 1e-6) / 1e9
-        traffic = read_traffic()
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                    "traffic": traffic, "kernel": "score_scan_kernel<bf16,128,4>",
-                    "algorithmic_bytes_per_launch": k_bytes,
-                    "avg_launch_us": round(scan_us, 3)}
+    rooflines = {}
+    for name, us in kernel_us.items():
+        if us is None or name not in kernel_bytes:
+            continue
+        achieved = kernel_bytes[name] / (us * 1e-6) / 1e9
+        rooflines[name] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                           "traffic": read_traffic(name), "kernel": name,
+                           "algorithmic_bytes_per_launch": round(kernel_bytes[name]),
+                           "avg_launch_us": us}
+    roofline = max(rooflines.values(), key=lambda r: r["avg_launch_us"]) if rooflines else None
 
     encoder = None
     if args.encoder_steps > 0:
         encoder = encoder_leg(lib, ct, torch, hip, args.encoder_steps, eps)
 
     e2e_gbps = (k_bytes + v_bytes) / (ms_per_step * 1e-3) / 1e9
+    stream_gbps = read_stream_gbps(torch, Kd)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -402,9 +466,11 @@ def main():
                    "n_kv_heads": n_kv, "d": d, "eps": eps, "kv_dtype": "bf16",
                    "rotating_sets": args.sets},
         "roofline": roofline,
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
         "hbm_gbps_end_to_end": round(e2e_gbps, 1),
         "hbm_frac_end_to_end": round(e2e_gbps / PEAK_HBM_GBPS, 4),
+        "read_stream_gbps": round(stream_gbps, 1),
         "bytes_per_step": {"K": k_bytes, "V_union": round(v_bytes)},
         "v_union_fraction": round(v_bytes / k_bytes, 4),
         "mean_k_eps": round(float(np.mean(kmean)), 1),
