@@ -178,20 +178,22 @@ def read_traffic(kernel):
     return entry.get("traffic_bytes_per_dispatch")
 
 
-def read_stream_gbps(torch, bufs, reps=60):
-    """Achievable read rate on this machine: a plain library reduction over the
-    same rotating 64 MiB K buffers the decode steps read (timed with events)."""
-    views = [b.view(torch.int32).view(-1) for b in bufs]
-    for v in views:
-        torch.sum(v)
+def copy_stream_gbps(torch, bufs, reps=60):
+    """Achievable streaming rate on this machine: a plain device copy from the
+    same rotating 64 MiB K buffers the decode steps read into one 64 MiB
+    destination, counted as bytes read plus bytes written (timed with events)."""
+    dst = torch.empty_like(bufs[0])
+    for b in bufs:
+        dst.copy_(b)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(reps):
-        torch.sum(views[i % len(views)])
-    b.record()
+        dst.copy_(bufs[i % len(bufs)])
+    e.record()
     torch.cuda.synchronize()
-    return sum(v.numel() * 4 for v in views) / len(views) * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    nbytes = 2 * dst.numel() * dst.element_size()
+    return nbytes * reps / (a.elapsed_time(e) * 1e-3) / 1e9
 
 
 def group_heads(G):
@@ -448,7 +450,7 @@ def main():
         encoder = encoder_leg(lib, ct, torch, hip, args.encoder_steps, eps)
 
     e2e_gbps = (k_bytes + v_bytes) / (ms_per_step * 1e-3) / 1e9
-    stream_gbps = read_stream_gbps(torch, Kd)
+    stream_gbps = copy_stream_gbps(torch, Kd)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -470,7 +472,7 @@ def main():
         "cpu_baseline": cpu,
         "hbm_gbps_end_to_end": round(e2e_gbps, 1),
         "hbm_frac_end_to_end": round(e2e_gbps / PEAK_HBM_GBPS, 4),
-        "read_stream_gbps": round(stream_gbps, 1),
+        "copy_stream_gbps": round(stream_gbps, 1),
         "bytes_per_step": {"K": k_bytes, "V_union": round(v_bytes)},
         "v_union_fraction": round(v_bytes / k_bytes, 4),
         "mean_k_eps": round(float(np.mean(kmean)), 1),

@@ -28,6 +28,8 @@
 //            every pair.  key64 is unique, so the search always ends on one key.
 // Counts are exact integers, so k_eps is exact given the weights; masses are
 // fp64 sums of fp32 weights.  tau = R / Z uses the same weights as Z.
+#include <type_traits>
+
 #include "kernels.h"
 #include "vsum_body.h"
 
@@ -119,6 +121,7 @@ struct ResolveShared {
   double fin_R;
   uint32_t fin_below;
   unsigned long long kmin, kmax;
+  float f0, f1;  // bin b0 of level 0 is the score range [f0, f1)
 };
 
 // Wave totals of the current histogram (nb <= kBins bins in sh.hc / sh.hm):
@@ -261,6 +264,32 @@ __device__ void finish_small(ResolveShared& sh, int c, float m, double R, double
   }
 }
 
+// The smallest score s >= lo with lin_bin(s, lo, inv) >= b, for a whole wave
+// (every lane returns it); -inf for b <= 0 and +inf past the last bin.  The
+// bin is non-decreasing in s, so s lies in bins [b, b') iff
+// bin_floor(b) <= s < bin_floor(b'): membership by two compares instead of
+// recomputing the bin.  A 64-ary search over the order-preserving integer
+// encoding of the scores: lin_bin(lo) = 0 < b and lin_bin(+inf) = kBins - 1
+// >= b keep the answer in (L, H]; each round tests the points L + step * j,
+// j = 1..64, step = ceil((H - L) / 64), and keeps one step.
+__device__ float bin_floor(int b, float lo, float inv) {
+  if (b <= 0) return -INFINITY;
+  if (b >= kBins) return INFINITY;
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  uint32_t L = ukey(lo), H = ukey(INFINITY);
+  while (H - L > 1u) {
+    const uint32_t step = (H - L + 63u) >> 6;
+    const uint32_t off = step * (lane + 1u);  // at most (H - L) + 63 * 64 < 2^32
+    const uint32_t p = off < H - L ? L + off : H;
+    const bool ge = p == H || lin_bin(ukey_to_float(p), lo, inv) >= b;
+    const uint64_t bal = __ballot(ge);  // lane 63 tests H, so never empty
+    const int j = __ffsll(static_cast<long long>(bal)) - 1;  // first point at or past
+    H = __shfl(p, j, kWave);
+    L = j > 0 ? __shfl(p, j - 1, kWave) : L;
+  }
+  return ukey_to_float(H);
+}
+
 // The elements of one row as seen by one thread of its block: element
 // i = u * kResolveThreads + t.  With PT > 0 the thread holds its PT elements
 // in registers, all loaded when the block starts (rows of n <= PT * 1024);
@@ -279,6 +308,28 @@ struct RowElems {
 #pragma unroll
       for (int u = 0; u < PT; ++u)
         v[u] = row[min(u * kResolveThreads + static_cast<int>(threadIdx.x), last)];
+    }
+  }
+
+  // As for_each, but every slot of a register row is visited without a
+  // branch: f(i, s, valid), where slots past n (valid false) hold a copy of
+  // the row's last element and must contribute nothing.
+  template <typename F>
+  __device__ __forceinline__ void for_each_all(F&& f) {
+    if constexpr (PT > 0) {
+      int t = threadIdx.x;
+      asm volatile("" : "+v"(t));
+#pragma unroll
+      for (int u = 0; u < PT; ++u) asm volatile("" : "+v"(v[u]));
+      const int nn = static_cast<int>(n);
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int i = u * kResolveThreads + t;
+        f(static_cast<int64_t>(i), v[u], i < nn);
+        if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for_each([&](int64_t i, float s) { f(i, s, true); });
     }
   }
 
@@ -384,8 +435,8 @@ __device__ __forceinline__ void resolve_row(
   } else {
     for (int b = t; b < kBins; b += kResolveThreads) sh.hm[b] = 0.0;
     __syncthreads();
-    E.for_each([&](int64_t, float s) {
-      atomicAdd(&sh.hm[lin_bin(s, lo, inv)], static_cast<double>(weight(s, m)));
+    E.for_each_all([&](int64_t, float s, bool valid) {
+      atomicAdd(&sh.hm[lin_bin(s, lo, inv)], valid ? static_cast<double>(weight(s, m)) : 0.0);
     });
   }
   __syncthreads();
@@ -414,22 +465,36 @@ __device__ __forceinline__ void resolve_row(
   // up to kCandCap of them, with one LDS atomic per wave and step; returns
   // how many there are.  With count_below it also adds the number of keys in
   // lower bins to `below`.
-  auto collect = [&](bool count_below) -> uint32_t {
+  // Bin b0 is the score range [f0, f1) (two waves search in parallel).
+  if (wave < 2) {
+    const float f = bin_floor(b0 + wave, lo, inv);
+    if (lane == 0) (wave == 0 ? sh.f0 : sh.f1) = f;
+  }
+  auto collect = [&](bool count_below, auto with_prefix) -> uint32_t {
+    // Only passes after the first (plen > 0) match the key prefix; the first
+    // builds key64 only in waves that hold a candidate.
+    constexpr bool kPrefix = decltype(with_prefix)::value;
     if (t == 0) {
       sh.ncand = 0u;
       sh.kmin = ~0ull;
       sh.kmax = 0ull;
     }
     __syncthreads();
+    const float f0 = sh.f0, f1 = sh.f1;
     uint32_t nbelow = 0u;
     unsigned long long kmn = ~0ull, kmx = 0ull;
-    E.for_each([&](int64_t i, float s) {
-      const int bin = lin_bin(s, lo, inv);
-      nbelow += bin < b0 ? 1u : 0u;
-      const uint64_t k = key64(s, static_cast<uint32_t>(i));
-      const bool in = bin == b0 && prefix_match(k, prefix, plen);
+    E.for_each_all([&](int64_t i, float s, bool valid) {
+      // bitwise, not short-circuit: no branch per key
+      nbelow += (valid & (s < f0)) ? 1u : 0u;
+      bool in = valid & (s >= f0) & (s < f1);
+      uint64_t k = 0ull;
+      if constexpr (kPrefix) {
+        k = key64(s, static_cast<uint32_t>(i));
+        in = in & prefix_match(k, prefix, plen);
+      }
       const uint64_t bal = __ballot(in);
       if (bal != 0ull) {
+        if constexpr (!kPrefix) k = key64(s, static_cast<uint32_t>(i));
         const int leader = __ffsll(static_cast<long long>(bal)) - 1;
         uint32_t base = 0u;
         if (lane == leader) base = atomicAdd(&sh.ncand, static_cast<uint32_t>(__popcll(bal)));
@@ -468,7 +533,7 @@ __device__ __forceinline__ void resolve_row(
     return sh.ncand;
   };
 
-  uint32_t cnt_in = collect(true);
+  uint32_t cnt_in = collect(true, std::false_type{});
   uint32_t ncand = min(cnt_in, static_cast<uint32_t>(kCandCap));
   bool in_lds = cnt_in <= static_cast<uint32_t>(kCandCap);
   if (in_lds) {  // skip the leading bits all candidates share
@@ -486,7 +551,7 @@ __device__ __forceinline__ void resolve_row(
   // keys, the bound only guards against non-finite scores.
   for (int guard = 0; guard < 16 && !done; ++guard) {
     if (!in_lds && cnt_in <= static_cast<uint32_t>(kCandCap)) {
-      cnt_in = collect(false);
+      cnt_in = collect(false, std::true_type{});
       ncand = min(cnt_in, static_cast<uint32_t>(kCandCap));
       in_lds = true;
       // Skip the leading bits all candidates share.
@@ -537,8 +602,9 @@ __device__ __forceinline__ void resolve_row(
         }
       }
     } else {
+      const float f0 = sh.f0, f1 = sh.f1;
       E.for_each([&](int64_t i, float s) {
-        if (lin_bin(s, lo, inv) == b0) {
+        if (s >= f0 && s < f1) {
           const uint64_t k = key64(s, static_cast<uint32_t>(i));
           if (prefix_match(k, prefix, plen)) {
             const int b = static_cast<int>((k >> shift) & static_cast<uint64_t>(nb - 1));
