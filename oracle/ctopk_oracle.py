@@ -29,15 +29,25 @@ Readings where the page leaves a step open:
 * diam_{H,T} is the largest Euclidean distance between a head value row and a
   tail value row;
 * a row is "near-boundary" when T_{k_eps} or T_{k_eps - 1} lies within
-  1e-6 * eps of eps; such rows are reported, not failed, on a k_eps mismatch.
+  1e-6 * eps of eps; such rows are reported, not failed, on a k_eps mismatch;
+* the blockwise deterministic bound (the Abstract names "blockwise variants"
+  of bounds that control TV from the ordered logits, without printing one):
+  with the keys cut into consecutive blocks B of `block` keys, block maxima
+  M_B and m = max s, the softmax mass of the keys scoring below a threshold t
+  is at most U(t) = sum_{M_B < t} |B| e^{M_B - m} + sum_{M_B >= t} (|B| - 1)
+  e^{t - m} (a block whose maximum is below t has all its keys below t; any
+  other block has at most |B| - 1 keys below t, each of weight below
+  e^{t - m}); the certified truncation keeps H_t = {i : s_i >= t} for the
+  largest t with U(t) <= eps * Z, so TV(P, P_hat_{H_t}) <= U(t) / Z <= eps.
 
 Everything is computed in float64.  bf16 and fp32 inputs convert to float64
 exactly.  The score scale is applied as the float64 value of the float32 the
 device receives.
 
 Parity status: every function here is pinned by the tests in
-``tests/test_oracle_pins.py`` (identities, brute force, closed forms and the
-Gaussian design rule).  The pages print no worked example, so no specific
+``tests/test_oracle_pins.py`` (identities, brute force, closed forms, the
+Gaussian design rule, and the blockwise bound's validity, monotonicity and
+optimality).  The pages print no worked example, so no specific
 (q, K, V) -> (k_eps, tau, out) triple is pinned by a printed value.
 """
 from __future__ import annotations
@@ -296,3 +306,96 @@ def gaussian_tail_fraction(sigma: float, z: float) -> float:
     the large-n limit: E[e^s 1{s <= t}] / E[e^s] = Phi(z - sigma)."""
     from scipy.special import ndtr
     return float(ndtr(z - sigma))
+
+
+# ---------------------------------------------------------------------------
+# blockwise deterministic bound (Abstract: "blockwise variants" of the
+# deterministic bounds that control TV from the ordered logits)
+# ---------------------------------------------------------------------------
+BOUND_BLOCK = 64
+
+
+def block_maxima(s, block: int = BOUND_BLOCK):
+    """Maxima and sizes of the consecutive blocks of `block` keys of one row."""
+    s = np.asarray(s, dtype=np.float64)
+    n = s.shape[-1]
+    nb = -(-n // block)
+    M = np.array([s[b * block:(b + 1) * block].max() for b in range(nb)])
+    sizes = np.array([min(block, n - b * block) for b in range(nb)], dtype=np.float64)
+    return M, sizes
+
+
+def block_bound(M, sizes, m: float, t: float) -> float:
+    """U(t) * e^{-m} scale: sum_{M_B < t} |B| e^{M_B - m} + sum_{M_B >= t} (|B| - 1) e^{t - m},
+    an upper bound on the softmax mass (unnormalised, relative to e^m) of the
+    keys scoring below t."""
+    below = M < t
+    return float(np.sum(sizes[below] * np.exp(M[below] - m))
+                 + np.sum(sizes[~below] - 1.0) * math.exp(t - m))
+
+
+def bound_threshold(s, eps: float, block: int = BOUND_BLOCK):
+    """The largest t with U(t) <= eps * Z, and U(t).
+
+    U is non-decreasing in t and equal to A_j + c_j e^{t - m} on the interval
+    (M_(j-1), M_(j)] between consecutive sorted block maxima (A_j sums
+    |B| e^{M_B - m} over the j blocks with the smallest maxima, c_j sums
+    |B| - 1 over the others), so the largest feasible t of each interval is
+    min(M_(j), m + log((eps Z - A_j) / c_j)); the answer is the one of the
+    last interval where that exceeds M_(j-1).  Returns (t, U(t), Z, m)."""
+    s = np.asarray(s, dtype=np.float64)
+    m = float(s.max())
+    Z = float(np.sum(np.exp(s - m)))
+    M, sizes = block_maxima(s, block)
+    order = np.argsort(M, kind="stable")
+    Ms, szs = M[order], sizes[order]
+    nb = len(Ms)
+    A = np.concatenate([[0.0], np.cumsum(szs * np.exp(Ms - m))])
+    c = np.concatenate([np.cumsum((szs - 1.0)[::-1])[::-1], [0.0]])
+    budget = eps * Z
+    best = -math.inf
+    for j in range(nb):
+        lo = Ms[j - 1] if j > 0 else -math.inf
+        if A[j] > budget:
+            break
+        if c[j] > 0.0:
+            room = budget - A[j]
+            tj = min(Ms[j], m + math.log(room / c[j])) if room > 0.0 else -math.inf
+        else:
+            tj = Ms[j]
+        if tj > lo:
+            best = tj
+    return best, block_bound(M, sizes, m, best), Z, m
+
+
+def certify_bound(S, V, eps: float, row_to_v=None, block: int = BOUND_BLOCK):
+    """Certified truncation from the blockwise bound, for every row of S.
+
+    Keeps H_t = {i : s_i >= t} at the threshold of bound_threshold.  Returns
+    a dict: t [R], k [R] (= |H_t|, never below the minimal k_eps), tau_bound
+    [R] (= U(t) / Z <= eps), tv [R] (the exact TV of the truncation,
+    <= tau_bound), out [R, dv] (head-only renormalised output over H_t) and
+    head_mask [R, n]."""
+    S = np.atleast_2d(np.asarray(S, dtype=np.float64))
+    V = as_f64(V)
+    if V.ndim == 2:
+        V = V[None]
+    R, n = S.shape
+    if row_to_v is None:
+        row_to_v = np.zeros(R, dtype=np.int64)
+    if not (0.0 < eps < 1.0):
+        raise ValueError("eps must lie in (0, 1)")
+    ts, tb, tv, ks = np.empty(R), np.empty(R), np.empty(R), np.empty(R, dtype=np.int64)
+    head = np.zeros((R, n), dtype=bool)
+    out = np.empty((R, V.shape[-1]))
+    for r in range(R):
+        t, U, Z, m = bound_threshold(S[r], eps, block)
+        w = np.exp(S[r] - m)
+        h = S[r] >= t
+        head[r] = h
+        ks[r] = int(h.sum())
+        ts[r], tb[r] = t, U / Z
+        tv[r] = float(np.sort(w[~h]).sum()) / Z
+        out[r] = (w[h] @ V[row_to_v[r]][h]) / w[h].sum()
+    return {"t": ts, "k": ks, "tau_bound": tb, "tv": tv, "out": out, "head_mask": head}
+

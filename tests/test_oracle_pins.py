@@ -299,3 +299,87 @@ def test_eps_outside_open_interval_rejected():
     for eps in (0.0, 1.0, -0.1, 1.5):
         with pytest.raises(ValueError):
             oracle.certify_scores(np.zeros((1, 4)), np.ones((1, 4, 1)), eps)
+
+
+# ---------------------------------------------------------------------------
+# blockwise deterministic bound (Abstract: "blockwise variants")
+# ---------------------------------------------------------------------------
+def _bound_rows(seed, n, sigma, count=3):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((count, n)) * sigma
+
+
+@pytest.mark.parametrize("block", [1, 7, 64])
+@pytest.mark.parametrize("sigma", [0.5, 2.0, 4.0])
+def test_block_bound_dominates_tail_mass(block, sigma):
+    # U(t) >= the brute-force mass of the keys below t, at random thresholds
+    for s in _bound_rows(11, 700, sigma):
+        m = s.max()
+        M, sizes = oracle.block_maxima(s, block)
+        w = np.exp(s - m)
+        for t in np.random.default_rng(1).uniform(s.min() - 1, m + 1, 50):
+            assert w[s < t].sum() <= oracle.block_bound(M, sizes, m, t) * (1 + 1e-12) + 1e-300
+
+
+def test_block_bound_is_monotone():
+    s = _bound_rows(12, 900, 2.0, 1)[0]
+    M, sizes = oracle.block_maxima(s, 64)
+    ts = np.sort(np.concatenate([np.linspace(s.min() - 1, s.max() + 1, 400), M]))
+    U = np.array([oracle.block_bound(M, sizes, s.max(), t) for t in ts])
+    assert np.all(np.diff(U) >= -1e-12 * U[1:])
+
+
+@pytest.mark.parametrize("eps", [0.001, 0.01, 0.1, 0.5])
+def test_bound_threshold_is_the_largest_feasible(eps):
+    # against a dense grid of thresholds: no grid point above t keeps U <= eps Z
+    for s in _bound_rows(13, 1500, 2.0):
+        t, U, Z, m = oracle.bound_threshold(s, eps)
+        assert U <= eps * Z * (1 + 1e-12)
+        M, sizes = oracle.block_maxima(s)
+        grid = np.linspace(t, s.max() + 1, 3000)[1:]
+        feas = [g for g in grid if oracle.block_bound(M, sizes, m, g) <= eps * Z]
+        assert not feas or max(feas) - t <= 1e-9 * max(1.0, abs(t))
+
+
+@pytest.mark.parametrize("eps", [0.01, 0.1])
+@pytest.mark.parametrize("sigma", [1.0, 3.0])
+def test_bound_certificate_properties(eps, sigma):
+    S = _bound_rows(14, 3000, sigma, 4)
+    V = np.random.default_rng(2).standard_normal((1, 3000, 8))
+    b = oracle.certify_bound(S, V, eps)
+    e = oracle.certify_scores(S, V, eps)
+    assert np.all(b["tv"] <= b["tau_bound"] * (1 + 1e-12))
+    assert np.all(b["tau_bound"] <= eps * (1 + 1e-12))
+    assert np.all(b["k"] >= e["k_eps"])  # a valid certificate is never smaller than the minimal one
+    for r in range(S.shape[0]):  # H_t is a top set: every kept key outscores every dropped key
+        h = b["head_mask"][r]
+        if (~h).any():  # the bound may also keep every key
+            assert S[r][h].min() > S[r][~h].max()
+        assert b["k"][r] == h.sum()
+
+
+def test_bound_closed_form_equal_scores():
+    # all scores equal: every block maximum is 0, Z = n, and on (-inf, 0] the
+    # bound is (n - nb) e^t, so t = log(eps n / (n - nb)), every key is kept
+    # and the certified bound is exactly eps
+    n, eps = 1000, 0.05
+    nb = -(-n // 64)
+    t, U, Z, m = oracle.bound_threshold(np.zeros(n), eps)
+    assert Z == n and m == 0.0
+    assert t == pytest.approx(math.log(eps * n / (n - nb)), rel=1e-13)
+    assert U / Z == pytest.approx(eps, rel=1e-13)
+    b = oracle.certify_bound(np.zeros((1, n)), np.ones((1, n, 2)), eps)
+    assert b["k"][0] == n and b["tv"][0] == 0.0
+
+
+@pytest.mark.parametrize("eps", [0.001, 0.01, 0.2])
+def test_bound_with_unit_blocks_is_the_minimal_topk(eps):
+    # blocks of one key make the bound exact (U(t) is the mass below t), so the
+    # certified head is the minimal Top-k head
+    rng = np.random.default_rng(15)
+    S = rng.standard_normal((5, 800)) * 2.0
+    V = rng.standard_normal((1, 800, 4))
+    b = oracle.certify_bound(S, V, eps, block=1)
+    e = oracle.certify_scores(S, V, eps)
+    assert np.array_equal(b["k"], e["k_eps"])
+    assert np.array_equal(b["head_mask"], e["head_mask"])
