@@ -45,8 +45,9 @@ PEAK_HBM_GBPS = 8000.0
 KERNELS_BY_PLAN = {
     2: ("score_scan", "hist0", "resolve", "vsum", "finalize"),
     3: ("score_scan", "hist0", "select_dense", "tail", "finalize"),
+    4: ("score_scan", "hist0", "bound", "vsum", "finalize"),
 }
-PLAN_NAMES = {1: "encoder", 2: "decode", 3: "decode_overlap"}
+PLAN_NAMES = {1: "encoder", 2: "decode", 3: "decode_overlap", 4: "decode_bound"}
 # Rows of at most this many keys are resolved in registers, without the
 # separate level-0 histogram kernel (whose event pair then times no kernel).
 REGISTER_ROW_KEYS = 32768
@@ -219,6 +220,66 @@ def tail_pass_rows(bits, k, n_kv, G, n):
     return rows
 
 
+def bound_leg(lib, ct, torch, hip, Q, Kd, Vd, steps, eps):
+    """The same decode workload certified by the blockwise bound
+    (CTOPK_FLAG_BOUND): per-call time, per-kernel times and the keys kept,
+    against the exact select's."""
+    sets = len(Q)
+    n_q, d = Q[0].shape
+    n = Kd[0].shape[1]
+    out = torch.empty((n_q, d), dtype=torch.float32, device="cuda")
+    k_eps = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    tau = torch.empty(n_q, dtype=torch.float64, device="cuda")
+    args = [ct.make_args(Q[r], Kd[r], Vd[r], eps, out=out, k_eps=k_eps, tau=tau,
+                         flags=ct.CTOPK_FLAG_BOUND) for r in range(sets)]
+    assert ct.ctopk_plan(args[0]) == ct.CTOPK_PLAN_DECODE_BOUND
+    names = KERNELS_BY_PLAN[ct.CTOPK_PLAN_DECODE_BOUND]
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lib.ctopk_certify_ex
+
+    def step(i):
+        rc = call(ctypes.byref(args[i % sets]), sptr)
+        if rc != 0:
+            raise RuntimeError(ct.ctopk_last_error_string())
+
+    kmean, taumax = [], 0.0
+    for i in range(sets):
+        step(i)
+        torch.cuda.synchronize()
+        kmean.append(float(k_eps.double().mean().item()))
+        taumax = max(taumax, float(tau.max().item()))
+    for i in range(20):
+        step(i)
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), sptr)
+    for i in range(steps):
+        step(i)
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), sptr)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    n_ev = 2 * len(names)
+    evs = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    arrs = [(ctypes.c_void_p * n_ev)(*[ctypes.c_void_p(e) for e in row]) for row in evs]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        lib.ctopk_record_kernel_events(arrs[i], n_ev)
+        step(i)
+    torch.cuda.synchronize()
+    per = np.array([[hip.elapsed_ms(row[2 * j], row[2 * j + 1]) for j in range(len(names))]
+                    for row in evs])
+    kern = {name: (None if name == "hist0" else round(float(per[:, j].mean()) * 1e3, 3))
+            for j, name in enumerate(names)}
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    return {"eps": eps, "steps": steps, "us_per_call": round(us, 3),
+            "query_heads_per_s": round(n_q / (us * 1e-6), 1), "kernel_us": kern,
+            "mean_k_over_n": round(float(np.mean(kmean)) / n, 4), "max_tau": taumax}
+
+
 def encoder_leg(lib, ct, torch, hip, steps, eps, sets=16):
     """All-queries (encoder-shaped) workload: batch 8, 12 heads, 512 queries and
     512 keys per head, d = 64, bf16, per-head temperature; every query row of a
@@ -301,6 +362,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--bound-steps", type=int, default=1000,
+                    help="calls of the blockwise-bound leg on the decode workload; 0 skips it")
     ap.add_argument("--encoder-steps", type=int, default=500,
                     help="calls of the all-queries (encoder-shaped) leg; 0 skips it")
     args = ap.parse_args()
@@ -445,6 +508,10 @@ def main():
                            "avg_launch_us": us}
     roofline = max(rooflines.values(), key=lambda r: r["avg_launch_us"]) if rooflines else None
 
+    bound = None
+    if args.bound_steps > 0:
+        bound = bound_leg(lib, ct, torch, hip, Q, Kd, Vd, args.bound_steps, eps)
+
     encoder = None
     if args.encoder_steps > 0:
         encoder = encoder_leg(lib, ct, torch, hip, args.encoder_steps, eps)
@@ -479,6 +546,7 @@ def main():
         "plan": PLAN_NAMES.get(plan, plan),
         "kernel_us": kernel_us,
         "ms_per_step_with_kernel_events": None if ms_events is None else round(ms_events, 5),
+        "bound_certificate": bound,
         "encoder": encoder,
     }
     print(json.dumps(line), flush=True)

@@ -6,7 +6,8 @@ declared in include/ctopk.h).  This package holds the kernels' sources
 whose functions carry the C names.
 """
 from .ctopk import (  # noqa: F401
-    CTOPK_BF16, CTOPK_F32, CTOPK_PLAN_DECODE, CTOPK_PLAN_DECODE_OVERLAP, CTOPK_PLAN_ENCODER,
+    CTOPK_BF16, CTOPK_F32, CTOPK_FLAG_BOUND, CTOPK_PLAN_DECODE, CTOPK_PLAN_DECODE_BOUND,
+    CTOPK_PLAN_DECODE_OVERLAP, CTOPK_PLAN_ENCODER,
     CtopkArgs, CtopkError, EXPORTED, LIB_PATH, ctopk_certify,
     ctopk_certify_ex, ctopk_certify_logits, ctopk_last_error_string,
     ctopk_logits_workspace_bytes, ctopk_plan, ctopk_record_kernel_events, ctopk_validate,

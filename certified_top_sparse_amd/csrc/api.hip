@@ -69,7 +69,7 @@ constexpr int64_t kMaxElems = 1LL << 36;  // rows * n
 // Scratch layout shared by both paths (every region is fully written before
 // it is read within a call, so nothing needs zeroing).
 struct Layout {
-  size_t rowsel = 0, blkstat = 0, part = 0, pmass = 0;
+  size_t rowsel = 0, blkstat = 0, blkz = 0, part = 0, pmass = 0;
   size_t scores = 0, total = 0;
   int nblk = 0, nchunk = 0, hchunk = 0;
   int dchunk = 0;  // dense-stream chunks of the overlapped decode path (0: not taken)
@@ -89,6 +89,8 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   off += up(static_cast<size_t>(rows) * sizeof(ctopk::RowSel));
   L.blkstat = off;
   off += up(static_cast<size_t>(rows) * L.nblk * sizeof(float2));
+  L.blkz = off;  // per-tile softmax masses (blockwise-bound calls)
+  off += up(static_cast<size_t>(rows) * L.nblk * sizeof(float));
   L.part = off;
   off += up(static_cast<size_t>(rows) * pslots * (dv + 1) * sizeof(float));
   L.pmass = off;
@@ -161,6 +163,11 @@ int validate_args(const ctopk_args* a) {
                 a->n_q_heads, a->n_kv_heads);
   if (a->n_kv_heads > 65535)
     return fail(CTOPK_ERR_UNSUPPORTED, "n_kv_heads above 65535 is not supported");
+  if ((a->flags & ~CTOPK_FLAG_BOUND) != 0u)
+    return fail(CTOPK_ERR_UNSUPPORTED, "unknown flags 0x%x", a->flags & ~CTOPK_FLAG_BOUND);
+  if ((a->flags & CTOPK_FLAG_BOUND) && ctopk::ceil_div(a->n, ctopk::kScanTile) > ctopk::kBoundMaxTiles)
+    return fail(CTOPK_ERR_UNSUPPORTED, "the blockwise bound supports n <= %d",
+                ctopk::kBoundMaxTiles * ctopk::kScanTile);
   if (static_cast<int64_t>(a->n_q_heads) * a->n > kMaxElems)
     return fail(CTOPK_ERR_UNSUPPORTED, "n_q_heads * n above 2^36 is not supported");
   int rc = check_eps(a->eps);
@@ -185,6 +192,7 @@ int validate_args(const ctopk_args* a) {
 
 // The plan of a validated call (ctopk_plan_id).
 int plan_of(const ctopk_args* a) {
+  if (a->flags & CTOPK_FLAG_BOUND) return CTOPK_PLAN_DECODE_BOUND;
   const bool certificate = a->out_err != nullptr || a->out_dense != nullptr;
   if (certificate) return CTOPK_PLAN_DECODE;
   if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads))
@@ -277,6 +285,7 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   }
   float* scores = a->scores ? a->scores : reinterpret_cast<float*>(ws + L.scores);
   float2* blkstat = reinterpret_cast<float2*>(ws + L.blkstat);
+  float* blkz = plan == CTOPK_PLAN_DECODE_BOUND ? reinterpret_cast<float*>(ws + L.blkz) : nullptr;
   float* part = reinterpret_cast<float*>(ws + L.part);
   double* pmass = reinterpret_cast<double*>(ws + L.pmass);
   ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
@@ -284,10 +293,10 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
 
   rc = hip_check(ctopk::launch_score_scan(a->q, a->K, a->dtype, a->d, a->head_scale,
                                           default_scale, a->n, rows, a->n_kv_heads, scores,
-                                          blkstat, nullptr, 0, st),
+                                          blkstat, blkz, nullptr, 0, st),
                  "score_scan launch");
   if (rc != CTOPK_OK) return rc;
-  if (L.hchunk > 0) {  // long rows: level 0 from many blocks per row
+  if (L.hchunk > 0 && plan != CTOPK_PLAN_DECODE_BOUND) {  // long rows: level 0 from many blocks per row
     rc = hip_check(ctopk::launch_hist0(scores, a->n, rows, blkstat, L.nblk, L.hchunk, pmass,
                                        st),
                    "hist0 launch");
@@ -312,10 +321,16 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
     if (rc != CTOPK_OK) return rc;
     return ok();
   }
-  rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, blkstat, L.nblk, pmass,
-                                       L.hchunk, a->eps, rs, a->k_eps, a->tau, a->lse,
-                                       a->sel_mask, nullptr, 0, st),
-                 "resolve launch");
+  if (plan == CTOPK_PLAN_DECODE_BOUND) {
+    rc = hip_check(ctopk::launch_bound(scores, a->n, rows, blkstat, blkz, L.nblk, a->eps, rs,
+                                       a->k_eps, a->tau, a->lse, a->sel_mask, st),
+                   "bound launch");
+  } else {
+    rc = hip_check(ctopk::launch_resolve(scores, a->n, rows, blkstat, L.nblk, pmass,
+                                         L.hchunk, a->eps, rs, a->k_eps, a->tau, a->lse,
+                                         a->sel_mask, nullptr, 0, st),
+                   "resolve launch");
+  }
   if (rc != CTOPK_OK) return rc;
   rc = hip_check(ctopk::launch_vsum(scores, a->n, rows, a->n_kv_heads, a->V, a->dtype, a->d, rs,
                                     part, L.nchunk, a->out, a->out_dense, a->out_err, st),

@@ -24,6 +24,8 @@ constexpr int kCandCap = 8192;
 // Most keys per chunk of the tail pass of the overlapped decode plan (its key
 // list lives in LDS).
 constexpr int kFixKeys = 2048;
+// Most score-scan tiles per row for the blockwise bound (sorted in LDS).
+constexpr int kBoundMaxTiles = 2048;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -49,10 +51,11 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shme
 }
 
 // K1: scores[h, i] = scale_h * <q_h, K[h / G, i]> and blkstat[h, tile] =
-// (min, max) over the tile.  Also zeroes `zero_bytes` at `zero_base`.
+// (min, max) over the tile; with blkz non-NULL also blkz[h, tile] = the sum
+// over the tile of exp(s - its max).  Also zeroes `zero_bytes` at `zero_base`.
 hipError_t launch_score_scan(const void* q, const void* K, int dtype, int d,
                              const float* head_scale, float default_scale, int64_t n,
-                             int n_q, int n_kv, float* scores, float2* blkstat,
+                             int n_q, int n_kv, float* scores, float2* blkstat, float* blkz,
                              void* zero_base, size_t zero_bytes, hipStream_t st);
 
 // Level 0 of the select for long decode rows, many blocks per row: row
@@ -110,6 +113,15 @@ hipError_t launch_tail_fix(const float* scores, int64_t n, int rows, int n_v, co
                            int v_dtype, int dv, const RowSel* rs, const int32_t* k_eps,
                            const float* dpart, float* part, int nchunk, float* out,
                            hipStream_t st);
+
+// Blockwise deterministic bound, one workgroup per row: from the scan's tile
+// (min, max) and tile masses blkz, the largest threshold whose bound on the
+// mass below it fits eps * Z; keeps every key at or above it.  Writes RowSel
+// (thr at that score), k_eps (keys kept), tau (the certified bound), lse and
+// sel_mask (optional).  nblk <= kBoundMaxTiles.
+hipError_t launch_bound(const float* scores, int64_t n, int rows, const float2* blkstat,
+                        const float* blkz, int nblk, double eps, RowSel* rs, int32_t* k_eps,
+                        double* tau, double* lse, uint32_t* sel_mask, hipStream_t st);
 
 // Encoder-shaped path (all queries of a head, n <= 512, bf16, MFMA QK^T).
 hipError_t launch_encoder(const void* q, const void* K, const void* V, int d,

@@ -69,7 +69,7 @@ template <typename T, int D, int GB, bool HS>
 __global__ __launch_bounds__(256) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ K, const float* __restrict__ head_scale,
     float default_scale, int64_t n, int G, int nblk, float* __restrict__ scores,
-    float2* __restrict__ blkstat, void* zero_base, size_t zero_bytes) {
+    float2* __restrict__ blkstat, float* __restrict__ blkz, void* zero_base, size_t zero_bytes) {
   constexpr int EPL = Slice<T>::kElems;
   constexpr int LPR = D / EPL;
   constexpr int RPW = kWave / LPR;
@@ -145,53 +145,61 @@ __global__ __launch_bounds__(256) void score_scan_kernel(
     vmax = wave_max_dpp(vmax);
     vmin = -wave_max_dpp(-vmin);
     if (lane == 0) blkstat[static_cast<size_t>(h0 + j) * nblk + tile] = make_float2(vmin, vmax);
+    if (blkz != nullptr) {  // the tile's softmax mass relative to its maximum
+      static_assert(kScanTile == kWave, "one key per lane");
+      const int64_t i = tile0 + lane;
+      const float z = group_sum<kWave>(i < n ? weight(s_sc[j][lane], vmax) : 0.0f);
+      if (lane == 0) blkz[static_cast<size_t>(h0 + j) * nblk + tile] = z;
+    }
   }
 }
 
 template <typename T, int D, int GB>
 hipError_t launch_t(const void* q, const void* K, const float* head_scale, float default_scale,
-                    int64_t n, int n_q, int n_kv, float* scores, float2* blkstat, void* zb,
-                    size_t zbytes, hipStream_t st) {
+                    int64_t n, int n_q, int n_kv, float* scores, float2* blkstat, float* blkz,
+                    void* zb, size_t zbytes, hipStream_t st) {
   const int G = n_q / n_kv;
   const int nblk = static_cast<int>(ceil_div(n, kScanTile));
   dim3 grid(nblk, n_kv, static_cast<unsigned>(ceil_div(G, GB)));
   if (head_scale != nullptr)
     return launch(score_scan_kernel<T, D, GB, true>, grid, dim3(256), 0, st,
                   static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale,
-                  n, G, nblk, scores, blkstat, zb, zbytes);
+                  n, G, nblk, scores, blkstat, blkz, zb, zbytes);
   return launch(score_scan_kernel<T, D, GB, false>, grid, dim3(256), 0, st,
                 static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale, n,
-                G, nblk, scores, blkstat, zb, zbytes);
+                G, nblk, scores, blkstat, blkz, zb, zbytes);
 }
 
 template <typename T, int D>
 hipError_t launch_d(const void* q, const void* K, const float* hs, float ds, int64_t n, int n_q,
-                    int n_kv, float* scores, float2* bs, void* zb, size_t zbytes,
+                    int n_kv, float* scores, float2* bs, float* bz, void* zb, size_t zbytes,
                     hipStream_t st) {
   const int G = n_q / n_kv;
-  if (G == 1) return launch_t<T, D, 1>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
-  if (G == 2) return launch_t<T, D, 2>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
-  if (G <= 4) return launch_t<T, D, 4>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
-  return launch_t<T, D, 8>(q, K, hs, ds, n, n_q, n_kv, scores, bs, zb, zbytes, st);
+#define CTOPK_SCAN(GB) launch_t<T, D, GB>(q, K, hs, ds, n, n_q, n_kv, scores, bs, bz, zb, zbytes, st)
+  if (G == 1) return CTOPK_SCAN(1);
+  if (G == 2) return CTOPK_SCAN(2);
+  if (G <= 4) return CTOPK_SCAN(4);
+  return CTOPK_SCAN(8);
+#undef CTOPK_SCAN
 }
 
 }  // namespace
 
 hipError_t launch_score_scan(const void* q, const void* K, int dtype, int d,
                              const float* head_scale, float default_scale, int64_t n, int n_q,
-                             int n_kv, float* scores, float2* blkstat, void* zero_base,
-                             size_t zero_bytes, hipStream_t st) {
+                             int n_kv, float* scores, float2* blkstat, float* blkz,
+                             void* zero_base, size_t zero_bytes, hipStream_t st) {
   if (dtype == 1) {
     if (d == 128)
       return launch_d<uint16_t, 128>(q, K, head_scale, default_scale, n, n_q, n_kv, scores,
-                                     blkstat, zero_base, zero_bytes, st);
+                                     blkstat, blkz, zero_base, zero_bytes, st);
     return launch_d<uint16_t, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
-                                  zero_base, zero_bytes, st);
+                                  blkz, zero_base, zero_bytes, st);
   }
   if (d == 128)
     return launch_d<float, 128>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
-                                zero_base, zero_bytes, st);
-  return launch_d<float, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
+                                blkz, zero_base, zero_bytes, st);
+  return launch_d<float, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat, blkz,
                              zero_base, zero_bytes, st);
 }
 

@@ -29,6 +29,8 @@ CTOPK_BF16 = 1
 CTOPK_PLAN_ENCODER = 1
 CTOPK_PLAN_DECODE = 2
 CTOPK_PLAN_DECODE_OVERLAP = 3
+CTOPK_PLAN_DECODE_BOUND = 4
+CTOPK_FLAG_BOUND = 1
 
 STATUS_NAMES = {
     0: "CTOPK_OK", -1: "CTOPK_ERR_NULL", -2: "CTOPK_ERR_SHAPE", -3: "CTOPK_ERR_EPS",
@@ -67,6 +69,7 @@ class CtopkArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("out_err", ctypes.c_void_p),
         ("out_dense", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -209,7 +212,7 @@ def ctopk_certify(q, K, V, eps, out=None, k_eps=None, tau=None, stream=None):
 
 def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=None,
               tau=None, sel_mask=None, scores=None, lse=None, out_err=None,
-              out_dense=None) -> CtopkArgs:
+              out_dense=None, flags=0) -> CtopkArgs:
     n_q, d = q.shape
     n_kv, n, _ = K.shape
     a = CtopkArgs()
@@ -224,18 +227,21 @@ def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=
                  ("scores", scores), ("lse", lse), ("out_err", out_err),
                  ("out_dense", out_dense)):
         setattr(a, f, None if t is None else t.data_ptr())
+    a.flags = int(flags)
     return a
 
 
 def ctopk_certify_ex(q, K, V, eps, *, head_scale=None, workspace=None, want_mask=False,
                      want_scores=False, want_lse=False, want_err=False, want_dense=False,
-                     stream=None):
+                     bound=False, stream=None):
     """Full form: q [Hq, d], K/V [Hkv, n, d] in bf16 or fp32, optional per-head
     scale [Hq] fp32 and caller workspace (uint8 tensor).
 
     Returns a dict with out, k_eps, tau and, on request, sel_mask
     [Hq, ceil(n/32)] int32 bit words, scores [Hq, n] fp32, lse [Hq] fp64,
-    out_err [Hq] fp64 (||Attn - Attn_k||_2) and out_dense [Hq, d] fp32 (Attn)."""
+    out_err [Hq] fp64 (||Attn - Attn_k||_2) and out_dense [Hq, d] fp32 (Attn).
+    bound=True certifies with the blockwise bound (CTOPK_FLAG_BOUND): k_eps is
+    then the number of keys kept and tau the certified bound on their TV."""
     import torch
     lib = load()
     for name, t in (("q", q), ("K", K), ("V", V)):
@@ -267,7 +273,7 @@ def ctopk_certify_ex(q, K, V, eps, *, head_scale=None, workspace=None, want_mask
     a = make_args(q, K, V, eps, head_scale=head_scale, workspace=workspace, out=res["out"],
                   k_eps=res["k_eps"], tau=res["tau"], sel_mask=res.get("sel_mask"),
                   scores=res.get("scores"), lse=res.get("lse"), out_err=res.get("out_err"),
-                  out_dense=res.get("out_dense"))
+                  out_dense=res.get("out_dense"), flags=CTOPK_FLAG_BOUND if bound else 0)
     _check(lib.ctopk_certify_ex(ctypes.byref(a), _stream(stream)))
     return res
 

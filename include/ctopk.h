@@ -109,7 +109,25 @@ typedef struct ctopk_args {
                                ||mu_tail - mu_head||_2 (fp64); NULL: skip          */
   float* out_dense;         /* optional [n_q_heads, d] untruncated softmax output
                                Attn (fp32); NULL: skip                              */
+  uint32_t flags;           /* CTOPK_FLAG_* bits; 0 for the exact certificate        */
 } ctopk_args;
+
+/*
+ * CTOPK_FLAG_BOUND -- certify with the blockwise deterministic bound instead
+ * of the exact minimal k (the Abstract's "blockwise variants" of the bounds
+ * that control TV from the ordered logits; its formula is not printed, this
+ * is the library's reading).  With the keys in consecutive blocks B of 64
+ * (maxima M_B, m the row maximum), the softmax mass of the keys scoring below
+ * t is at most U(t) = sum_{M_B < t} |B| e^{M_B - m} + sum_{M_B >= t} (|B| - 1)
+ * e^{t - m}; the call keeps every key scoring at or above the largest fp32 t
+ * with U(t) <= eps * Z.  Outputs then mean: k_eps = number of keys kept (at
+ * least the minimal k), tau = U(t) / Z (an upper bound on the truncation's
+ * TV, <= eps), out = the renormalised output over the kept keys, sel_mask =
+ * the kept keys.  Decode shapes with n <= 131072; the score scan also
+ * records each block's softmax mass, from which Z follows, and no key-by-key
+ * select runs.
+ */
+#define CTOPK_FLAG_BOUND 1u
 
 /*
  * ctopk_certify_ex -- full form of ctopk_certify: fp32 or bf16 inputs, per-head
@@ -136,12 +154,16 @@ CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
  *     w v directly); combine.  Taken for decode rows of 16385..32768 keys when
  *     at least half of the compute units (128) remain beside one workgroup per
  *     query row and the dense stream's chunks hold at most 2048 keys, and
- *     never for calls that ask for out_err or out_dense.
+ *     never for calls that ask for out_err or out_dense;
+ *   CTOPK_PLAN_DECODE_BOUND (calls with CTOPK_FLAG_BOUND): score scan with
+ *     per-block masses; the blockwise bound (one workgroup per row, in place
+ *     of the select); value stream over the kept keys; combine.
  */
 typedef enum {
   CTOPK_PLAN_ENCODER = 1,
   CTOPK_PLAN_DECODE = 2,
-  CTOPK_PLAN_DECODE_OVERLAP = 3
+  CTOPK_PLAN_DECODE_OVERLAP = 3,
+  CTOPK_PLAN_DECODE_BOUND = 4
 } ctopk_plan_id;
 
 /*
@@ -196,7 +218,7 @@ CTOPK_API int ctopk_validate(const ctopk_args* a);
  * level-0 histogram's (when the plan launches none, its pair is recorded back
  * to back on the stream and measures only the stream's own gap between the
  * two records, not a kernel), then one pair per remaining kernel (three in
- * either decode plan).  Logits
+ * every decode plan).  Logits
  * path: select, value stream, output combine.  Kernels past count/2 pairs run
  * without events; pairs left over are
  * dropped when the call returns.  count must be even and at most 16 (0

@@ -217,3 +217,13 @@ def test_plan_reports_validation_status(lib):
     assert ct.ctopk_plan(good_args(eps=1.5)) == cb.CTOPK_ERR_EPS
     assert ct.ctopk_plan(good_args(q=None)) == cb.CTOPK_ERR_NULL
     assert ct.ctopk_plan(good_args(n_kv_heads=5)) == cb.CTOPK_ERR_SHAPE
+
+
+def test_bound_flag_plan_and_limits(lib):
+    assert ct.ctopk_plan(good_args(flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
+    # the bound takes precedence over the encoder-shaped and overlapped plans
+    assert ct.ctopk_plan(good_args(n=512, d=64, n_q_heads=512, n_kv_heads=8,
+                                   flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
+    assert ct.ctopk_plan(good_args(n=131072, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
+    assert ct.ctopk_validate(good_args(n=131073, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_ERR_UNSUPPORTED
+    assert ct.ctopk_validate(good_args(flags=2)) == cb.CTOPK_ERR_UNSUPPORTED
