@@ -24,8 +24,8 @@ constexpr int kCandCap = 8192;
 // Most keys per chunk of the tail pass of the overlapped decode plan (its key
 // list lives in LDS).
 constexpr int kFixKeys = 2048;
-// Most score-scan tiles per row for the blockwise bound (sorted in LDS).
-constexpr int kBoundMaxTiles = 2048;
+// Most score-scan tiles per row for the blockwise bound (staged in LDS).
+constexpr int kBoundMaxTiles = 4096;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -123,7 +123,7 @@ typedef struct ctopk_args {
  * with U(t) <= eps * Z.  Outputs then mean: k_eps = number of keys kept (at
  * least the minimal k), tau = U(t) / Z (an upper bound on the truncation's
  * TV, <= eps), out = the renormalised output over the kept keys, sel_mask =
- * the kept keys.  Decode shapes with n <= 131072; the score scan also
+ * the kept keys.  Decode shapes with n <= 262144; the score scan also
  * records each block's softmax mass, from which Z follows, and no key-by-key
  * select runs.
  */

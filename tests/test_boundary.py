@@ -224,6 +224,6 @@ def test_bound_flag_plan_and_limits(lib):
     # the bound takes precedence over the encoder-shaped and overlapped plans
     assert ct.ctopk_plan(good_args(n=512, d=64, n_q_heads=512, n_kv_heads=8,
                                    flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
-    assert ct.ctopk_plan(good_args(n=131072, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
-    assert ct.ctopk_validate(good_args(n=131073, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_ERR_UNSUPPORTED
+    assert ct.ctopk_plan(good_args(n=262144, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
+    assert ct.ctopk_validate(good_args(n=262145, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_ERR_UNSUPPORTED
     assert ct.ctopk_validate(good_args(flags=2)) == cb.CTOPK_ERR_UNSUPPORTED

@@ -103,9 +103,13 @@ def test_bound_fp32(ct, d, G):
     check_bound(ct, wl, 0.05, f"fp32 d={d} G={G}")
 
 
-def test_bound_long_decode_largest(ct):
-    wl = workloads.long_decode(batch=1)  # n = 131072, the bound's largest row
-    check_bound(ct, wl, 0.01, "long_decode n=131072")
+def test_bound_long_decode(ct):
+    check_bound(ct, workloads.long_decode(batch=1), 0.01, "long_decode n=131072")
+
+
+def test_bound_largest_row(ct):
+    wl = workloads.long_decode(n=262144, batch=1, n_q=8, n_kv=2)  # the bound's largest row
+    check_bound(ct, wl, 0.01, "long_decode n=262144")
 
 
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 1000])
