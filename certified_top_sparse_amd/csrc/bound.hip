@@ -19,16 +19,20 @@
 // the truncation <= U(f) / Z <= eps, certified without selecting keys one by
 // one.  Z comes from the scan's per-tile masses: Z = sum_B e^{M_B - m} z_B.
 //
-// On the device f is found without sorting the maxima: U(t) needs one pass
-// over the tiles, so each of the 16 waves of the row's workgroup evaluates U
-// at its own candidate and a round narrows the interval of fp32 thresholds
-// (in the order-preserving key space) 17-fold; eight or nine rounds cover the
-// 2^32 keys.  Every candidate taken is one whose U was evaluated and found
-// within the budget, so the certificate never rests on U being monotone in
-// floating point; monotonicity only makes the answer the largest such f.
-// The workgroup is latency-bound (one per row), so reductions use DPP and
-// scalar lane reads instead of LDS round trips, the round's decision is two
-// ballots, and the count pass keeps 32 score loads per lane in flight.
+// On the device f is found without sorting the maxima.  Each round tests 64
+// candidate thresholds at once: every tile adds its mass |B| e^{M_B - m}
+// (fixed point, rounded up, so the sums are exact, order-free and never
+// below the real ones) and |B| - 1 to the bucket of the candidates its
+// maximum reaches, with LDS integer atomics; one wave's prefix scan over the
+// 64 buckets then gives U at every candidate.  Round 0 spreads the
+// candidates over [m + log(eps Z / n), m] (U(t) <= n e^{t - m}, so the lower
+// end is within the budget, and nothing above m is); later rounds subdivide
+// the interval between the largest candidate within the budget and the next
+// one over it, 65-fold, until no fp32 value lies between them or six rounds
+// are done.  Every threshold taken is one whose U was evaluated and found
+// within the budget, so the certificate does not rest on U being monotone in
+// floating point.  The count pass settles whole tiles from their (min, max)
+// and reads scores only for tiles that straddle f.
 #include <cfloat>
 
 #include "kernels.h"
@@ -39,15 +43,25 @@ namespace {
 constexpr int kBoundThreads = 1024;
 constexpr int kBoundWaves = kBoundThreads / kWave;
 constexpr int kTilesPerThread = kBoundMaxTiles / kBoundThreads;
-constexpr int kCountUnroll = 32;  // score loads in flight per lane in the count pass
+constexpr int kCand = kWave;      // candidates per round, one per lane of the deciding wave
+constexpr int kRounds = 6;
+constexpr int kStraddleUnroll = 8;  // straddling tiles per wave in flight in the count pass
+constexpr double kFix = 17592186044416.0;  // 2^44: sum over 2^18 keys of |B| e^{..} * 2^44 < 2^63
 static_assert(kBoundMaxTiles % kBoundThreads == 0, "whole tiles per thread");
 static_assert(kBoundWaves <= 16, "per-wave results fit one DPP row");
+static_assert(static_cast<int64_t>(kBoundMaxTiles) * kScanTile <= (1 << 18), "fixed-point range");
 
 struct BoundShared {
-  float2 Mx[kBoundMaxTiles];  // (M_B, |B| e^{M_B - m}) per tile
-  double wd[kBoundWaves];     // per-wave partial results
-  double U[kBoundWaves];      // U at each wave's candidate
-  int feas[kBoundWaves];      // 1: within the budget, 0: not, -1: no candidate
+  unsigned long long xb[2][kCand];  // per-bucket fixed-point mass (two sets, alternating rounds)
+  uint32_t cb[2][kCand];            // per-bucket sum of |B| - 1
+  float cand[kCand];                // this round's candidate thresholds, non-decreasing
+  double wd[kBoundWaves];           // per-wave partial results
+  uint32_t wi[kBoundWaves];
+  float lo, hi;                     // lo: within the budget; hi: smallest candidate over it
+  double Ulo;                       // U(lo), fixed-point masses
+  int active;                       // another round follows
+  int nlist;                        // straddling tiles listed for the count pass
+  int list[kBoundMaxTiles];
 };
 
 template <int CTRL>
@@ -65,6 +79,10 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFu), l));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), l));
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 // Sum over each row of 16 lanes, in every lane of the row: quad exchanges,
@@ -95,6 +113,45 @@ __device__ __forceinline__ uint32_t wave_sum_u32_dpp(uint32_t v) {
          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
 }
 
+// Inclusive prefix sums across the 64 lanes with DPP: shifts by 1, 2, 4 and 8
+// within each row of 16 (lanes shifted in from outside the row add 0), then
+// each row takes the running total of the rows before it (row broadcasts of
+// lanes 15 and 31).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64_dpp(unsigned long long v) {
+  v += dpp_u64<kDppRowShr1, 0xF>(v);
+  v += dpp_u64<kDppRowShr2, 0xF>(v);
+  v += dpp_u64<kDppRowShr4, 0xF>(v);
+  v += dpp_u64<kDppRowShr8, 0xF>(v);
+  v += dpp_u64<kDppRowBcast15, 0xA>(v);
+  v += dpp_u64<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32_dpp(uint32_t v) {
+  v += dpp_u32<kDppRowShr1, 0xF>(v);
+  v += dpp_u32<kDppRowShr2, 0xF>(v);
+  v += dpp_u32<kDppRowShr4, 0xF>(v);
+  v += dpp_u32<kDppRowShr8, 0xF>(v);
+  v += dpp_u32<kDppRowBcast15, 0xA>(v);
+  v += dpp_u32<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
 // Workgroup sum in a fixed order (each wave's sum, then the per-wave sums
 // across the lanes of one DPP row), the same value in every thread.
 __device__ double block_sum(double v, BoundShared& sh) {
@@ -116,6 +173,12 @@ __device__ float block_max(float v, BoundShared& sh) {
   return wave_max_dpp(lane < kBoundWaves ? static_cast<float>(sh.wd[lane]) : -INFINITY);
 }
 
+__device__ __forceinline__ float round_down_f32(double x) {
+  float f = static_cast<float>(x);
+  if (static_cast<double>(f) > x) f = nextafterf(f, -INFINITY);
+  return f;
+}
+
 __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
     const float* __restrict__ scores, int64_t n, const float2* __restrict__ blkstat,
     const float* __restrict__ blkz, int nblk, double eps, RowSel* __restrict__ rs,
@@ -128,129 +191,179 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
   const int wave = t / kWave;
   const float2* bs = blkstat + static_cast<size_t>(row) * nblk;
   const float* bz = blkz + static_cast<size_t>(row) * nblk;
+  const int nn = static_cast<int>(n);  // n <= kBoundMaxTiles * kScanTile
   // every tile holds kScanTile keys but the last
-  const int last_sz = static_cast<int>(n - static_cast<int64_t>(nblk - 1) * kScanTile);
+  const int last_sz = nn - (nblk - 1) * kScanTile;
+  const uint32_t ctot = static_cast<uint32_t>(nn - nblk);  // sum over tiles of |B| - 1
 
-  // Tiles: maxima and masses loaded together; the row maximum m, Z, and
-  // (M_B, |B| e^{M_B - m}) staged in LDS.
-  float Mv[kTilesPerThread], zv[kTilesPerThread];
+  // This thread's tiles t, t + 1024, ...: (min, max) and mass, loaded together.
+  float Nv[kTilesPerThread], Mv[kTilesPerThread], zv[kTilesPerThread];
 #pragma unroll
   for (int u = 0; u < kTilesPerThread; ++u) {
     const int b = t + u * kBoundThreads;
-    Mv[u] = b < nblk ? bs[b].y : -INFINITY;
+    const float2 mm = b < nblk ? bs[b] : make_float2(INFINITY, -INFINITY);
+    Nv[u] = mm.x;
+    Mv[u] = mm.y;
     zv[u] = b < nblk ? bz[b] : 0.0f;
   }
+  if (t < 2 * kCand) {
+    sh.xb[t / kCand][t % kCand] = 0ull;
+    sh.cb[t / kCand][t % kCand] = 0u;
+  }
+  if (t == 0) sh.nlist = 0;
   float mloc = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kTilesPerThread; ++u) mloc = fmaxf(mloc, Mv[u]);
   const float m = block_max(mloc, sh);
   double zloc = 0.0;
+  unsigned long long X[kTilesPerThread];  // ceil(|B| e^{M_B - m} 2^44)
+#pragma unroll
+  for (int u = 0; u < kTilesPerThread; ++u) {
+    const int b = t + u * kBoundThreads;
+    X[u] = 0ull;
+    if (b < nblk) {
+      const double e = exp(static_cast<double>(Mv[u]) - static_cast<double>(m));
+      zloc += e * static_cast<double>(zv[u]);
+      X[u] = static_cast<unsigned long long>(
+          ceil(static_cast<double>(b == nblk - 1 ? last_sz : kScanTile) * e * kFix));
+    }
+  }
+  const double Z = block_sum(zloc, sh);
+  const double budget = eps * Z;
+
+  // Round 0's candidates: t_L + j (m - t_L) / 63, the last one m itself.
+  const double tl = static_cast<double>(m) + log(budget / static_cast<double>(nn));
+  if (wave == 0) sh.cand[lane] = lane == kCand - 1 ? m : round_down_f32(tl + (static_cast<double>(m) - tl) * lane / (kCand - 1));
+  __syncthreads();
+
+  float lo = -FLT_MAX, hi = INFINITY;  // U(-FLT_MAX) = 0: no key scores below it
+  double Ulo = 0.0;
+  for (int round = 0; round < kRounds; ++round) {
+    const int set = round & 1;
+    // Bucket of each tile: the number of candidates at or below its maximum
+    // (an arithmetic guess, corrected against the candidates themselves).
+    const float a0 = round == 0 ? static_cast<float>(tl) : lo;
+    const float inv_w = round == 0 ? static_cast<float>((kCand - 1) / (static_cast<double>(m) - tl))
+                                   : static_cast<float>((kCand + 1) / (static_cast<double>(hi) - static_cast<double>(lo)));
+    const float off = round == 0 ? 1.0f : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kTilesPerThread; ++u) {
+      const int b = t + u * kBoundThreads;
+      if (b < nblk) {
+        const float M = Mv[u];
+        const float g = (M - a0) * inv_w + off;  // a guess only: any value is corrected below
+        int j = g > 0.0f ? (g < static_cast<float>(kCand) ? static_cast<int>(g) : kCand) : 0;
+        while (j < kCand && sh.cand[j] <= M) ++j;
+        while (j > 0 && sh.cand[j - 1] > M) --j;
+        if (j < kCand) {  // below every candidate from j on
+          atomicAdd(&sh.xb[set][j], X[u]);
+          atomicAdd(&sh.cb[set][j], static_cast<uint32_t>((b == nblk - 1 ? last_sz : kScanTile) - 1));
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // U at every candidate from the bucket prefix sums; the decision.
+      const float cj = sh.cand[lane];
+      const unsigned long long xs = wave_incl_scan_u64_dpp(sh.xb[set][lane]);
+      const uint32_t cs = wave_incl_scan_u32_dpp(sh.cb[set][lane]);
+      sh.xb[set][lane] = 0ull;  // this set serves again two rounds on
+      sh.cb[set][lane] = 0u;
+      const bool valid = round == 0 || (cj > lo && cj < hi);
+      const double U = static_cast<double>(xs) * (1.0 / kFix) +
+                       static_cast<double>(ctot - cs) * exp(static_cast<double>(cj) - static_cast<double>(m));
+      const bool ok = valid && U <= budget;
+      const uint64_t okm = __ballot(ok);
+      const uint64_t overm = __ballot(valid && !ok);
+      float nlo = lo, nhi = hi;
+      double nU = Ulo;
+      const int best = okm ? 63 - __clzll(okm) : -1;
+      if (best >= 0) {
+        nlo = readlane_f32(cj, best);
+        nU = readlane_f64(U, best);
+      }
+      const uint64_t above = best < 0 ? overm : (best == 63 ? 0ull : overm & (~0ull << (best + 1)));
+      if (above) nhi = readlane_f32(cj, __ffsll(static_cast<unsigned long long>(above)) - 1);
+      // Next round's candidates: lo + (j + 1) (hi - lo) / 65.
+      const bool bounded = nhi < INFINITY;
+      const double step = (static_cast<double>(nhi) - static_cast<double>(nlo)) * (1.0 / (kCand + 1));
+      const float nc = bounded ? round_down_f32(static_cast<double>(nlo) + step * (lane + 1)) : nlo;
+      const bool more = __ballot(bounded && nc > nlo && nc < nhi) != 0ull;
+      sh.cand[lane] = nc;
+      if (lane == 0) {
+        sh.lo = nlo;
+        sh.hi = nhi;
+        sh.Ulo = nU;
+        sh.active = more ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    lo = sh.lo;
+    hi = sh.hi;
+    Ulo = sh.Ulo;
+    if (!sh.active) break;  // uniform: every thread read the same flag
+  }
+  const uint32_t kf = ukey(lo);  // f = lo; a key is kept iff ukey(s) >= kf
+
+  // Count and mask: whole tiles from their (min, max); the tiles that
+  // straddle f (and a short last tile) listed for a read of their scores.
+  const int nwords = (nn + 31) / 32;
+  uint32_t* mrow = sel_mask ? sel_mask + static_cast<size_t>(row) * static_cast<size_t>(nwords) : nullptr;
+  uint32_t cnt = 0u;
 #pragma unroll
   for (int u = 0; u < kTilesPerThread; ++u) {
     const int b = t + u * kBoundThreads;
     if (b < nblk) {
-      const double e = exp(static_cast<double>(Mv[u]) - static_cast<double>(m));
-      zloc += e * static_cast<double>(zv[u]);
-      sh.Mx[b] = make_float2(Mv[u], static_cast<float>(static_cast<double>(b == nblk - 1 ? last_sz : kScanTile) * e));
+      const bool whole = b < nblk - 1 || last_sz == kScanTile;
+      if (whole && ukey(Nv[u]) >= kf) {
+        cnt += kScanTile;
+        if (mrow != nullptr) {
+          mrow[2 * b] = ~0u;
+          mrow[2 * b + 1] = ~0u;
+        }
+      } else if (whole && ukey(Mv[u]) < kf) {
+        if (mrow != nullptr) {
+          mrow[2 * b] = 0u;
+          mrow[2 * b + 1] = 0u;
+        }
+      } else {
+        sh.list[atomicAdd(&sh.nlist, 1)] = b;
+      }
     }
   }
-  const double Z = block_sum(zloc, sh);  // its barriers also publish sh.Mx
-  const double budget = eps * Z;
-
-  // Search over fp32 thresholds in key space.  klo is always a threshold
-  // within the budget (U(-FLT_MAX) = 0: no key scores below it), and the
-  // answer is at most ukey(m) (above m, U is at least Z).
-  uint32_t klo = ukey(-FLT_MAX), khi = ukey(m);
-  double Ulo = 0.0;
-  for (int round = 0; round < 16 && khi != klo; ++round) {
-    const uint32_t span = khi - klo;
-    const bool fine = span <= static_cast<uint32_t>(kBoundWaves);
-    auto cand = [&](int w) -> uint32_t {  // candidate w, strictly above klo, at most khi
-      return fine ? klo + static_cast<uint32_t>(w) + 1u
-                  : klo + static_cast<uint32_t>((static_cast<uint64_t>(span) * (w + 1)) /
-                                                (kBoundWaves + 1));
-    };
-    const uint32_t cw = cand(wave);
-    if (cw <= khi) {
-      const float tc = ukey_to_float(cw);
-      double a = 0.0;   // sum of |B| e^{M_B - m} over tiles wholly below tc
-      uint32_t c = 0u;  // sum of |B| - 1 over the others
-      for (int b0 = 0; b0 < nblk; b0 += 4 * kWave) {
-        float2 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int b = b0 + u * kWave + lane;
-          v[u] = b < nblk ? sh.Mx[b] : make_float2(-INFINITY, 0.0f);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int b = b0 + u * kWave + lane;
-          const bool below = v[u].x < tc;
-          a += below ? static_cast<double>(v[u].y) : 0.0;
-          c += (below || b >= nblk) ? 0u : static_cast<uint32_t>((b == nblk - 1 ? last_sz : kScanTile) - 1);
-        }
-      }
-      a = wave_sum_f64(a);
-      c = wave_sum_u32_dpp(c);
-      const double U = a + static_cast<double>(c) * exp(static_cast<double>(tc) - static_cast<double>(m));
-      if (lane == 0) {
-        sh.U[wave] = U;
-        sh.feas[wave] = U <= budget ? 1 : 0;
-      }
-    } else if (lane == 0) {
-      sh.feas[wave] = -1;
-    }
-    __syncthreads();
-    // Every thread takes the same decision from the same LDS values: the
-    // largest candidate within the budget becomes klo, the first one above
-    // it that is not bounds khi.
-    const int fl = lane < kBoundWaves ? sh.feas[lane] : -1;
-    const uint64_t ok = __ballot(fl == 1);
-    const uint64_t over = __ballot(fl == 0);
-    const int best = ok ? 63 - __clzll(ok) : -1;
-    if (best >= 0) {
-      Ulo = sh.U[best];
-    }
-    const uint64_t above = best >= 0 ? (best >= 63 ? 0ull : (over >> (best + 1)) << (best + 1)) : over;
-    const uint32_t nhi = above ? cand(__ffsll(static_cast<unsigned long long>(above)) - 1) - 1u : khi;
-    if (best >= 0) klo = cand(best);
-    khi = nhi;
-    __syncthreads();  // sh.feas and sh.U are rewritten next round
-  }
-  const uint32_t kf = klo;  // the key of f
-
-  // Keep every key whose key order is at or above f's (the value stream's
-  // test): count them and write the mask, kCountUnroll loads per lane in
-  // flight; wave w takes 64-key groups w, w + 16, ...
-  // n <= kBoundMaxTiles * kScanTile, so key and word indices fit in int.
+  __syncthreads();
   const float* sr = scores + static_cast<size_t>(row) * static_cast<size_t>(n);
-  const int nn = static_cast<int>(n);
-  const int nwords = (nn + 31) / 32;
-  uint32_t* mrow = sel_mask ? sel_mask + static_cast<size_t>(row) * static_cast<size_t>(nwords) : nullptr;
-  const int ngroups = (nn + kWave - 1) / kWave;
-  uint32_t cnt = 0u;
-  for (int g0 = wave; g0 < ngroups; g0 += kBoundWaves * kCountUnroll) {
-    float v[kCountUnroll];
+  const int nl = sh.nlist;
+  uint32_t scnt = 0u;  // kept keys of this wave's straddling tiles (wave-uniform)
+  for (int e0 = wave; e0 < nl; e0 += kBoundWaves * kStraddleUnroll) {
+    int bl[kStraddleUnroll];
+    float v[kStraddleUnroll];
 #pragma unroll
-    for (int u = 0; u < kCountUnroll; ++u) v[u] = sr[min((g0 + u * kBoundWaves) * kWave + lane, nn - 1)];
+    for (int u = 0; u < kStraddleUnroll; ++u) {
+      const int e = e0 + u * kBoundWaves;
+      bl[u] = e < nl ? sh.list[e] : -1;
+      v[u] = sr[min(max(bl[u], 0) * kScanTile + lane, nn - 1)];
+    }
 #pragma unroll
-    for (int u = 0; u < kCountUnroll; ++u) {
-      const int g = g0 + u * kBoundWaves;
-      const bool kept = g * kWave + lane < nn && ukey(v[u]) >= kf;
-      const uint64_t bits = __ballot(kept);
-      cnt += static_cast<uint32_t>(__popcll(bits));
-      if (mrow != nullptr && g < ngroups) {
-        if (lane == 0) mrow[2 * g] = static_cast<uint32_t>(bits);
-        if (lane == 1 && 2 * g + 1 < nwords) mrow[2 * g + 1] = static_cast<uint32_t>(bits >> 32);
+    for (int u = 0; u < kStraddleUnroll; ++u) {
+      if (bl[u] >= 0) {  // wave-uniform
+        const int i = bl[u] * kScanTile + lane;
+        const uint64_t bits = __ballot(i < nn && ukey(v[u]) >= kf);
+        scnt += static_cast<uint32_t>(__popcll(bits));
+        if (mrow != nullptr) {
+          if (lane == 0) mrow[2 * bl[u]] = static_cast<uint32_t>(bits);
+          if (lane == 1 && 2 * bl[u] + 1 < nwords) mrow[2 * bl[u] + 1] = static_cast<uint32_t>(bits >> 32);
+        }
       }
     }
   }
-  if (lane == 0) sh.feas[wave] = static_cast<int>(cnt);  // the search's last barrier preceded this
+  const uint32_t wsum = wave_sum_u32_dpp(cnt + (lane == 0 ? scnt : 0u));
+  if (lane == 0) sh.wi[wave] = wsum;
   __syncthreads();
 
   if (t == 0) {
     int64_t k = 0;
-    for (int w = 0; w < kBoundWaves; ++w) k += sh.feas[w];
+    for (int w2 = 0; w2 < kBoundWaves; ++w2) k += sh.wi[w2];
     rs[row].m = m;
     rs[row].lo = m;
     rs[row].Z = Z;
@@ -266,7 +379,8 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
 hipError_t launch_bound(const float* scores, int64_t n, int rows, const float2* blkstat,
                         const float* blkz, int nblk, double eps, RowSel* rs, int32_t* k_eps,
                         double* tau, double* lse, uint32_t* sel_mask, hipStream_t st) {
-  if (nblk < 1 || nblk > kBoundMaxTiles) return hipErrorInvalidValue;
+  if (nblk < 1 || nblk > kBoundMaxTiles || n > static_cast<int64_t>(kBoundMaxTiles) * kScanTile)
+    return hipErrorInvalidValue;
   return launch(bound_kernel, dim3(rows), dim3(kBoundThreads), 0, st, scores, n, blkstat, blkz,
                 nblk, eps, rs, k_eps, tau, lse, sel_mask);
 }
