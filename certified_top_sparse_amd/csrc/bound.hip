@@ -59,6 +59,8 @@ struct BoundShared {
   uint32_t wi[kBoundWaves];
   float lo, hi;                     // lo: within the budget; hi: smallest candidate over it
   double Ulo;                       // U(lo), fixed-point masses
+  unsigned long long Alo;           // fixed-point mass of the tiles wholly below lo
+  uint32_t Clo;                     // and their sum of |B| - 1
   int active;                       // another round follows
   int nlist;                        // straddling tiles listed for the count pass
   int list[kBoundMaxTiles];
@@ -238,6 +240,11 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
 
   float lo = -FLT_MAX, hi = INFINITY;  // U(-FLT_MAX) = 0: no key scores below it
   double Ulo = 0.0;
+  // Tiles with M_B < lo lie below every later candidate and tiles with M_B
+  // >= hi below none, so only tiles with lo <= M_B < hi are bucketed; the
+  // former enter through (Alo, Clo), carried from round to round.
+  unsigned long long Alo = 0ull;
+  uint32_t Clo = 0u;
   for (int round = 0; round < kRounds; ++round) {
     const int set = round & 1;
     // Bucket of each tile: the number of candidates at or below its maximum
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
 #pragma unroll
     for (int u = 0; u < kTilesPerThread; ++u) {
       const int b = t + u * kBoundThreads;
-      if (b < nblk) {
+      if (b < nblk && Mv[u] >= lo && Mv[u] < hi) {
         const float M = Mv[u];
         const float g = (M - a0) * inv_w + off;  // a guess only: any value is corrected below
         int j = g > 0.0f ? (g < static_cast<float>(kCand) ? static_cast<int>(g) : kCand) : 0;
@@ -265,8 +272,8 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
     if (wave == 0) {
       // U at every candidate from the bucket prefix sums; the decision.
       const float cj = sh.cand[lane];
-      const unsigned long long xs = wave_incl_scan_u64_dpp(sh.xb[set][lane]);
-      const uint32_t cs = wave_incl_scan_u32_dpp(sh.cb[set][lane]);
+      const unsigned long long xs = Alo + wave_incl_scan_u64_dpp(sh.xb[set][lane]);
+      const uint32_t cs = Clo + wave_incl_scan_u32_dpp(sh.cb[set][lane]);
       sh.xb[set][lane] = 0ull;  // this set serves again two rounds on
       sh.cb[set][lane] = 0u;
       const bool valid = round == 0 || (cj > lo && cj < hi);
@@ -277,10 +284,15 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
       const uint64_t overm = __ballot(valid && !ok);
       float nlo = lo, nhi = hi;
       double nU = Ulo;
+      unsigned long long nA = Alo;
+      uint32_t nC = Clo;
       const int best = okm ? 63 - __clzll(okm) : -1;
       if (best >= 0) {
         nlo = readlane_f32(cj, best);
         nU = readlane_f64(U, best);
+        nA = static_cast<unsigned long long>(__builtin_amdgcn_readlane(static_cast<int>(xs & 0xFFFFFFFFu), best)) & 0xFFFFFFFFull;
+        nA |= static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(xs >> 32), best))) << 32;
+        nC = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(cs), best));
       }
       const uint64_t above = best < 0 ? overm : (best == 63 ? 0ull : overm & (~0ull << (best + 1)));
       if (above) nhi = readlane_f32(cj, __ffsll(static_cast<unsigned long long>(above)) - 1);
@@ -294,6 +306,8 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
         sh.lo = nlo;
         sh.hi = nhi;
         sh.Ulo = nU;
+        sh.Alo = nA;
+        sh.Clo = nC;
         sh.active = more ? 1 : 0;
       }
     }
@@ -301,6 +315,8 @@ __global__ __launch_bounds__(kBoundThreads) void bound_kernel(
     lo = sh.lo;
     hi = sh.hi;
     Ulo = sh.Ulo;
+    Alo = sh.Alo;
+    Clo = sh.Clo;
     if (!sh.active) break;  // uniform: every thread read the same flag
   }
   const uint32_t kf = ukey(lo);  // f = lo; a key is kept iff ukey(s) >= kf
