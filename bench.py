@@ -62,6 +62,7 @@ KERNEL_SOURCES = {
     "resolve": ("select.hip", "vsum_body.h") + _COMMON,
     "tail": ("vsum.hip", "vsum_body.h") + _COMMON,
     "vsum": ("vsum.hip", "vsum_body.h") + _COMMON,
+    "bound": ("bound.hip",) + _COMMON,
 }
 
 
@@ -277,7 +278,8 @@ def bound_leg(lib, ct, torch, hip, Q, Kd, Vd, steps, eps):
             hip.destroy(e)
     return {"eps": eps, "steps": steps, "us_per_call": round(us, 3),
             "query_heads_per_s": round(n_q / (us * 1e-6), 1), "kernel_us": kern,
-            "mean_k_over_n": round(float(np.mean(kmean)) / n, 4), "max_tau": taumax}
+            "mean_k_over_n": round(float(np.mean(kmean)) / n, 4), "max_tau": taumax,
+            "bound_kernel_traffic_bytes": read_traffic("bound")}
 
 
 def encoder_leg(lib, ct, torch, hip, steps, eps, sets=16):
