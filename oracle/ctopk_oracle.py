@@ -40,14 +40,34 @@ Readings where the page leaves a step open:
   e^{t - m}); the certified truncation keeps H_t = {i : s_i >= t} for the
   largest t with U(t) <= eps * Z, so TV(P, P_hat_{H_t}) <= U(t) / Z <= eps.
 
+4-bit key copy and score bounds.  A second page ("Certified Sparse
+Attention via Perturbed Retrieval", arXiv 2610.24991: its Abstract, and the
+"Limitations and Discussion" figure quoted on the paperfoot.com page) names a
+4-bit key scan with deterministic score bounds, shared across a GQA group,
+that generates candidates exactly while reading every key, and prints no
+formula.  Readings taken:
+
+* each key k_i (a row of d values) gets a scale a_i = amax_i / 7 and codes
+  c_ij = clamp(rint(k_ij / a_i), -7, 7), computed in float32 as written (the
+  codes are integers, so a copy made elsewhere must match them exactly);
+  a_i = 0 and all codes 0 when the row is zero;
+* the residual e_i = k_i - a_i c_i is summarised by its Euclidean norm rho_i;
+* the score s_i = scale (q . k_i) then lies in
+  [shat_i - R_i, shat_i + R_i] with shat_i = scale a_i (q . c_i) and
+  R_i = scale ||q||_2 rho_i (Cauchy-Schwarz on q . e_i);
+* the candidates for a threshold T are exactly {i : s_i >= T}: keys whose
+  interval lies at or above T are in, keys whose interval lies below T are
+  out, and only the keys whose interval straddles T need their full score.
+
 Everything is computed in float64.  bf16 and fp32 inputs convert to float64
 exactly.  The score scale is applied as the float64 value of the float32 the
 device receives.
 
 Parity status: every function here is pinned by the tests in
 ``tests/test_oracle_pins.py`` (identities, brute force, closed forms, the
-Gaussian design rule, and the blockwise bound's validity, monotonicity and
-optimality).  The pages print no worked example, so no specific
+Gaussian design rule, the blockwise bound's validity, monotonicity and
+optimality, and the 4-bit copy's reconstruction error, interval containment
+on every key, and the exact cases where the residual vanishes).  The pages print no worked example, so no specific
 (q, K, V) -> (k_eps, tau, out) triple is pinned by a printed value.
 """
 from __future__ import annotations
@@ -399,3 +419,63 @@ def certify_bound(S, V, eps: float, row_to_v=None, block: int = BOUND_BLOCK):
         out[r] = (w[h] @ V[row_to_v[r]][h]) / w[h].sum()
     return {"t": ts, "k": ks, "tau_bound": tb, "tv": tv, "out": out, "head_mask": head}
 
+
+
+# ---------------------------------------------------------------------------
+# 4-bit key copy with deterministic score bounds ("Certified Sparse Attention
+# via Perturbed Retrieval", arXiv 2610.24991, Abstract: a 4-bit scan with
+# deterministic bounds shared across a GQA group generates the candidates
+# exactly but reads every key)
+# ---------------------------------------------------------------------------
+K4_LEVEL = 7  # codes in [-7, 7]
+
+
+def quantize_k4(K):
+    """Per-key symmetric 4-bit copy of K [..., n, d] (float or bf16 bits).
+
+    Returns (codes int8 [..., n, d], a float32 [..., n], rho float64 [..., n]):
+    a = float32(amax) / float32(7) and codes = clamp(rint(float32(k) / a), -7, 7)
+    in float32 arithmetic (a zero row gets a = 0 and codes 0); rho is the
+    exact Euclidean norm of k - a * codes."""
+    Kf = as_f64(K).astype(np.float32)  # bf16 and fp32 values are exact in fp32
+    amax = np.max(np.abs(Kf), axis=-1)
+    a = (amax / np.float32(K4_LEVEL)).astype(np.float32)
+    safe = np.where(a > 0, a, np.float32(1.0)).astype(np.float32)
+    c = np.rint((Kf / safe[..., None]).astype(np.float32))
+    c = np.clip(c, -K4_LEVEL, K4_LEVEL)
+    c = np.where(a[..., None] > 0, c, 0).astype(np.int8)
+    resid = Kf.astype(np.float64) - a.astype(np.float64)[..., None] * c.astype(np.float64)
+    rho = np.sqrt(np.sum(resid * resid, axis=-1))
+    return c, a, rho
+
+
+def pack_k4(codes):
+    """Two's-complement nibbles, element 2j in the low half of byte j."""
+    c = np.asarray(codes, dtype=np.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_k4(packed, d: int):
+    """Inverse of pack_k4."""
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int16)
+    lo, hi = p & 0xF, (p >> 4) & 0xF
+    out = np.empty(p.shape[:-1] + (d,), dtype=np.int16)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    return np.where(out >= 8, out - 16, out).astype(np.int8)
+
+
+def k4_score_bounds(q, codes, a, rho, scale):
+    """Score intervals of one query row q [d] against every key of a 4-bit
+    copy: shat = scale * a * (q . codes) and R = scale * ||q||_2 * rho, so
+    the exact score scale * (q . k) lies in [shat - R, shat + R]."""
+    q = as_f64(q)
+    sc = float(scale)
+    shat = sc * np.asarray(a, dtype=np.float64) * (codes.astype(np.float64) @ q)
+    R = abs(sc) * float(np.linalg.norm(q)) * np.asarray(rho, dtype=np.float64)
+    return shat, R
+
+
+def candidates(q, K, scale, T):
+    """The candidate set the scan generates: {i : scale * (q . k_i) >= T}."""
+    s = float(scale) * (as_f64(K) @ as_f64(q))
+    return s >= T

@@ -383,3 +383,83 @@ def test_bound_with_unit_blocks_is_the_minimal_topk(eps):
     e = oracle.certify_scores(S, V, eps)
     assert np.array_equal(b["k"], e["k_eps"])
     assert np.array_equal(b["head_mask"], e["head_mask"])
+
+
+# ---------------------------------------------------------------------------
+# 4-bit key copy and score bounds ("Certified Sparse Attention via Perturbed
+# Retrieval", arXiv 2610.24991, Abstract)
+# ---------------------------------------------------------------------------
+def _bf16_keys(seed, n, d, spread=1.0):
+    rng = np.random.default_rng(seed)
+    return workloads.bf16_rne(rng.standard_normal((n, d), dtype=np.float32) * np.float32(spread))
+
+
+def test_k4_reconstruction_error_and_range():
+    K = _bf16_keys(40, 2000, 128, 3.0)
+    c, a, rho = oracle.quantize_k4(K)
+    Kf = oracle.as_f64(K)
+    assert c.min() >= -7 and c.max() <= 7
+    err = np.abs(Kf - a.astype(np.float64)[:, None] * c)
+    assert np.all(err <= a.astype(np.float64)[:, None] * 0.5 * (1 + 1e-6))  # nearest code
+    # the largest element of each row maps to the end code
+    top = np.argmax(np.abs(Kf), axis=1)
+    assert np.all(np.abs(c[np.arange(len(top)), top]) == 7)
+    # rho is the residual norm, which the elementwise error bounds
+    assert np.all(rho <= np.sqrt(128) * a * 0.5 * (1 + 1e-6))
+    assert np.allclose(rho, np.linalg.norm(Kf - a.astype(np.float64)[:, None] * c, axis=1), rtol=1e-12)
+
+
+def test_k4_pack_layout_and_roundtrip():
+    # element 2j in the low nibble of byte j, two's complement
+    assert list(oracle.pack_k4(np.array([1, -1, 7, -7], dtype=np.int8))) == [0xF1, 0x97]
+    rng = np.random.default_rng(41)
+    c = rng.integers(-8, 8, size=(3, 50, 64)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_k4(oracle.pack_k4(c), 64), c)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_k4_bounds_contain_every_exact_score(d):
+    rng = np.random.default_rng(42 + d)
+    K = _bf16_keys(43 + d, 3000, d, 2.0)
+    c, a, rho = oracle.quantize_k4(K)
+    for r in range(5):
+        q = workloads.bf16_rne(rng.standard_normal(d, dtype=np.float32))
+        scale = np.float32(rng.uniform(0.05, 0.5))
+        s = float(scale) * (oracle.as_f64(K) @ oracle.as_f64(q))
+        shat, R = oracle.k4_score_bounds(q, c, a, rho, scale)
+        assert np.all(np.abs(s - shat) <= R * (1 + 1e-12) + 1e-12)
+        # classification against a threshold agrees with the exact candidate set
+        T = float(np.quantile(s, 0.9))
+        cand = oracle.candidates(q, K, scale, T)
+        assert np.all(cand[shat - R >= T]) and not np.any(cand[shat + R < T])
+
+
+def test_k4_exact_when_the_residual_vanishes():
+    # keys that are integer multiples of a power of two with largest entry 7 units
+    rng = np.random.default_rng(44)
+    c0 = rng.integers(-7, 8, size=(200, 64)).astype(np.float32)
+    c0[:, 0] = 7.0
+    K = (c0 * np.float32(0.125)).astype(np.float32)
+    c, a, rho = oracle.quantize_k4(K)
+    assert np.all(a == np.float32(0.125)) and np.array_equal(c, c0.astype(np.int8))
+    assert np.all(rho == 0.0)
+    q = rng.standard_normal(64)
+    shat, R = oracle.k4_score_bounds(q, c, a, rho, 0.3)
+    assert np.all(R == 0.0)
+    assert np.allclose(shat, 0.3 * (K.astype(np.float64) @ q), rtol=0, atol=1e-12)
+    # a zero row: scale 0, codes 0, no residual
+    c, a, rho = oracle.quantize_k4(np.zeros((1, 64), dtype=np.float32))
+    assert a[0] == 0 and not c.any() and rho[0] == 0
+
+
+def test_k4_bound_is_attained_for_a_query_along_the_residual():
+    # Cauchy-Schwarz is tight when q is parallel to the residual: |s - shat| = R
+    K = _bf16_keys(45, 10, 128)
+    c, a, rho = oracle.quantize_k4(K)
+    Kf = oracle.as_f64(K)
+    for i in range(10):
+        e = Kf[i] - float(a[i]) * c[i]
+        q = 3.0 * e / np.linalg.norm(e)
+        s = 0.2 * (Kf[i] @ q)
+        shat, R = oracle.k4_score_bounds(q, c[i:i + 1], a[i:i + 1], rho[i:i + 1], 0.2)
+        assert s - shat[0] == pytest.approx(R[0], rel=1e-12)
