@@ -282,6 +282,86 @@ def bound_leg(lib, ct, torch, hip, Q, Kd, Vd, steps, eps):
             "bound_kernel_traffic_bytes": read_traffic("bound")}
 
 
+def k4_leg(lib, ct, torch, hip, Q, Kd, T_cut, T_top, steps):
+    """The 4-bit key copy on the decode inputs: exact candidate generation
+    (ctopk_candidates_k4) at two thresholds per head -- the certified cut
+    score (candidates = the exact head) and the 64th largest score (a
+    retrieval-sized set) -- with per-kernel times, keys rescored at full
+    width, and the scan's bytes against the full-width score scan's."""
+    sets = len(Q)
+    n_q, d = Q[0].shape
+    n_kv, n, _ = Kd[0].shape
+    copies = [ct.ctopk_quantize_k4(K) for K in Kd]
+    torch.cuda.synchronize()
+    ev0, ev1 = hip.event(), hip.event()
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev0), sptr)
+    for r in range(sets):
+        ct.ctopk_quantize_k4(Kd[r])
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev1), sptr)
+    torch.cuda.synchronize()
+    quant_us = hip.elapsed_ms(ev0, ev1) * 1e3 / sets
+    mask = torch.empty((n_q, (n + 31) // 32), dtype=torch.int32, device="cuda")
+    count = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    resc = torch.empty(n_kv, dtype=torch.int32, device="cuda")
+    names = ("k4_scan", "k4_rescore", "k4_count")
+    out = {"quantize_us_per_call": round(quant_us, 3),
+           "scan_bytes_per_call": n_kv * n * (d // 2 + 8),
+           "full_width_scan_bytes": n_kv * n * d * 2}
+    for label, Ts in (("cut_score", T_cut), ("top64", T_top)):
+        thr = [torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).cuda() for t in Ts]
+        args = [ct.make_k4_args(Q[r], Kd[r], *copies[r], thr[r], sel_mask=mask, count=count,
+                                rescored=resc) for r in range(sets)]
+        call = lib.ctopk_candidates_k4
+
+        def step(i):
+            rc = call(ctypes.byref(args[i % sets]), sptr)
+            if rc != 0:
+                raise RuntimeError(ct.ctopk_last_error_string())
+
+        fr, cnt = [], []
+        for r in range(sets):
+            step(r)
+            torch.cuda.synchronize()
+            fr.append(float(resc.double().sum().item()) / (n_kv * n))
+            cnt.append(float(count.double().mean().item()))
+        for i in range(20):
+            step(i)
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.lib.hipEventRecord(ctypes.c_void_p(e0), sptr)
+        for i in range(steps):
+            step(i)
+        hip.lib.hipEventRecord(ctypes.c_void_p(e1), sptr)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+        hip.destroy(e0)
+        hip.destroy(e1)
+        n_ev = 2 * len(names)
+        evs = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+        arrs = [(ctypes.c_void_p * n_ev)(*[ctypes.c_void_p(e) for e in row]) for row in evs]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            lib.ctopk_record_kernel_events(arrs[i], n_ev)
+            step(i)
+        torch.cuda.synchronize()
+        per = np.array([[hip.elapsed_ms(row[2 * j], row[2 * j + 1]) for j in range(len(names))]
+                        for row in evs])
+        for row in evs:
+            for e in row:
+                hip.destroy(e)
+        kern = {nm: round(float(per[:, j].mean()) * 1e3, 3) for j, nm in enumerate(names)}
+        scan_gbps = out["scan_bytes_per_call"] / (kern["k4_scan"] * 1e-6) / 1e9
+        out[label] = {"us_per_call": round(us, 3), "kernel_us": kern,
+                      "mean_candidates": round(float(np.mean(cnt)), 1),
+                      "rescored_fraction": round(float(np.mean(fr)), 4),
+                      "k4_scan_gbps": round(scan_gbps, 1),
+                      "bytes_per_call": round(out["scan_bytes_per_call"] + float(np.mean(fr)) * n_kv * n * d * 2)}
+    hip.destroy(ev0)
+    hip.destroy(ev1)
+    return out
+
+
 def encoder_leg(lib, ct, torch, hip, steps, eps, sets=16):
     """All-queries (encoder-shaped) workload: batch 8, 12 heads, 512 queries and
     512 keys per head, d = 64, bf16, per-head temperature; every query row of a
@@ -366,6 +446,8 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--bound-steps", type=int, default=1000,
                     help="calls of the blockwise-bound leg on the decode workload; 0 skips it")
+    ap.add_argument("--k4-steps", type=int, default=500,
+                    help="calls per threshold of the 4-bit candidate leg; 0 skips it")
     ap.add_argument("--encoder-steps", type=int, default=500,
                     help="calls of the all-queries (encoder-shaped) leg; 0 skips it")
     args = ap.parse_args()
@@ -411,11 +493,15 @@ def main():
     union_rows = []
     tail_rows = []
     kmean = []
+    T_cut, T_top = [], []
     for r in range(args.sets):
-        res = ct.ctopk_certify_ex(Q[r], Kd[r], Vd[r], args.eps, want_mask=True)
+        res = ct.ctopk_certify_ex(Q[r], Kd[r], Vd[r], args.eps, want_mask=True, want_scores=True)
         torch.cuda.synchronize()
         words = res["sel_mask"].cpu().numpy().astype(np.int32).view(np.uint8)
         bits = np.unpackbits(words.reshape(n_q, -1), axis=1, bitorder="little")[:, :n].astype(bool)
+        sc = res["scores"].cpu().numpy()
+        T_cut.append(np.array([sc[h][bits[h]].min() for h in range(n_q)], dtype=np.float32))
+        T_top.append(np.sort(sc, axis=1)[:, -64].astype(np.float32))
         union_rows.append(int(bits.reshape(n_kv, G, n).any(axis=1).sum()))
         kr = res["k_eps"].cpu().numpy()
         tail_rows.append(tail_pass_rows(bits, kr, n_kv, G, n))
@@ -514,6 +600,10 @@ def main():
     if args.bound_steps > 0:
         bound = bound_leg(lib, ct, torch, hip, Q, Kd, Vd, args.bound_steps, eps)
 
+    k4 = None
+    if args.k4_steps > 0:
+        k4 = k4_leg(lib, ct, torch, hip, Q, Kd, T_cut, T_top, args.k4_steps)
+
     encoder = None
     if args.encoder_steps > 0:
         encoder = encoder_leg(lib, ct, torch, hip, args.encoder_steps, eps)
@@ -549,6 +639,7 @@ def main():
         "kernel_us": kernel_us,
         "ms_per_step_with_kernel_events": None if ms_events is None else round(ms_events, 5),
         "bound_certificate": bound,
+        "k4_candidates": k4,
         "encoder": encoder,
     }
     print(json.dumps(line), flush=True)

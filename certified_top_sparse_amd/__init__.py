@@ -8,10 +8,10 @@ whose functions carry the C names.
 from .ctopk import (  # noqa: F401
     CTOPK_BF16, CTOPK_F32, CTOPK_FLAG_BOUND, CTOPK_PLAN_DECODE, CTOPK_PLAN_DECODE_BOUND,
     CTOPK_PLAN_DECODE_OVERLAP, CTOPK_PLAN_ENCODER,
-    CtopkArgs, CtopkError, EXPORTED, LIB_PATH, ctopk_certify,
+    CtopkArgs, CtopkError, CtopkK4Args, EXPORTED, LIB_PATH, ctopk_candidates_k4, ctopk_certify,
     ctopk_certify_ex, ctopk_certify_logits, ctopk_last_error_string,
     ctopk_logits_workspace_bytes, ctopk_plan, ctopk_record_kernel_events, ctopk_validate,
-    ctopk_version,
-    ctopk_workspace_bytes,
+    ctopk_k4_workspace_bytes, ctopk_quantize_k4, ctopk_validate_k4, ctopk_version,
+    ctopk_workspace_bytes, make_k4_args,
     default_scale, load, make_args,
 )

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libctopk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "score_scan.hip", "select.hip", "bound.hip", "vsum.hip", "encoder.hip"]
+SOURCES = ["api.hip", "score_scan.hip", "select.hip", "bound.hip", "vsum.hip", "encoder.hip", "k4.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",

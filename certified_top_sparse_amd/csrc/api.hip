@@ -7,6 +7,8 @@
 // Logits path (ctopk_certify_logits):
 //   resolve (including level 0) -> vsum
 // Encoder-shaped path (all queries of a head, small n): one fused kernel.
+// 4-bit candidates (ctopk_candidates_k4): 4-bit scan (intervals, settled
+//   bits, straddle masks) -> rescoring of straddling keys -> counts.
 // Every launch goes to the caller's stream; nothing is copied to the host.
 #include <math.h>
 #include <stdarg.h>
@@ -205,6 +207,52 @@ int plan_of(const ctopk_args* a) {
 int hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(CTOPK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return CTOPK_OK;
+}
+
+size_t k4_workspace(int64_t n, int n_q, int n_kv) {
+  const int nzb = ctopk::k4_head_blocks(n_q / n_kv);
+  return up(static_cast<size_t>(n_kv) * nzb * static_cast<size_t>(ctopk::ceil_div(n, ctopk::kScanTile)) *
+            sizeof(unsigned long long));
+}
+
+int check_k4_shape(const void* K, int32_t dtype, int64_t n, int32_t d, int32_t n_kv) {
+  if (dtype != CTOPK_F32 && dtype != CTOPK_BF16)
+    return fail(CTOPK_ERR_UNSUPPORTED, "dtype %d is not CTOPK_F32 or CTOPK_BF16", dtype);
+  if (n < 1 || n > kMaxN) return fail(CTOPK_ERR_SHAPE, "n must be in [1, 2^31-1], got %lld",
+                                      static_cast<long long>(n));
+  if (d != 64 && d != 128) return fail(CTOPK_ERR_SHAPE, "d must be 64 or 128, got %d", d);
+  if (n_kv < 1) return fail(CTOPK_ERR_SHAPE, "n_kv_heads must be >= 1, got %d", n_kv);
+  if (n_kv > 65535) return fail(CTOPK_ERR_UNSUPPORTED, "n_kv_heads above 65535 is not supported");
+  if (static_cast<int64_t>(n_kv) * n > kMaxElems)
+    return fail(CTOPK_ERR_UNSUPPORTED, "n_kv_heads * n above 2^36 is not supported");
+  if (!aligned16(K)) return fail(CTOPK_ERR_ALIGN, "K must be 16-byte aligned");
+  return CTOPK_OK;
+}
+
+int validate_k4(const ctopk_k4_args* a) {
+  if (a == nullptr) return fail(CTOPK_ERR_NULL, "args is NULL");
+  if (!a->q || !a->K || !a->K4 || !a->kscale || !a->kres || !a->threshold)
+    return fail(CTOPK_ERR_NULL, "q, K, K4, kscale, kres and threshold must be non-NULL");
+  if (!a->sel_mask || !a->count) return fail(CTOPK_ERR_NULL, "sel_mask and count must be non-NULL");
+  int rc = check_k4_shape(a->K, a->dtype, a->n, a->d, a->n_kv_heads);
+  if (rc != CTOPK_OK) return rc;
+  if (a->n_q_heads < 1 || a->n_q_heads % a->n_kv_heads != 0)
+    return fail(CTOPK_ERR_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                a->n_q_heads, a->n_kv_heads);
+  if (static_cast<int64_t>(a->n_q_heads) * a->n > kMaxElems)
+    return fail(CTOPK_ERR_UNSUPPORTED, "n_q_heads * n above 2^36 is not supported");
+  if (!aligned16(a->q) || !aligned(a->K4, 4) || !aligned(a->kscale, 4) || !aligned(a->kres, 4) ||
+      !aligned(a->threshold, 4) || !aligned(a->sel_mask, 4) || !aligned(a->count, 4) ||
+      (a->head_scale && !aligned(a->head_scale, 4)) || (a->rescored && !aligned(a->rescored, 4)) ||
+      (a->bounds && !aligned(a->bounds, 8)))
+    return fail(CTOPK_ERR_ALIGN, "q must be 16-byte aligned, K4 and the other arrays element aligned");
+  if (a->workspace != nullptr) {
+    if (!aligned(a->workspace, kAlign)) return fail(CTOPK_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const size_t need = k4_workspace(a->n, a->n_q_heads, a->n_kv_heads);
+    if (a->workspace_bytes < need)
+      return fail(CTOPK_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", a->workspace_bytes, need);
+  }
   return CTOPK_OK;
 }
 
@@ -407,6 +455,51 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
   return ok();
+}
+
+int ctopk_quantize_k4(const void* K, int32_t dtype, int64_t n, int32_t d, int32_t n_kv_heads,
+                      uint8_t* K4, float* kscale, float* kres, ctopk_stream_t stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CallEvents events;
+  if (!K || !K4 || !kscale || !kres) return fail(CTOPK_ERR_NULL, "K, K4, kscale and kres must be non-NULL");
+  int rc = check_k4_shape(K, dtype, n, d, n_kv_heads);
+  if (rc != CTOPK_OK) return rc;
+  if (!aligned(K4, 4) || !aligned(kscale, 4) || !aligned(kres, 4))
+    return fail(CTOPK_ERR_ALIGN, "K4, kscale and kres must be 4-byte aligned");
+  rc = hip_check(ctopk::launch_quantize_k4(K, dtype, d, static_cast<int64_t>(n_kv_heads) * n, K4,
+                                           kscale, kres, st),
+                 "quantize launch");
+  return rc == CTOPK_OK ? ok() : rc;
+}
+
+int ctopk_validate_k4(const ctopk_k4_args* a) {
+  const int rc = validate_k4(a);
+  return rc == CTOPK_OK ? ok() : rc;
+}
+
+size_t ctopk_k4_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads) {
+  if (n < 1 || n > kMaxN || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0) return 0;
+  return k4_workspace(n, n_q_heads, n_kv_heads);
+}
+
+int ctopk_candidates_k4(const ctopk_k4_args* a, ctopk_stream_t stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CallEvents events;
+  int rc = validate_k4(a);
+  if (rc != CTOPK_OK) return rc;
+  void* ws = a->workspace;
+  if (ws == nullptr) {
+    rc = cached_workspace(k4_workspace(a->n, a->n_q_heads, a->n_kv_heads), st, &ws);
+    if (rc != CTOPK_OK) return rc;
+  }
+  const float default_scale = static_cast<float>(1.0 / sqrt(static_cast<double>(a->d)));
+  rc = hip_check(ctopk::launch_candidates_k4(a->q, a->K, a->dtype, a->d, a->K4, a->kscale, a->kres,
+                                             a->head_scale, default_scale, a->threshold, a->n,
+                                             a->n_q_heads, a->n_kv_heads, a->sel_mask, a->count,
+                                             a->rescored, reinterpret_cast<float2*>(a->bounds), ws,
+                                             st),
+                 "candidates launch");
+  return rc == CTOPK_OK ? ok() : rc;
 }
 
 int ctopk_record_kernel_events(void* const* events, int32_t count) {

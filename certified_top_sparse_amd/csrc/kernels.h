@@ -119,6 +119,21 @@ hipError_t launch_tail_fix(const float* scores, int64_t n, int rows, int n_v, co
 // mass below it fits eps * Z; keeps every key at or above it.  Writes RowSel
 // (thr at that score), k_eps (keys kept), tau (the certified bound), lse and
 // sel_mask (optional).  nblk <= kBoundMaxTiles.
+// 4-bit key copy: K [rows, d] (rows = n_kv * n) -> K4 [rows, d / 2] packed
+// codes, kscale [rows] and kres [rows] (an upper bound on the residual norm).
+hipError_t launch_quantize_k4(const void* K, int dtype, int d, int64_t rows, uint8_t* K4,
+                              float* kscale, float* kres, hipStream_t st);
+// Head blocks per KV head of the 4-bit scan (straddle masks are kept per block).
+int k4_head_blocks(int group);
+// Exact candidates {i : s_hi >= thr[h]} from the 4-bit copy: mask [n_q, ceil(n/32)],
+// count [n_q], optional rescored [n_kv] (keys whose full-width row was read) and
+// bounds [n_q, n] (lo, hi).  straddle: n_kv * k4_head_blocks(G) * ceil(n/64) uint64.
+hipError_t launch_candidates_k4(const void* q, const void* K, int dtype, int d, const uint8_t* K4,
+                                const float* kscale, const float* kres, const float* head_scale,
+                                float default_scale, const float* thr, int64_t n, int n_q,
+                                int n_kv, uint32_t* mask, int32_t* count, int32_t* rescored,
+                                float2* bounds, void* straddle, hipStream_t st);
+
 hipError_t launch_bound(const float* scores, int64_t n, int rows, const float2* blkstat,
                         const float* blkz, int nblk, double eps, RowSel* rs, int32_t* k_eps,
                         double* tau, double* lse, uint32_t* sel_mask, hipStream_t st);

@@ -22,45 +22,10 @@
 //     of K read);
 
 #include "kernels.h"
+#include "scan_dot.h"
 
 namespace ctopk {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-template <typename T>
-struct Slice;
-
-// bf16: 8 elements per 16-byte slice, dot2 on packed pairs.
-template <>
-struct Slice<uint16_t> {
-  static constexpr int kElems = 8;
-  __device__ static __forceinline__ float dot(const uint4& k, const uint4& q) {
-    float a = 0.0f;
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.x),
-                                        __builtin_bit_cast(bf16x2_t, q.x), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.y),
-                                        __builtin_bit_cast(bf16x2_t, q.y), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.z),
-                                        __builtin_bit_cast(bf16x2_t, q.z), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.w),
-                                        __builtin_bit_cast(bf16x2_t, q.w), a, false);
-    return a;
-  }
-};
-
-// fp32: 4 elements per 16-byte slice.
-template <>
-struct Slice<float> {
-  static constexpr int kElems = 4;
-  __device__ static __forceinline__ float dot(const uint4& k, const uint4& q) {
-    float a = __uint_as_float(k.x) * __uint_as_float(q.x);
-    a = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), a);
-    a = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), a);
-    a = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), a);
-    return a;
-  }
-};
 
 // One block per tile of kScanTile keys of one KV head and up to GB query
 // heads: 4 waves, each covering kScanTile / 4 keys with all of its K loads

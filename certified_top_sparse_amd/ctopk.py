@@ -42,7 +42,8 @@ STATUS_NAMES = {
 EXPORTED = (
     "ctopk_certify", "ctopk_certify_ex", "ctopk_workspace_bytes", "ctopk_certify_logits",
     "ctopk_logits_workspace_bytes", "ctopk_validate", "ctopk_last_error_string",
-    "ctopk_version", "ctopk_record_kernel_events", "ctopk_plan",
+    "ctopk_version", "ctopk_record_kernel_events", "ctopk_plan", "ctopk_quantize_k4",
+    "ctopk_candidates_k4", "ctopk_validate_k4", "ctopk_k4_workspace_bytes",
 )
 
 
@@ -70,6 +71,30 @@ class CtopkArgs(ctypes.Structure):
         ("out_err", ctypes.c_void_p),
         ("out_dense", ctypes.c_void_p),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class CtopkK4Args(ctypes.Structure):
+    """Mirror of ctopk_k4_args."""
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("K", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("n", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_scale", ctypes.c_void_p),
+        ("K4", ctypes.c_void_p),
+        ("kscale", ctypes.c_void_p),
+        ("kres", ctypes.c_void_p),
+        ("threshold", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("sel_mask", ctypes.c_void_p),
+        ("count", ctypes.c_void_p),
+        ("rescored", ctypes.c_void_p),
+        ("bounds", ctypes.c_void_p),
     ]
 
 
@@ -118,6 +143,14 @@ def load(path: str = LIB_PATH):
     lib.ctopk_version.restype = ctypes.c_char_p
     lib.ctopk_record_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.ctopk_record_kernel_events.restype = ctypes.c_int
+    lib.ctopk_quantize_k4.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, vp]
+    lib.ctopk_quantize_k4.restype = ctypes.c_int
+    lib.ctopk_candidates_k4.argtypes = [ctypes.POINTER(CtopkK4Args), vp]
+    lib.ctopk_candidates_k4.restype = ctypes.c_int
+    lib.ctopk_validate_k4.argtypes = [ctypes.POINTER(CtopkK4Args)]
+    lib.ctopk_validate_k4.restype = ctypes.c_int
+    lib.ctopk_k4_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.ctopk_k4_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -316,3 +349,78 @@ def default_scale(d: int) -> float:
     """The float32 value of 1/sqrt(d) the library uses when no scale is given."""
     import numpy as np
     return float(np.float32(1.0 / math.sqrt(d)))
+
+
+# ---------------------------------------------------------------------------
+# 4-bit key copy and exact candidates
+# ---------------------------------------------------------------------------
+def ctopk_quantize_k4(K, *, stream=None):
+    """4-bit copy of K [Hkv, n, d] (bf16 or fp32): returns (K4 uint8
+    [Hkv, n, d/2], kscale fp32 [Hkv, n], kres fp32 [Hkv, n])."""
+    import torch
+    lib = load()
+    _require_cuda_contig("K", K)
+    n_kv, n, d = K.shape
+    dev = K.device
+    K4 = torch.empty((n_kv, n, d // 2), dtype=torch.uint8, device=dev)
+    ks = torch.empty((n_kv, n), dtype=torch.float32, device=dev)
+    kr = torch.empty((n_kv, n), dtype=torch.float32, device=dev)
+    _check(lib.ctopk_quantize_k4(_ptr(K), _dtype_code(K), n, d, n_kv, _ptr(K4), _ptr(ks), _ptr(kr),
+                                 _stream(stream)))
+    return K4, ks, kr
+
+
+def make_k4_args(q, K, K4, kscale, kres, threshold, *, head_scale=None, workspace=None,
+                 sel_mask=None, count=None, rescored=None, bounds=None) -> CtopkK4Args:
+    """Fill a CtopkK4Args from tensors (no checks beyond what the C side does)."""
+    n_q, d = q.shape
+    n_kv, n, _ = K.shape
+    a = CtopkK4Args()
+    a.q, a.K = _ptr(q), _ptr(K)
+    a.dtype = _dtype_code(K)
+    a.n, a.d, a.n_q_heads, a.n_kv_heads = n, d, n_q, n_kv
+    a.head_scale = _ptr(head_scale)
+    a.K4, a.kscale, a.kres, a.threshold = _ptr(K4), _ptr(kscale), _ptr(kres), _ptr(threshold)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    a.sel_mask, a.count, a.rescored, a.bounds = _ptr(sel_mask), _ptr(count), _ptr(rescored), _ptr(bounds)
+    return a
+
+
+def ctopk_validate_k4(args: CtopkK4Args) -> int:
+    return int(load().ctopk_validate_k4(ctypes.byref(args)))
+
+
+def ctopk_k4_workspace_bytes(n, n_q_heads, n_kv_heads) -> int:
+    return int(load().ctopk_k4_workspace_bytes(n, n_q_heads, n_kv_heads))
+
+
+def ctopk_candidates_k4(q, K, K4, kscale, kres, threshold, *, head_scale=None, workspace=None,
+                        want_bounds=False, stream=None):
+    """Exact candidates {i : s_hi >= threshold[h]} from the 4-bit copy.
+    Returns a dict: sel_mask [Hq, ceil(n/32)] int32 words, count [Hq] int32,
+    rescored [Hkv] int32 and, on request, bounds [Hq, n, 2] fp32 (lo, hi)."""
+    import torch
+    lib = load()
+    for name, t in (("q", q), ("K", K), ("K4", K4), ("kscale", kscale), ("kres", kres),
+                    ("threshold", threshold)):
+        _require_cuda_contig(name, t)
+    if q.dtype != K.dtype:
+        raise TypeError("q and K must share one dtype")
+    n_q, d = q.shape
+    n_kv, n, _ = K.shape
+    dev = q.device
+    res = {
+        "sel_mask": torch.empty((n_q, (n + 31) // 32), dtype=torch.int32, device=dev),
+        "count": torch.empty(n_q, dtype=torch.int32, device=dev),
+        "rescored": torch.empty(n_kv, dtype=torch.int32, device=dev),
+    }
+    if want_bounds:
+        res["bounds"] = torch.empty((n_q, n, 2), dtype=torch.float32, device=dev)
+    if head_scale is not None:
+        _require_cuda_contig("head_scale", head_scale)
+    a = make_k4_args(q, K, K4, kscale, kres, threshold, head_scale=head_scale, workspace=workspace,
+                     sel_mask=res["sel_mask"], count=res["count"], rescored=res["rescored"],
+                     bounds=res.get("bounds"))
+    _check(lib.ctopk_candidates_k4(ctypes.byref(a), _stream(stream)))
+    return res

@@ -206,10 +206,79 @@ CTOPK_API size_t ctopk_logits_workspace_bytes(int64_t n, int32_t dv, int32_t row
 CTOPK_API int ctopk_validate(const ctopk_args* a);
 
 /*
+ * 4-bit key copy and exact candidate generation ("Certified Sparse Attention
+ * via Perturbed Retrieval", arXiv 2610.24991, Abstract: a 4-bit scan with
+ * deterministic bounds, shared across a GQA group, generates candidates
+ * exactly while reading every key; the page prints no formula, so the copy
+ * and the bound below are the library's reading).
+ *
+ * ctopk_quantize_k4 -- builds the copy of K [n_kv_heads, n, d] (dtype bf16 or
+ * fp32, d 64 or 128, 16-byte aligned): per key a = amax / 7 (fp32, rounded to
+ * nearest), codes c_j = clamp(rint(k_j / a), -7, 7) computed in fp32, packed
+ * as two's-complement nibbles with element 2j in the low half of byte j
+ * (K4 [n_kv_heads, n, d/2], 4-byte aligned), kscale [n_kv_heads, n] = a, and
+ * kres [n_kv_heads, n] >= ||k - a c||_2 (rounded up).  A zero key gets a = 0
+ * and codes 0.  Enqueued on `stream`; the caller owns every buffer and may
+ * keep the copy for any later ctopk_candidates_k4 call on the same K.
+ * Returns CTOPK_ERR_NULL / _SHAPE / _UNSUPPORTED / _ALIGN on bad arguments.
+ */
+CTOPK_API int ctopk_quantize_k4(const void* K, int32_t dtype, int64_t n, int32_t d,
+                                int32_t n_kv_heads, uint8_t* K4, float* kscale, float* kres,
+                                ctopk_stream_t stream);
+
+/*
+ * ctopk_candidates_k4 -- for per-head thresholds T_h, the exact candidate set
+ * { i : s_hi >= T_h }, with s_hi = scale_h * <q_h, k_i> in the library's fp32
+ * arithmetic (the scores ctopk_certify_ex returns): the 4-bit scan bounds every
+ * score within R = |scale_h| ||q_h||_2 kres_i (plus the rounding of the fp32
+ * dot products) of scale_h * kscale_i * <q_h, codes_i>, settles every key whose
+ * interval lies wholly on one side of T_h, and reads the full-width row only
+ * of keys whose interval straddles T_h for some head of its group.
+ *
+ * Inputs: q [n_q_heads, d] and K (as for ctopk_certify_ex, same dtype), the
+ * copy from ctopk_quantize_k4, head_scale [n_q_heads] fp32 (NULL: 1/sqrt(d)),
+ * threshold [n_q_heads] fp32.  Outputs: sel_mask [n_q_heads, ceil(n/32)] bit
+ * words (bit i%32 of word i/32: key i is a candidate), count [n_q_heads] int32
+ * (candidates per head), and optionally rescored [n_kv_heads] int32 (full-width
+ * rows read per KV head, counted once per block of up to 8 query heads) and
+ * bounds [n_q_heads, n] float2 (each score interval (lo, hi)).  workspace:
+ * NULL (a cached per-device buffer) or 256-byte aligned with at least
+ * ctopk_k4_workspace_bytes(...) bytes.
+ */
+typedef struct {
+  const void* q;
+  const void* K;
+  int32_t dtype;
+  int64_t n;
+  int32_t d;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  const float* head_scale;
+  const uint8_t* K4;
+  const float* kscale;
+  const float* kres;
+  const float* threshold;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t* sel_mask;
+  int32_t* count;
+  int32_t* rescored;
+  float* bounds;
+} ctopk_k4_args;
+
+CTOPK_API int ctopk_candidates_k4(const ctopk_k4_args* a, ctopk_stream_t stream);
+
+/* Host-side checks of ctopk_candidates_k4 alone (no HIP call). */
+CTOPK_API int ctopk_validate_k4(const ctopk_k4_args* a);
+
+/* Device scratch bytes ctopk_candidates_k4 needs (0 on bad sizes). */
+CTOPK_API size_t ctopk_k4_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads);
+
+/*
  * ctopk_record_kernel_events -- instrumentation for benchmarks and profilers.
  *
- * Arms the calling thread so that its NEXT ctopk_certify, ctopk_certify_ex or
- * ctopk_certify_logits call attaches the event pair (events[2i],
+ * Arms the calling thread so that its NEXT ctopk_certify, ctopk_certify_ex,
+ * ctopk_certify_logits or ctopk_candidates_k4 call attaches the event pair (events[2i],
  * events[2i+1]) -- hipEvent_t handles created by the caller -- to the i-th
  * kernel it launches: the events take that kernel's start and end times on
  * the call's stream (hipExtLaunchKernel), so hipEventElapsedTime on a pair is
@@ -219,7 +288,8 @@ CTOPK_API int ctopk_validate(const ctopk_args* a);
  * to back on the stream and measures only the stream's own gap between the
  * two records, not a kernel), then one pair per remaining kernel (three in
  * every decode plan).  Logits
- * path: select, value stream, output combine.  Kernels past count/2 pairs run
+ * path: select, value stream, output combine.  Candidates: 4-bit scan,
+ * rescoring, counts.  Kernels past count/2 pairs run
  * without events; pairs left over are
  * dropped when the call returns.  count must be even and at most 16 (0
  * disarms); returns CTOPK_ERR_SHAPE otherwise, CTOPK_ERR_NULL for a NULL

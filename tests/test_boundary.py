@@ -227,3 +227,62 @@ def test_bound_flag_plan_and_limits(lib):
     assert ct.ctopk_plan(good_args(n=262144, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
     assert ct.ctopk_validate(good_args(n=262145, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_ERR_UNSUPPORTED
     assert ct.ctopk_validate(good_args(flags=2)) == cb.CTOPK_ERR_UNSUPPORTED
+
+
+def good_k4_args(**kw):
+    a = cb.CtopkK4Args()
+    a.q, a.K = A16, A16 * 2
+    a.dtype = cb.CTOPK_BF16
+    a.n, a.d, a.n_q_heads, a.n_kv_heads = 32768, 128, 32, 8
+    a.K4, a.kscale, a.kres, a.threshold = A16 * 3, A16 * 4, A16 * 5, A16 * 6
+    a.sel_mask, a.count = A16 * 7, A16 * 8
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_k4_struct_layout_matches_header():
+    text = open(HEADER).read()
+    body = text[text.index("ctopk_candidates_k4 -- "):text.index("} ctopk_k4_args;")]
+    body = body[body.index("typedef struct {") + len("typedef struct {"):]
+    names = re.findall(r"\b(\w+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert names == [f for f, _ in cb.CtopkK4Args._fields_]
+
+
+def test_k4_validation(lib):
+    v = ct.ctopk_validate_k4
+    assert v(good_k4_args()) == cb.CTOPK_OK
+    assert v(good_k4_args(rescored=A16 * 9, bounds=A16 * 10, head_scale=A16 * 11)) == cb.CTOPK_OK
+    for f in ("q", "K", "K4", "kscale", "kres", "threshold", "sel_mask", "count"):
+        assert v(good_k4_args(**{f: 0})) == cb.CTOPK_ERR_NULL, f
+    assert v(good_k4_args(d=96)) == cb.CTOPK_ERR_SHAPE
+    assert v(good_k4_args(n=0)) == cb.CTOPK_ERR_SHAPE
+    assert v(good_k4_args(n_q_heads=30)) == cb.CTOPK_ERR_SHAPE
+    assert v(good_k4_args(n_kv_heads=0)) == cb.CTOPK_ERR_SHAPE
+    assert v(good_k4_args(dtype=7)) == cb.CTOPK_ERR_UNSUPPORTED
+    assert v(good_k4_args(q=A16 + 4)) == cb.CTOPK_ERR_ALIGN
+    assert v(good_k4_args(K=A16 + 8)) == cb.CTOPK_ERR_ALIGN
+    assert v(good_k4_args(K4=A16 + 2)) == cb.CTOPK_ERR_ALIGN
+    assert v(good_k4_args(bounds=A16 + 4)) == cb.CTOPK_ERR_ALIGN
+    need = ct.ctopk_k4_workspace_bytes(32768, 32, 8)
+    assert need >= 8 * 512 * 8  # one straddle word per (KV head, tile)
+    assert v(good_k4_args(workspace=A16 * 12, workspace_bytes=need)) == cb.CTOPK_OK
+    assert v(good_k4_args(workspace=A16 * 12, workspace_bytes=need - 1)) == cb.CTOPK_ERR_WORKSPACE
+    assert v(good_k4_args(workspace=A16 * 12 + 16, workspace_bytes=need)) == cb.CTOPK_ERR_ALIGN
+    assert ct.ctopk_k4_workspace_bytes(0, 32, 8) == 0
+    assert ct.ctopk_k4_workspace_bytes(100, 30, 8) == 0
+    # groups wider than 8 heads keep one straddle word per block of 8
+    assert ct.ctopk_k4_workspace_bytes(32768, 128, 8) >= 2 * need
+
+
+def test_k4_entry_points_reject_before_any_gpu_call(lib):
+    vp = ctypes.c_void_p
+    assert lib.ctopk_candidates_k4(ctypes.byref(good_k4_args(d=96)), None) == cb.CTOPK_ERR_SHAPE
+    assert lib.ctopk_quantize_k4(vp(A16), cb.CTOPK_BF16, 4096, 96, 8, vp(A16), vp(A16), vp(A16),
+                                 None) == cb.CTOPK_ERR_SHAPE
+    assert lib.ctopk_quantize_k4(None, cb.CTOPK_BF16, 4096, 128, 8, vp(A16), vp(A16), vp(A16),
+                                 None) == cb.CTOPK_ERR_NULL
+    assert lib.ctopk_quantize_k4(vp(A16 + 8), cb.CTOPK_BF16, 4096, 128, 8, vp(A16), vp(A16),
+                                 vp(A16), None) == cb.CTOPK_ERR_ALIGN
+    assert lib.ctopk_quantize_k4(vp(A16), 5, 4096, 128, 8, vp(A16), vp(A16), vp(A16),
+                                 None) == cb.CTOPK_ERR_UNSUPPORTED
