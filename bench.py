@@ -57,7 +57,9 @@ _COMMON = ("kernels.h", "device_common.h")
 # Sources each kernel is built from: a counter figure applies only while they
 # are unchanged.
 KERNEL_SOURCES = {
-    "score_scan": ("score_scan.hip",) + _COMMON,
+    "score_scan": ("score_scan.hip", "scan_dot.h") + _COMMON,
+    "k4_scan": ("k4.hip", "scan_dot.h") + _COMMON,
+    "k4_rescore": ("k4.hip", "scan_dot.h") + _COMMON,
     "select_dense": ("select.hip", "vsum_body.h") + _COMMON,
     "resolve": ("select.hip", "vsum_body.h") + _COMMON,
     "tail": ("vsum.hip", "vsum_body.h") + _COMMON,
@@ -304,7 +306,7 @@ def k4_leg(lib, ct, torch, hip, Q, Kd, T_cut, T_top, steps):
     mask = torch.empty((n_q, (n + 31) // 32), dtype=torch.int32, device="cuda")
     count = torch.empty(n_q, dtype=torch.int32, device="cuda")
     resc = torch.empty(n_kv, dtype=torch.int32, device="cuda")
-    names = ("k4_scan", "k4_rescore", "k4_count")
+    names = ("k4_scan", "k4_rescore")
     out = {"quantize_us_per_call": round(quant_us, 3),
            "scan_bytes_per_call": n_kv * n * (d // 2 + 8),
            "full_width_scan_bytes": n_kv * n * d * 2}

@@ -8,7 +8,7 @@
 //   resolve (including level 0) -> vsum
 // Encoder-shaped path (all queries of a head, small n): one fused kernel.
 // 4-bit candidates (ctopk_candidates_k4): 4-bit scan (intervals, settled
-//   bits, straddle masks) -> rescoring of straddling keys -> counts.
+//   bits, straddle masks) -> rescoring of straddling keys, with the counts.
 // Every launch goes to the caller's stream; nothing is copied to the host.
 #include <math.h>
 #include <stdarg.h>

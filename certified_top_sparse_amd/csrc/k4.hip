@@ -102,134 +102,201 @@ hipError_t launch_quantize_d(const void* K, int64_t rows, uint8_t* K4, float* ks
 }
 
 // ---------------------------------------------------------------------------
-// The scan: one block per (64-key tile, KV head, up to GB query heads).
-// D / 8 lanes per key, each with 8 codes (4 bytes) and the matching 8 fp32
-// elements of every q_h of the block.
+// The scan on MFMA: scores of up to 8 query heads against 16 keys per
+// v_mfma_f32_16x16x32_bf16 group, rows = heads, columns = keys, k over d in
+// blocks of 32 (A[i][k] in lane i + 16 (k / 8), B[k][j] in lane j + 16 (k / 8),
+// D[i][j] in lane j + 16 (i / 4), element i % 4).  The order of k inside the
+// product is free as long as both operands share it: in block kb, lane group
+// g holds elements 8 KB g + 8 kb + t (t < 8), so one load of 4 KB bytes gives
+// a lane its key's codes for every block.  A code c enters the product as
+// the bf16 number 136 + c (0x4300 | (c + 8): exact, and made from the nibble
+// with two bit operations), so the product is sum q (136 + c) and the dot is
+// that minus 136 sum q.  One wave per 64-key tile; no LDS, no barrier.
 // ---------------------------------------------------------------------------
+typedef __bf16 k4_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float k4_f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 template <typename T, int D, int GB>
 __global__ __launch_bounds__(256) void k4_scan_kernel(
     const T* __restrict__ q, const uint8_t* __restrict__ K4, const float* __restrict__ kscale,
     const float* __restrict__ kres, const float* __restrict__ head_scale, float default_scale,
     const float* __restrict__ thr, int64_t n, int G, int nblk, int nzb,
     uint32_t* __restrict__ mask, unsigned long long* __restrict__ smask,
-    float2* __restrict__ bounds) {
-  constexpr int CPL = 8;              // codes per lane
-  constexpr int LPR = D / CPL;        // lanes per key
-  constexpr int RPW = kWave / LPR;    // keys per wave and step
-  constexpr int WAVES = 4;
-  constexpr int ITER = kScanTile / (WAVES * RPW);
-  static_assert(GB <= LPR, "one lane per head within a key's lanes");
-  static_assert(kScanTile == kWave, "one key per lane in the classification");
-  __shared__ float s_dot[GB][kScanTile];
-  __shared__ float s_a[kScanTile], s_rho[kScanTile];
-  __shared__ uint32_t s_str[GB][2];
-
-  const int tile = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int z = blockIdx.z;
+    float2* __restrict__ bounds, int32_t* __restrict__ count, int32_t* __restrict__ rescored) {
+  constexpr int KB = D / 32;           // k blocks
+  constexpr int BPL = 4 * KB;          // code bytes per lane and key
+  constexpr int GROUPS = kScanTile / 16;
+  constexpr bool kSplit = sizeof(T) == 4;  // fp32 q: a high and a low bf16 part
+  static_assert(GB <= 8, "heads are MFMA rows 0..7");
+  static_assert(kScanTile == 64, "four 16-key groups per wave");
+  __shared__ float s_dot[4][kScanTile * GB];  // wave-private
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int seg = lane % LPR;
-  const int rg = lane / LPR;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= nblk) return;  // whole wave; nothing below synchronises the block
+  const int kvh = blockIdx.y;
+  const int z = blockIdx.z;
   const int h0 = kvh * G + z * GB;
   const int nh = min(GB, G - z * GB);
+  const int j = lane & 15;
+  const int g = lane >> 4;
   const int64_t tile0 = static_cast<int64_t>(tile) * kScanTile;
-  const int lbase = wave * (ITER * RPW);
   const size_t kbase = static_cast<size_t>(kvh) * static_cast<size_t>(n);
+  if (tile == 0) {  // the totals the rescoring adds to
+    if (lane < nh) count[h0 + lane] = 0;
+    if (lane == 0 && z == 0 && rescored != nullptr) rescored[kvh] = 0;
+  }
 
-  // Codes first (rows past n re-read row n - 1 and are never classified).
-  uint32_t cw[ITER];
+  // Codes: group u's key tile0 + 16 u + j, bytes BPL g .. BPL g + BPL - 1.
+  uint32_t cw[GROUPS][KB];
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int64_t r = min(tile0 + lbase + it * RPW + rg, n - 1);
-    cw[it] = *reinterpret_cast<const uint32_t*>(K4 + (kbase + r) * (D / 2) + seg * (CPL / 2));
+  for (int u = 0; u < GROUPS; ++u) {
+    const int64_t r = min(tile0 + 16 * u + j, n - 1);
+    const uint8_t* src = K4 + (kbase + r) * (D / 2) + BPL * g;
+    if constexpr (KB == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      cw[u][0] = v.x;
+      cw[u][1] = v.y;
+      cw[u][2] = v.z;
+      cw[u][3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      cw[u][0] = v.x;
+      cw[u][1] = v.y;
+    }
   }
-  if (wave == 0) {
-    const int64_t r = min(tile0 + lane, n - 1);
-    s_a[lane] = kscale[kbase + r];
-    s_rho[lane] = kres[kbase + r];
-  }
-  // q slices in fp32, and per head |scale| ||q||_2 and the dot products'
-  // rounding allowance.
-  float qv[GB][CPL];
-  float sc[GB], b2[GB], b1[GB];
+
+  // A operands: row i = lane & 15 is head h0 + i (zero past nh), its elements
+  // 8 KB g + 8 kb .. + 7 for block kb; per-row sums for the offset and norms.
+  const int i_row = lane & 15;
+  const bool row_live = i_row < nh;
+  uint4 ah[KB], al[KB];
+  float qs = 0.0f, q1 = 0.0f, q2 = 0.0f;
 #pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    const int hj = h0 + min(j, nh - 1);
-    const T* qs = q + static_cast<size_t>(hj) * D + seg * CPL;
-    float n1 = 0.0f, n2 = 0.0f;
+  for (int kb = 0; kb < KB; ++kb) {
+    const T* src = q + static_cast<size_t>(h0 + min(i_row, nh - 1)) * D + 8 * KB * g + 8 * kb;
+    float x[8];
+    if constexpr (kSplit) {
+      const uint4 v0 = *reinterpret_cast<const uint4*>(src);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(src + 4);
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      float v;
-      if constexpr (sizeof(T) == 2) {
-        v = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(qs)[e]) << 16);
-      } else {
-        v = reinterpret_cast<const float*>(qs)[e];
+      for (int t = 0; t < 8; ++t) x[t] = row_live ? __uint_as_float(w[t]) : 0.0f;
+      uint32_t hw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t bh = bf16_rne_bits(x[t]);
+        const float xh = __uint_as_float(bh << 16);
+        const uint32_t bl = bf16_rne_bits(x[t] - xh);
+        hw[t / 2] |= bh << (16 * (t & 1));
+        lw[t / 2] |= bl << (16 * (t & 1));
+        qs += xh + __uint_as_float(bl << 16);
       }
-      qv[j][e] = v;
-      n1 += fabsf(v);
-      n2 = fmaf(v, v, n2);
+      ah[kb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      al[kb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+      uint4 v = *reinterpret_cast<const uint4*>(src);
+      if (!row_live) v = make_uint4(0u, 0u, 0u, 0u);
+      Slice<uint16_t>::unpack(v, x);
+      ah[kb] = v;
+      al[kb] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qs += x[t];
     }
-    n1 = group_sum<LPR>(n1);
-    n2 = group_sum<LPR>(n2);
-    sc[j] = head_scale != nullptr ? head_scale[hj] : default_scale;
-    const float as = fabsf(sc[j]);
-    b2[j] = as * sqrtf(n2) * 1.00001f;
-    // |fl(dot) - dot| <= (steps) 2^-24 sum |q_e c_e| <= (D + 4) 2^-24 * 7 ||q||_1 * a,
-    // once for the 4-bit dot and once for the full-width one (amax = 7 a)
-    b1[j] = as * n1 * (2.0f * kLevel * static_cast<float>(D + 4) * 5.9604645e-8f) * 1.00001f;
-  }
-
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    float c[CPL];
-#pragma unroll
-    for (int e = 0; e < CPL; ++e)
-      c[e] = static_cast<float>(static_cast<int>(cw[it] << (28 - 4 * e)) >> 28);  // nibble e, signed
-    const int lr = lbase + it * RPW + rg;
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) acc = fmaf(qv[j][e], c[e], acc);
-      acc = group_sum<LPR>(acc);
-      if (seg == j) s_dot[j][lr] = acc;
+    for (int t = 0; t < 8; ++t) {
+      q1 += fabsf(x[t]);
+      q2 = fmaf(x[t], x[t], q2);
     }
   }
-  __syncthreads();
+  // row totals over the four lane groups (lanes i, i + 16, i + 32, i + 48)
+  qs += __shfl_xor(qs, 16, 64);
+  qs += __shfl_xor(qs, 32, 64);
+  q1 += __shfl_xor(q1, 16, 64);
+  q1 += __shfl_xor(q1, 32, 64);
+  q2 += __shfl_xor(q2, 16, 64);
+  q2 += __shfl_xor(q2, 32, 64);
 
-  // Wave w classifies heads w, w + 4, ...: one key per lane.
-  const int64_t i = tile0 + lane;
-  const bool real = i < n;
+  k4_f32x4_t acc[GROUPS];
+#pragma unroll
+  for (int u = 0; u < GROUPS; ++u) {
+    acc[u] = k4_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint32_t w = cw[u][kb] ^ 0x88888888u;  // nibbles c + 8
+      uint32_t b[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        b[p] = 0x43004300u | ((w >> (8 * p)) & 0xFu) | (((w >> (8 * p + 4)) & 0xFu) << 16);
+      const k4_bf16x8_t bv = __builtin_bit_cast(k4_bf16x8_t, make_uint4(b[0], b[1], b[2], b[3]));
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(k4_bf16x8_t, ah[kb]), bv,
+                                                       acc[u], 0, 0, 0);
+      if constexpr (kSplit)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(k4_bf16x8_t, al[kb]), bv,
+                                                         acc[u], 0, 0, 0);
+    }
+  }
+
+  // The dots to one key per lane: lane j + 16 hq holds heads 4 hq + e of keys
+  // 16 u + j; through wave-private LDS each lane takes key `lane`, all heads.
+  float* sd = s_dot[wave];
+#pragma unroll
+  for (int u = 0; u < GROUPS; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * (lane >> 4) + e;
+      if (i < GB) sd[(16 * u + j) * GB + i] = acc[u][e];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+  const int64_t key = tile0 + lane;
+  const bool real = key < n;
+  const float a = kscale[kbase + min(key, n - 1)];
+  const float rho = kres[kbase + min(key, n - 1)];
   const int64_t nwords = ceil_div(n, 32);
-  for (int j = wave; j < nh; j += WAVES) {
-    const float a = s_a[lane];
-    const float shat = (sc[j] * s_dot[j][lane]) * a;
-    // plus the roundings of the two products and of R itself
-    const float R = (b2[j] * s_rho[lane] + b1[j] * a + fabsf(shat) * 4.7683716e-7f) * 1.000001f;
-    const float lo = shat - R, hi = shat + R;
-    const float th = thr[h0 + j];
-    const bool in = real && lo >= th;
-    const bool straddle = real && !(lo >= th) && !(hi < th);
-    const uint64_t bin = __ballot(in);
-    const uint64_t bst = __ballot(straddle);
-    uint32_t* mrow = mask + static_cast<size_t>(h0 + j) * static_cast<size_t>(nwords);
-    if (lane == 0) mrow[2 * tile] = static_cast<uint32_t>(bin);
-    if (lane == 1 && 2 * tile + 1 < nwords) mrow[2 * tile + 1] = static_cast<uint32_t>(bin >> 32);
-    if (lane == 0) {
-      s_str[j][0] = static_cast<uint32_t>(bst);
-      s_str[j][1] = static_cast<uint32_t>(bst >> 32);
+  uint64_t any_str = 0ull;
+#pragma unroll
+  for (int i = 0; i < GB; ++i) {
+    if (i < nh) {  // uniform
+      // head i's constants, from row lane i (uniform values)
+      const float Si = readlane_f(qs, i);
+      const float n1 = readlane_f(q1, i);
+      const float n2 = readlane_f(q2, i);
+      const float sci = head_scale != nullptr ? head_scale[h0 + i] : default_scale;
+      const float as = fabsf(sci);
+      const float b2 = as * sqrtf(n2) * 1.00001f;
+      // rounding of the 4-bit product (terms q (136 + c) and 136 sum q) and of
+      // the full-width dot (|k| <= 7 a); fp32 q: its low part's own rounding
+      const float b1 = as * n1 *
+                       ((429.0f * static_cast<float>(D + 4)) * 5.9604645e-8f +
+                        (kSplit ? 7.0f * 7.6293945e-6f : 0.0f)) * 1.00001f;
+      const float th = thr[h0 + i];
+      const float dot = sd[lane * GB + i] - 136.0f * Si;
+      const float shat = (sci * dot) * a;
+      const float R = (b2 * rho + b1 * a + fabsf(shat) * 4.7683716e-7f) * 1.000001f;
+      const float lo = shat - R, hi = shat + R;
+      const bool in = real && lo >= th;
+      const bool strad = real && !(lo >= th) && !(hi < th);
+      const uint64_t bi = __ballot(in);
+      any_str |= __ballot(strad);
+      uint32_t* mrow = mask + static_cast<size_t>(h0 + i) * static_cast<size_t>(nwords);
+      if (lane == 0) mrow[2 * tile] = static_cast<uint32_t>(bi);
+      if (lane == 1 && 2 * tile + 1 < nwords) mrow[2 * tile + 1] = static_cast<uint32_t>(bi >> 32);
+      if (bounds != nullptr && real)
+        bounds[static_cast<size_t>(h0 + i) * static_cast<size_t>(n) + key] = make_float2(lo, hi);
     }
-    if (bounds != nullptr && real)
-      bounds[static_cast<size_t>(h0 + j) * static_cast<size_t>(n) + i] = make_float2(lo, hi);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t any = 0ull;
-    for (int j = 0; j < nh; ++j)
-      any |= static_cast<uint64_t>(s_str[j][0]) | (static_cast<uint64_t>(s_str[j][1]) << 32);
-    smask[(static_cast<size_t>(kvh) * nzb + z) * nblk + tile] = any;
-  }
+  if (lane == 0) smask[(static_cast<size_t>(kvh) * nzb + z) * nblk + tile] = any_str;
 }
 
 // ---------------------------------------------------------------------------
@@ -244,7 +311,8 @@ template <typename T, int D, int GB>
 __global__ __launch_bounds__(256) void k4_rescore_kernel(
     const T* __restrict__ q, const T* __restrict__ K, const float* __restrict__ head_scale,
     float default_scale, const float* __restrict__ thr, int64_t n, int G, int nblk, int nzb,
-    const unsigned long long* __restrict__ smask, uint32_t* __restrict__ mask) {
+    const unsigned long long* __restrict__ smask, uint32_t* __restrict__ mask,
+    int32_t* __restrict__ count, int32_t* __restrict__ rescored) {
   constexpr int EPL = Slice<T>::kElems;
   constexpr int LPR = D / EPL;
   constexpr int RPW = kWave / LPR;
@@ -283,8 +351,7 @@ __global__ __launch_bounds__(256) void k4_rescore_kernel(
   }
   __syncthreads();
   const int nkeys = s_off[kRescoreTiles];
-  if (nkeys == 0) return;  // uniform: nothing straddles in this chunk
-  if (wave < kRescoreTiles / 2) {
+  if (nkeys > 0 && wave < kRescoreTiles / 2) {
     // wave w lists tiles 2w and 2w + 1: lane l of tile u writes its key if set
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -311,67 +378,55 @@ __global__ __launch_bounds__(256) void k4_rescore_kernel(
   __syncthreads();
 
   const T* Kb = K + static_cast<size_t>(kvh) * static_cast<size_t>(n) * D;
-  for (int base = wave * RPW; base < nkeys; base += WAVES * RPW) {
-    const int e = base + rg;
-    const bool live = e < nkeys;
-    const int key = s_keys[live ? e : nkeys - 1];
-    const uint4 kv = load_stream16(Kb + static_cast<size_t>(key) * D + seg * EPL);
+  constexpr int UNROLL = 8;  // rows in flight per lane
+  for (int base = wave * RPW; base < nkeys; base += WAVES * RPW * UNROLL) {  // none when nothing straddles
+    uint4 kv[UNROLL];
+    int key[UNROLL];
 #pragma unroll
-    for (int j = 0; j < GB; ++j) {
-      const float acc = group_sum<LPR>(Slice<T>::dot(kv, qv[j]));
-      const float s = acc * sc[j];
-      if (live && seg == j && j < nh && s >= th[j]) {
-        const int local = key - tile0 * kScanTile;
-        atomicOr(&s_bits[j][local >> 5], 1u << (local & 31));
+    for (int it = 0; it < UNROLL; ++it) {
+      const int e = base + it * WAVES * RPW + rg;
+      key[it] = e < nkeys ? s_keys[e] : -1;
+      kv[it] = load_stream16(Kb + static_cast<size_t>(max(key[it], 0)) * D + seg * EPL);
+    }
+#pragma unroll
+    for (int it = 0; it < UNROLL; ++it) {
+#pragma unroll
+      for (int j = 0; j < GB; ++j) {
+        const float acc = group_sum<LPR>(Slice<T>::dot(kv[it], qv[j]));
+        const float s = acc * sc[j];
+        if (key[it] >= 0 && seg == j && j < nh && s >= th[j]) {
+          const int local = key[it] - tile0 * kScanTile;
+          atomicOr(&s_bits[j][local >> 5], 1u << (local & 31));
+        }
       }
     }
   }
   __syncthreads();
   // Merge into the mask words of the tiles that had straddling keys (this
-  // block owns those words for its heads).
+  // block owns those words for its heads), and count the chunk's candidates
+  // per head and its rescored keys (integer atomics onto totals the scan
+  // zeroed, so the sums are exact whatever the order).
   const int64_t nwords = ceil_div(n, 32);
+  uint32_t c = 0u;
   if (t < nh * 2 * kRescoreTiles) {
     const int j = t / (2 * kRescoreTiles);
     const int w = t % (2 * kRescoreTiles);
     const int u = w / 2;
     const int64_t word = static_cast<int64_t>(tile0) * 2 + w;
-    if (u < ntiles && s_tm[u] != 0ull && word < nwords) {
+    if (u < ntiles && word < nwords) {
       uint32_t* p = mask + static_cast<size_t>(h0 + j) * static_cast<size_t>(nwords) + word;
-      *p = *p | s_bits[j][w];
+      uint32_t v = *p;
+      if (s_tm[u] != 0ull) {
+        v |= s_bits[j][w];
+        *p = v;
+      }
+      c = static_cast<uint32_t>(__popc(v));
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Counts: blocks [0, n_q) popcount a head's mask row; blocks [n_q, n_q + n_kv)
-// count a KV head's rescored keys (over its head blocks).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k4_count_kernel(const uint32_t* __restrict__ mask,
-                                                       const unsigned long long* __restrict__ smask,
-                                                       int64_t nwords, int n_q, int nblk, int nzb,
-                                                       int32_t* __restrict__ count,
-                                                       int32_t* __restrict__ rescored) {
-  __shared__ int s_w[4];
-  const int b = blockIdx.x;
-  int c = 0;
-  if (b < n_q) {
-    const uint32_t* row = mask + static_cast<size_t>(b) * static_cast<size_t>(nwords);
-    for (int64_t w = threadIdx.x; w < nwords; w += 256) c += __popc(row[w]);
-  } else {
-    const unsigned long long* row = smask + static_cast<size_t>(b - n_q) * nzb * nblk;
-    for (int64_t w = threadIdx.x; w < static_cast<int64_t>(nzb) * nblk; w += 256) c += __popcll(row[w]);
-  }
-  c = static_cast<int>(wave_sum_u32(static_cast<uint32_t>(c)));
-  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
-    if (b < n_q) {
-      count[b] = tot;
-    } else if (rescored != nullptr) {
-      rescored[b - n_q] = tot;
-    }
-  }
+  static_assert(2 * kRescoreTiles == 16, "one head's words fill a 16-lane row");
+  c = static_cast<uint32_t>(group_sum<16>(static_cast<float>(c)));  // <= 512: exact in fp32
+  if (t < nh * 2 * kRescoreTiles && (t & 15) == 0) atomicAdd(&count[h0 + t / 16], static_cast<int32_t>(c));
+  if (t == 0 && rescored != nullptr && nkeys > 0) atomicAdd(&rescored[kvh], nkeys);
 }
 
 template <typename T, int D, int GB>
@@ -382,18 +437,16 @@ hipError_t launch_k4_t(const void* q, const void* K, const uint8_t* K4, const fl
   const int G = n_q / n_kv;
   const int nblk = static_cast<int>(ceil_div(n, kScanTile));
   const int nzb = static_cast<int>(ceil_div(G, GB));
-  hipError_t e = launch(k4_scan_kernel<T, D, GB>, dim3(nblk, n_kv, nzb), dim3(256), 0, st,
+  hipError_t e = launch(k4_scan_kernel<T, D, GB>, dim3(static_cast<unsigned>(ceil_div(nblk, 4)), n_kv, nzb),
+                        dim3(256), 0, st,
                         static_cast<const T*>(q), K4, ks, kr, hs, ds, thr, n, G, nblk, nzb, mask,
-                        smask, bounds);
+                        smask, bounds, count, rescored);
   if (e != hipSuccess) return e;
   e = launch(k4_rescore_kernel<T, D, GB>,
              dim3(static_cast<unsigned>(ceil_div(nblk, kRescoreTiles)), n_kv, nzb), dim3(256), 0,
              st, static_cast<const T*>(q), static_cast<const T*>(K), hs, ds, thr, n, G, nblk, nzb,
-             static_cast<const unsigned long long*>(smask), mask);
-  if (e != hipSuccess) return e;
-  return launch(k4_count_kernel, dim3(n_q + n_kv), dim3(256), 0, st,
-                static_cast<const uint32_t*>(mask), static_cast<const unsigned long long*>(smask),
-                ceil_div(n, 32), n_q, nblk, nzb, count, rescored);
+             static_cast<const unsigned long long*>(smask), mask, count, rescored);
+  return e;
 }
 
 template <typename T, int D>

@@ -288,8 +288,8 @@ CTOPK_API size_t ctopk_k4_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t 
  * to back on the stream and measures only the stream's own gap between the
  * two records, not a kernel), then one pair per remaining kernel (three in
  * every decode plan).  Logits
- * path: select, value stream, output combine.  Candidates: 4-bit scan,
- * rescoring, counts.  Kernels past count/2 pairs run
+ * path: select, value stream, output combine.  Candidates: 4-bit scan, then
+ * rescoring with the counts.  Kernels past count/2 pairs run
  * without events; pairs left over are
  * dropped when the call returns.  count must be even and at most 16 (0
  * disarms); returns CTOPK_ERR_SHAPE otherwise, CTOPK_ERR_NULL for a NULL
