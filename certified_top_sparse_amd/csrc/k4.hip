@@ -30,6 +30,7 @@ namespace ctopk {
 namespace {
 
 constexpr int kLevel = 7;
+constexpr int kK4TilesPerWave = 1;  // 64-key tiles per wave of the 4-bit scan
 
 template <int L>
 __device__ __forceinline__ float group_max(float v) {
@@ -142,38 +143,55 @@ __global__ __launch_bounds__(256) void k4_scan_kernel(
   __shared__ float s_dot[4][kScanTile * GB];  // wave-private
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int tile = blockIdx.x * 4 + wave;
-  if (tile >= nblk) return;  // whole wave; nothing below synchronises the block
+  const int tile_first = (blockIdx.x * 4 + wave) * kK4TilesPerWave;
+  if (tile_first >= nblk) return;  // whole wave; nothing below synchronises the block
   const int kvh = blockIdx.y;
   const int z = blockIdx.z;
   const int h0 = kvh * G + z * GB;
   const int nh = min(GB, G - z * GB);
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int64_t tile0 = static_cast<int64_t>(tile) * kScanTile;
   const size_t kbase = static_cast<size_t>(kvh) * static_cast<size_t>(n);
-  if (tile == 0) {  // the totals the rescoring adds to
+  if (tile_first == 0) {  // the totals the rescoring adds to
     if (lane < nh) count[h0 + lane] = 0;
     if (lane == 0 && z == 0 && rescored != nullptr) rescored[kvh] = 0;
   }
 
-  // Codes: group u's key tile0 + 16 u + j, bytes BPL g .. BPL g + BPL - 1.
-  uint32_t cw[GROUPS][KB];
+  // All loads first: codes of group u's key tile0 + 16 u + j (bytes BPL g ..
+  // BPL g + BPL - 1) and each key's scale and residual bound, per tile.
+  uint32_t cw[kK4TilesPerWave][GROUPS][KB];
+  float a_key[kK4TilesPerWave], rho_key[kK4TilesPerWave];
 #pragma unroll
-  for (int u = 0; u < GROUPS; ++u) {
-    const int64_t r = min(tile0 + 16 * u + j, n - 1);
-    const uint8_t* src = K4 + (kbase + r) * (D / 2) + BPL * g;
-    if constexpr (KB == 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      cw[u][0] = v.x;
-      cw[u][1] = v.y;
-      cw[u][2] = v.z;
-      cw[u][3] = v.w;
-    } else {
-      const uint2 v = *reinterpret_cast<const uint2*>(src);
-      cw[u][0] = v.x;
-      cw[u][1] = v.y;
+  for (int tt = 0; tt < kK4TilesPerWave; ++tt) {
+    const int64_t tile0 = static_cast<int64_t>(tile_first + tt) * kScanTile;
+#pragma unroll
+    for (int u = 0; u < GROUPS; ++u) {
+      const int64_t r = min(tile0 + 16 * u + j, n - 1);
+      const uint8_t* src = K4 + (kbase + r) * (D / 2) + BPL * g;
+      if constexpr (KB == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        cw[tt][u][0] = v.x;
+        cw[tt][u][1] = v.y;
+        cw[tt][u][2] = v.z;
+        cw[tt][u][3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        cw[tt][u][0] = v.x;
+        cw[tt][u][1] = v.y;
+      }
     }
+    const int64_t r = min(tile0 + lane, n - 1);
+    a_key[tt] = kscale[kbase + r];
+    rho_key[tt] = kres[kbase + r];
+  }
+
+  // Each head's scale and threshold (uniform loads, issued with the rest).
+  float sc_h[GB], th_h[GB];
+#pragma unroll
+  for (int i = 0; i < GB; ++i) {
+    const int hi = h0 + min(i, nh - 1);
+    sc_h[i] = head_scale != nullptr ? head_scale[hi] : default_scale;
+    th_h[i] = thr[hi];
   }
 
   // A operands: row i = lane & 15 is head h0 + i (zero past nh), its elements
@@ -227,76 +245,82 @@ __global__ __launch_bounds__(256) void k4_scan_kernel(
   q2 += __shfl_xor(q2, 16, 64);
   q2 += __shfl_xor(q2, 32, 64);
 
-  k4_f32x4_t acc[GROUPS];
 #pragma unroll
-  for (int u = 0; u < GROUPS; ++u) {
-    acc[u] = k4_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int tt = 0; tt < kK4TilesPerWave; ++tt) {
+    const int tile = tile_first + tt;
+    if (tile >= nblk) break;  // uniform
+    const int64_t tile0 = static_cast<int64_t>(tile) * kScanTile;
+    k4_f32x4_t acc[GROUPS];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint32_t w = cw[u][kb] ^ 0x88888888u;  // nibbles c + 8
-      uint32_t b[4];
+    for (int u = 0; u < GROUPS; ++u) {
+      acc[u] = k4_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        b[p] = 0x43004300u | ((w >> (8 * p)) & 0xFu) | (((w >> (8 * p + 4)) & 0xFu) << 16);
-      const k4_bf16x8_t bv = __builtin_bit_cast(k4_bf16x8_t, make_uint4(b[0], b[1], b[2], b[3]));
-      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(k4_bf16x8_t, ah[kb]), bv,
-                                                       acc[u], 0, 0, 0);
-      if constexpr (kSplit)
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(k4_bf16x8_t, al[kb]), bv,
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint32_t w = cw[tt][u][kb] ^ 0x88888888u;  // nibbles c + 8
+        uint32_t b[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          b[p] = 0x43004300u | ((w >> (8 * p)) & 0xFu) | (((w >> (8 * p + 4)) & 0xFu) << 16);
+        const k4_bf16x8_t bv = __builtin_bit_cast(k4_bf16x8_t, make_uint4(b[0], b[1], b[2], b[3]));
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(k4_bf16x8_t, ah[kb]), bv,
                                                          acc[u], 0, 0, 0);
+        if constexpr (kSplit)
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(k4_bf16x8_t, al[kb]), bv,
+                                                           acc[u], 0, 0, 0);
+      }
     }
-  }
 
-  // The dots to one key per lane: lane j + 16 hq holds heads 4 hq + e of keys
-  // 16 u + j; through wave-private LDS each lane takes key `lane`, all heads.
-  float* sd = s_dot[wave];
+    // The dots to one key per lane: lane j + 16 hq holds heads 4 hq + e of keys
+    // 16 u + j; through wave-private LDS each lane takes key `lane`, all heads.
+    float* sd = s_dot[wave];
 #pragma unroll
-  for (int u = 0; u < GROUPS; ++u) {
+    for (int u = 0; u < GROUPS; ++u) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * (lane >> 4) + e;
-      if (i < GB) sd[(16 * u + j) * GB + i] = acc[u][e];
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * (lane >> 4) + e;
+        if (i < GB) sd[(16 * u + j) * GB + i] = acc[u][e];
+      }
     }
-  }
-  __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
-  const int64_t key = tile0 + lane;
-  const bool real = key < n;
-  const float a = kscale[kbase + min(key, n - 1)];
-  const float rho = kres[kbase + min(key, n - 1)];
-  const int64_t nwords = ceil_div(n, 32);
-  uint64_t any_str = 0ull;
+    __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+    const int64_t key = tile0 + lane;
+    const bool real = key < n;
+    const float a = a_key[tt];
+    const float rho = rho_key[tt];
+    const int64_t nwords = ceil_div(n, 32);
+    uint64_t any_str = 0ull;
 #pragma unroll
-  for (int i = 0; i < GB; ++i) {
-    if (i < nh) {  // uniform
-      // head i's constants, from row lane i (uniform values)
-      const float Si = readlane_f(qs, i);
-      const float n1 = readlane_f(q1, i);
-      const float n2 = readlane_f(q2, i);
-      const float sci = head_scale != nullptr ? head_scale[h0 + i] : default_scale;
-      const float as = fabsf(sci);
-      const float b2 = as * sqrtf(n2) * 1.00001f;
-      // rounding of the 4-bit product (terms q (136 + c) and 136 sum q) and of
-      // the full-width dot (|k| <= 7 a); fp32 q: its low part's own rounding
-      const float b1 = as * n1 *
-                       ((429.0f * static_cast<float>(D + 4)) * 5.9604645e-8f +
-                        (kSplit ? 7.0f * 7.6293945e-6f : 0.0f)) * 1.00001f;
-      const float th = thr[h0 + i];
-      const float dot = sd[lane * GB + i] - 136.0f * Si;
-      const float shat = (sci * dot) * a;
-      const float R = (b2 * rho + b1 * a + fabsf(shat) * 4.7683716e-7f) * 1.000001f;
-      const float lo = shat - R, hi = shat + R;
-      const bool in = real && lo >= th;
-      const bool strad = real && !(lo >= th) && !(hi < th);
-      const uint64_t bi = __ballot(in);
-      any_str |= __ballot(strad);
-      uint32_t* mrow = mask + static_cast<size_t>(h0 + i) * static_cast<size_t>(nwords);
-      if (lane == 0) mrow[2 * tile] = static_cast<uint32_t>(bi);
-      if (lane == 1 && 2 * tile + 1 < nwords) mrow[2 * tile + 1] = static_cast<uint32_t>(bi >> 32);
-      if (bounds != nullptr && real)
-        bounds[static_cast<size_t>(h0 + i) * static_cast<size_t>(n) + key] = make_float2(lo, hi);
+    for (int i = 0; i < GB; ++i) {
+      if (i < nh) {  // uniform
+        // head i's constants, from row lane i (uniform values)
+        const float Si = readlane_f(qs, i);
+        const float n1 = readlane_f(q1, i);
+        const float n2 = readlane_f(q2, i);
+        const float sci = sc_h[i];
+        const float as = fabsf(sci);
+        const float b2 = as * sqrtf(n2) * 1.00001f;
+        // rounding of the 4-bit product (terms q (136 + c) and 136 sum q) and of
+        // the full-width dot (|k| <= 7 a); fp32 q: its low part's own rounding
+        const float b1 = as * n1 *
+                         ((429.0f * static_cast<float>(D + 4)) * 5.9604645e-8f +
+                          (kSplit ? 7.0f * 7.6293945e-6f : 0.0f)) * 1.00001f;
+        const float th = th_h[i];
+        const float dot = sd[lane * GB + i] - 136.0f * Si;
+        const float shat = (sci * dot) * a;
+        const float R = (b2 * rho + b1 * a + fabsf(shat) * 4.7683716e-7f) * 1.000001f;
+        const float lo = shat - R, hi = shat + R;
+        const bool in = real && lo >= th;
+        const bool strad = real && !(lo >= th) && !(hi < th);
+        const uint64_t bi = __ballot(in);
+        any_str |= __ballot(strad);
+        uint32_t* mrow = mask + static_cast<size_t>(h0 + i) * static_cast<size_t>(nwords);
+        if (lane == 0) mrow[2 * tile] = static_cast<uint32_t>(bi);
+        if (lane == 1 && 2 * tile + 1 < nwords) mrow[2 * tile + 1] = static_cast<uint32_t>(bi >> 32);
+        if (bounds != nullptr && real)
+          bounds[static_cast<size_t>(h0 + i) * static_cast<size_t>(n) + key] = make_float2(lo, hi);
+      }
     }
+    if (lane == 0) smask[(static_cast<size_t>(kvh) * nzb + z) * nblk + tile] = any_str;
   }
-  if (lane == 0) smask[(static_cast<size_t>(kvh) * nzb + z) * nblk + tile] = any_str;
 }
 
 // ---------------------------------------------------------------------------
@@ -437,7 +461,8 @@ hipError_t launch_k4_t(const void* q, const void* K, const uint8_t* K4, const fl
   const int G = n_q / n_kv;
   const int nblk = static_cast<int>(ceil_div(n, kScanTile));
   const int nzb = static_cast<int>(ceil_div(G, GB));
-  hipError_t e = launch(k4_scan_kernel<T, D, GB>, dim3(static_cast<unsigned>(ceil_div(nblk, 4)), n_kv, nzb),
+  hipError_t e = launch(k4_scan_kernel<T, D, GB>,
+                        dim3(static_cast<unsigned>(ceil_div(nblk, 4 * kK4TilesPerWave)), n_kv, nzb),
                         dim3(256), 0, st,
                         static_cast<const T*>(q), K4, ks, kr, hs, ds, thr, n, G, nblk, nzb, mask,
                         smask, bounds, count, rescored);
