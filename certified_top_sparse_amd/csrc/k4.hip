@@ -257,10 +257,12 @@ __global__ __launch_bounds__(256) void k4_scan_kernel(
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const uint32_t w = cw[tt][u][kb] ^ 0x88888888u;  // nibbles c + 8
+        const uint32_t lo = w & 0x0F0F0F0Fu;                // elements 0, 2, 4, 6 (one a byte)
+        const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;         // elements 1, 3, 5, 7
         uint32_t b[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          b[p] = 0x43004300u | ((w >> (8 * p)) & 0xFu) | (((w >> (8 * p + 4)) & 0xFu) << 16);
+        for (int p = 0; p < 4; ++p)  // bytes [lo_p, 0, hi_p, 0], then the bf16 exponent byte
+          b[p] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u + 0x00010001u * p) | 0x43004300u;
         const k4_bf16x8_t bv = __builtin_bit_cast(k4_bf16x8_t, make_uint4(b[0], b[1], b[2], b[3]));
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(k4_bf16x8_t, ah[kb]), bv,
                                                          acc[u], 0, 0, 0);
