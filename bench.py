@@ -364,6 +364,83 @@ def k4_leg(lib, ct, torch, hip, Q, Kd, T_cut, T_top, steps):
     return out
 
 
+def long_leg(lib, ct, torch, hip, steps, eps):
+    """Long-context decode: batch 4 folded into 128 query / 32 KV heads,
+    n = 131072, d = 128, bf16, per-head temperature in [0.5, 2] (1 GiB each of
+    K and V, far above the 256 MB Infinity Cache, so no rotation is needed).
+    Per-call time, per-kernel times, and the score scan's rate against the
+    8 TB/s peak."""
+    wl = workloads.long_decode(batch=4)
+    n_q, d = wl["q"].shape
+    n_kv, n, _ = wl["K"].shape
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    q, K, V, hs = dev(wl["q"]), dev(wl["K"]), dev(wl["V"]), dev(wl["head_scale"])
+    del wl
+    out = torch.empty((n_q, d), dtype=torch.float32, device="cuda")
+    k_eps = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    tau = torch.empty(n_q, dtype=torch.float64, device="cuda")
+    mask = torch.empty((n_q, (n + 31) // 32), dtype=torch.int32, device="cuda")
+    res = ct.ctopk_certify_ex(q, K, V, eps, head_scale=hs, want_mask=True)
+    torch.cuda.synchronize()
+    words = res["sel_mask"].cpu().numpy().astype(np.int32).view(np.uint8)
+    bits = np.unpackbits(words.reshape(n_q, -1), axis=1, bitorder="little")[:, :n].astype(bool)
+    union = int(bits.reshape(n_kv, n_q // n_kv, n).any(axis=1).sum())
+    kmean = float(res["k_eps"].double().mean().item()) / n
+    args = ct.make_args(q, K, V, eps, head_scale=hs, out=out, k_eps=k_eps, tau=tau)
+    plan = ct.ctopk_plan(args)
+    names = KERNELS_BY_PLAN[plan]
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lib.ctopk_certify_ex
+
+    def step():
+        rc = call(ctypes.byref(args), sptr)
+        if rc != 0:
+            raise RuntimeError(ct.ctopk_last_error_string())
+
+    for _ in range(5):
+        step()
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), sptr)
+    for _ in range(steps):
+        step()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), sptr)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    n_ev = 2 * len(names)
+    evs = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    arrs = [(ctypes.c_void_p * n_ev)(*[ctypes.c_void_p(e) for e in row]) for row in evs]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        lib.ctopk_record_kernel_events(arrs[i], n_ev)
+        step()
+    torch.cuda.synchronize()
+    per = np.array([[hip.elapsed_ms(row[2 * j], row[2 * j + 1]) for j in range(len(names))]
+                    for row in evs])
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    kern = {nm: round(float(per[:, j].mean()) * 1e3, 3) for j, nm in enumerate(names)}
+    k_bytes = n_kv * n * d * 2
+    scan_gbps = k_bytes / (kern["score_scan"] * 1e-6) / 1e9
+    e2e_gbps = (k_bytes + union * d * 2) / (us * 1e-6) / 1e9
+    return {"workload": "long_decode batch 4: 128 query / 32 KV heads, n=131072, d=128, bf16",
+            "eps": eps, "steps": steps, "plan": PLAN_NAMES.get(plan, plan),
+            "us_per_call": round(us, 3), "query_heads_per_s": round(n_q / (us * 1e-6), 1),
+            "kernel_us": kern, "scan_gbps": round(scan_gbps, 1),
+            "scan_frac_of_peak": round(scan_gbps / PEAK_HBM_GBPS, 4),
+            "hbm_gbps_end_to_end": round(e2e_gbps, 1), "v_union_fraction": round(union / (n_kv * n), 4),
+            "mean_k_over_n": round(kmean, 4)}
+
+
 def encoder_leg(lib, ct, torch, hip, steps, eps, sets=16):
     """All-queries (encoder-shaped) workload: batch 8, 12 heads, 512 queries and
     512 keys per head, d = 64, bf16, per-head temperature; every query row of a
@@ -448,6 +525,8 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--bound-steps", type=int, default=1000,
                     help="calls of the blockwise-bound leg on the decode workload; 0 skips it")
+    ap.add_argument("--long-steps", type=int, default=40,
+                    help="calls of the long-context decode leg (n = 131072, 1 GiB of K); 0 skips it")
     ap.add_argument("--k4-steps", type=int, default=500,
                     help="calls per threshold of the 4-bit candidate leg; 0 skips it")
     ap.add_argument("--encoder-steps", type=int, default=500,
@@ -602,6 +681,10 @@ def main():
     if args.bound_steps > 0:
         bound = bound_leg(lib, ct, torch, hip, Q, Kd, Vd, args.bound_steps, eps)
 
+    long_decode = None
+    if args.long_steps > 0:
+        long_decode = long_leg(lib, ct, torch, hip, args.long_steps, eps)
+
     k4 = None
     if args.k4_steps > 0:
         k4 = k4_leg(lib, ct, torch, hip, Q, Kd, T_cut, T_top, args.k4_steps)
@@ -642,6 +725,7 @@ def main():
         "ms_per_step_with_kernel_events": None if ms_events is None else round(ms_events, 5),
         "bound_certificate": bound,
         "k4_candidates": k4,
+        "long_decode": long_decode,
         "encoder": encoder,
     }
     print(json.dumps(line), flush=True)
