@@ -242,8 +242,9 @@ CTOPK_API int ctopk_quantize_k4(const void* K, int32_t dtype, int64_t n, int32_t
  * (candidates per head), and optionally rescored [n_kv_heads] int32 (full-width
  * rows read per KV head, counted once per block of up to 8 query heads) and
  * bounds [n_q_heads, n] float2 (each score interval (lo, hi)).  workspace:
- * NULL (a cached per-device buffer) or 256-byte aligned with at least
- * ctopk_k4_workspace_bytes(...) bytes.
+ * NULL (the cached per-device buffer ctopk_certify uses, with the same caveat:
+ * calls on different streams of one device race) or 256-byte aligned with at
+ * least ctopk_k4_workspace_bytes(...) bytes.
  */
 typedef struct {
   const void* q;
