@@ -466,6 +466,8 @@ int ctopk_quantize_k4(const void* K, int32_t dtype, int64_t n, int32_t d, int32_
   if (rc != CTOPK_OK) return rc;
   if (!aligned(K4, 4) || !aligned(kscale, 4) || !aligned(kres, 4))
     return fail(CTOPK_ERR_ALIGN, "K4, kscale and kres must be 4-byte aligned");
+  if (static_cast<int64_t>(n_kv_heads) * n > (int64_t{1} << 34))  // the copy's grid is rows / 16 blocks
+    return fail(CTOPK_ERR_UNSUPPORTED, "n_kv_heads * n above 2^34 is not supported by the copy");
   rc = hip_check(ctopk::launch_quantize_k4(K, dtype, d, static_cast<int64_t>(n_kv_heads) * n, K4,
                                            kscale, kres, st),
                  "quantize launch");

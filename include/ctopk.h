@@ -220,7 +220,8 @@ CTOPK_API int ctopk_validate(const ctopk_args* a);
  * kres [n_kv_heads, n] >= ||k - a c||_2 (rounded up).  A zero key gets a = 0
  * and codes 0.  Enqueued on `stream`; the caller owns every buffer and may
  * keep the copy for any later ctopk_candidates_k4 call on the same K.
- * Returns CTOPK_ERR_NULL / _SHAPE / _UNSUPPORTED / _ALIGN on bad arguments.
+ * n_kv_heads * n must be at most 2^34.  Returns CTOPK_ERR_NULL / _SHAPE /
+ * _UNSUPPORTED / _ALIGN on bad arguments.
  */
 CTOPK_API int ctopk_quantize_k4(const void* K, int32_t dtype, int64_t n, int32_t d,
                                 int32_t n_kv_heads, uint8_t* K4, float* kscale, float* kres,

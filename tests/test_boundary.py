@@ -286,3 +286,5 @@ def test_k4_entry_points_reject_before_any_gpu_call(lib):
                                  vp(A16), None) == cb.CTOPK_ERR_ALIGN
     assert lib.ctopk_quantize_k4(vp(A16), 5, 4096, 128, 8, vp(A16), vp(A16), vp(A16),
                                  None) == cb.CTOPK_ERR_UNSUPPORTED
+    assert lib.ctopk_quantize_k4(vp(A16), cb.CTOPK_BF16, 1 << 30, 128, 32, vp(A16), vp(A16),
+                                 vp(A16), None) == cb.CTOPK_ERR_UNSUPPORTED
