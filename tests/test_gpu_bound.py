@@ -95,7 +95,7 @@ def test_bound_gqa_decode_full(ct):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
 def test_bound_fp32(ct, d, G):
     wl = workloads.gqa_decode(n=3001, n_q=2 * G, n_kv=2, d=d, planted=5, temp_range=(0.5, 2.0))
     wl = dict(wl, q=workloads.bf16_to_f32(wl["q"]), K=workloads.bf16_to_f32(wl["K"]),
@@ -130,3 +130,9 @@ def test_bound_equal_scores(ct):
 
 def test_bound_with_certificate(ct):
     check_bound(ct, workloads.gqa_decode(n=6000), 0.05, "with output error", certificate=True)
+
+
+@pytest.mark.parametrize("eps", [1e-4, 0.9])
+def test_bound_extreme_eps(ct, eps):
+    check_bound(ct, workloads.gqa_decode(n=3000, n_q=16, n_kv=1, temp_range=(0.5, 8.0)), eps,
+                f"eps={eps}, group of 16")
