@@ -358,6 +358,10 @@ def k4_leg(lib, ct, torch, hip, Q, Kd, T_cut, T_top, steps):
                       "mean_candidates": round(float(np.mean(cnt)), 1),
                       "rescored_fraction": round(float(np.mean(fr)), 4),
                       "k4_scan_gbps": round(scan_gbps, 1),
+                      "k4_scan_roofline": {"bound": "hbm", "achieved": round(scan_gbps, 1),
+                                           "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                           "frac": round(scan_gbps / PEAK_HBM_GBPS, 4),
+                                           "traffic": read_traffic("k4_scan")},
                       "bytes_per_call": round(out["scan_bytes_per_call"] + float(np.mean(fr)) * n_kv * n * d * 2)}
     hip.destroy(ev0)
     hip.destroy(ev1)
