@@ -445,6 +445,65 @@ def long_leg(lib, ct, torch, hip, steps, eps):
             "mean_k_over_n": round(kmean, 4)}
 
 
+def logits_leg(lib, ct, torch, hip, steps, eps):
+    """The select and output on given logits (ctopk_certify_logits): 1024 rows
+    of sigma = 2 Gaussian fp32 logits, n = 65536, one shared fp32 V [n, 64]
+    (256 MiB of logits, above the 256 MB Infinity Cache).  Per-call and
+    per-kernel times, rows/s and the logits' read rate."""
+    wl = workloads.logit_sweep(2.0, 65536)
+    rows, n, dv = wl["rows"], wl["n"], wl["dv"]
+    L = torch.from_numpy(wl["logits"]).cuda()
+    V = torch.from_numpy(wl["V"]).cuda()
+    del wl
+    out = torch.empty((rows, dv), dtype=torch.float32, device="cuda")
+    k_eps = torch.empty(rows, dtype=torch.int32, device="cuda")
+    tau = torch.empty(rows, dtype=torch.float64, device="cuda")
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    vp = ctypes.c_void_p
+    argv = (vp(L.data_ptr()), vp(V.data_ptr()), ct.CTOPK_F32, n, dv, rows, 1, float(eps), None, 0,
+            sptr, vp(out.data_ptr()), vp(k_eps.data_ptr()), vp(tau.data_ptr()), None, None)
+
+    def step():
+        rc = lib.ctopk_certify_logits(*argv)
+        if rc != 0:
+            raise RuntimeError(ct.ctopk_last_error_string())
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    kmean = float(k_eps.double().mean().item()) / n
+    e0, e1 = hip.event(), hip.event()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e0), sptr)
+    for _ in range(steps):
+        step()
+    hip.lib.hipEventRecord(ctypes.c_void_p(e1), sptr)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    names = ("resolve", "vsum", "finalize")
+    n_ev = 2 * len(names)
+    evs = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    arrs = [(ctypes.c_void_p * n_ev)(*[ctypes.c_void_p(e) for e in row]) for row in evs]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        lib.ctopk_record_kernel_events(arrs[i], n_ev)
+        step()
+    torch.cuda.synchronize()
+    per = np.array([[hip.elapsed_ms(row[2 * j], row[2 * j + 1]) for j in range(len(names))]
+                    for row in evs])
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    kern = {nm: round(float(per[:, j].mean()) * 1e3, 3) for j, nm in enumerate(names)}
+    lbytes = rows * n * 4
+    return {"workload": "logit sweep: 1024 rows x 65536 fp32 logits, sigma=2, shared fp32 V [65536, 64]",
+            "eps": eps, "steps": steps, "us_per_call": round(us, 3),
+            "rows_per_s": round(rows / (us * 1e-6), 1), "kernel_us": kern,
+            "select_logit_gbps": round(lbytes / (kern["resolve"] * 1e-6) / 1e9, 1),
+            "mean_k_over_n": round(kmean, 4)}
+
+
 def encoder_leg(lib, ct, torch, hip, steps, eps, sets=16):
     """All-queries (encoder-shaped) workload: batch 8, 12 heads, 512 queries and
     512 keys per head, d = 64, bf16, per-head temperature; every query row of a
@@ -529,6 +588,8 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--bound-steps", type=int, default=1000,
                     help="calls of the blockwise-bound leg on the decode workload; 0 skips it")
+    ap.add_argument("--logits-steps", type=int, default=20,
+                    help="calls of the given-logits leg (1024 x 65536 fp32); 0 skips it")
     ap.add_argument("--long-steps", type=int, default=40,
                     help="calls of the long-context decode leg (n = 131072, 1 GiB of K); 0 skips it")
     ap.add_argument("--k4-steps", type=int, default=500,
@@ -685,6 +746,10 @@ def main():
     if args.bound_steps > 0:
         bound = bound_leg(lib, ct, torch, hip, Q, Kd, Vd, args.bound_steps, eps)
 
+    logits = None
+    if args.logits_steps > 0:
+        logits = logits_leg(lib, ct, torch, hip, args.logits_steps, eps)
+
     long_decode = None
     if args.long_steps > 0:
         long_decode = long_leg(lib, ct, torch, hip, args.long_steps, eps)
@@ -730,6 +795,7 @@ def main():
         "bound_certificate": bound,
         "k4_candidates": k4,
         "long_decode": long_decode,
+        "logits_select": logits,
         "encoder": encoder,
     }
     print(json.dumps(line), flush=True)
