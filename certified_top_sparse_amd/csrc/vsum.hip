@@ -328,11 +328,149 @@ hipError_t launch_t(const float* scores, int64_t n, int rows, int n_v, const voi
                 out, dense, err);
 }
 
+
+// Many query rows per V (a group of at least kGemmRows rows, as on given
+// logits with one shared V): the head sums of a chunk of keys are the product
+// W V of the masked weight matrix (w_ri = exp(s_ri - m_r) on the head, else
+// 0) with V, so a block of 64 rows runs it on MFMA (v_mfma_f32_16x16x4f32:
+// fp32 operands and sums) instead of re-reading V once per 8 rows.  Layouts:
+// A[i][k] in lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane
+// j + 16 (i / 4), element i % 4.  In step s of a 64-key super-step, k slot
+// kk holds key 16 kk + s, so each lane reads 16 consecutive logits of its
+// row; the super-step's V rows are staged in LDS at row 4 s + kk, with a
+// stride of D + 16 floats so the two 32-lane halves of a read hit disjoint
+// banks.
+constexpr int kGemmRows = 64;
+constexpr int kGemmKeys = 64;
+constexpr int kGemmPad = 16;
+
+typedef float gemm_f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vsum_gemm_kernel(
+    const float* __restrict__ scores, int64_t n, int G, const T* __restrict__ V,
+    const RowSel* __restrict__ rs, float* __restrict__ part, int nchunk, int64_t chunk_keys) {
+  constexpr int CT = D / 16;  // 16-column tiles
+  constexpr int EPL = VSlice<T>::kElems;
+  constexpr int VLOADS = kGemmKeys * D / EPL / 256;  // 16-byte V loads per thread and super-step
+  static_assert(VLOADS * 256 * EPL == kGemmKeys * D, "whole V tile per super-step");
+  __shared__ float s_v[kGemmKeys][D + kGemmPad];
+
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  const int chunk = blockIdx.x;
+  const int kvh = blockIdx.z;
+  const int li = lane & 15;   // A row / B column within the tile
+  const int kk = lane >> 4;   // k slot
+  const int rloc = static_cast<int>(blockIdx.y) * kGemmRows + 16 * wave + li;  // row in group
+  const bool row_live = rloc < G;
+  const int row = kvh * G + min(rloc, G - 1);
+  const RowSel sel = rs[row];
+  const float* srow = scores + static_cast<size_t>(row) * static_cast<size_t>(n);
+  const T* Vb = V + static_cast<size_t>(kvh) * static_cast<size_t>(n) * D;
+  const int64_t k_begin = static_cast<int64_t>(chunk) * chunk_keys;
+  const int64_t k_end = min(n, k_begin + chunk_keys);
+  const bool vec_rows = (n & 3) == 0;
+
+  gemm_f32x4_t acc[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) acc[c] = gemm_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float wsum = 0.0f;
+
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += kGemmKeys) {
+    // V rows k0 .. k0 + 63 (past n: row n - 1, weighted 0) into LDS.
+    uint4 vv[VLOADS];
+#pragma unroll
+    for (int u = 0; u < VLOADS; ++u) {
+      const int f = (u * 256 + t) * EPL;  // flat element index in the tile
+      const int64_t key = min(k0 + f / D, n - 1);
+      vv[u] = *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(key) * D + f % D);
+    }
+    // This lane's 16 logits: keys k0 + 16 kk .. + 15 of its row (16-byte loads
+    // when rows are 16-byte aligned, that is n % 4 == 0).
+    float sv[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int64_t key = k0 + 16 * kk + 4 * q4;
+      if (vec_rows && key + 3 < n) {
+        const float4 x = *reinterpret_cast<const float4*>(srow + key);
+        sv[4 * q4] = x.x;
+        sv[4 * q4 + 1] = x.y;
+        sv[4 * q4 + 2] = x.z;
+        sv[4 * q4 + 3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * q4 + e] = srow[min(key + e, n - 1)];
+      }
+    }
+    float wv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t key = k0 + 16 * kk + e;
+      const bool kept = row_live && key < k_end &&
+                        key64(sv[e], static_cast<uint32_t>(key)) >= sel.thr;
+      wv[e] = kept ? weight(sv[e], sel.m) : 0.0f;
+      wsum += wv[e];
+    }
+    __syncthreads();  // the previous super-step's reads of s_v are done
+#pragma unroll
+    for (int u = 0; u < VLOADS; ++u) {
+      const int f = (u * 256 + t) * EPL;
+      const int key = f / D;  // 16 kk' + s' -> LDS row 4 s' + kk'
+      float x[EPL];
+      VSlice<T>::load(vv[u], x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_v[4 * (key & 15) + (key >> 4)][f % D + e] = x[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[s], s_v[4 * s + kk][16 * c + li], acc[c],
+                                                      0, 0, 0);
+    }
+  }
+
+  // Partials: lane (j, q) holds rows 4 q + e of the wave's 16, column 16 c + j.
+  const int q = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = static_cast<int>(blockIdx.y) * kGemmRows + 16 * wave + 4 * q + e;
+    if (r < G) {
+      float* p = part + (static_cast<size_t>(kvh * G + r) * nchunk + chunk) * (D + 1);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) p[16 * c + li] = acc[c][e];
+    }
+  }
+  wsum += __shfl_xor(wsum, 16, 64);
+  wsum += __shfl_xor(wsum, 32, 64);
+  if (kk == 0 && row_live)
+    part[(static_cast<size_t>(row) * nchunk + chunk) * (D + 1) + D] = wsum;
+}
+
+template <typename T, int D>
+hipError_t launch_gemm(const float* scores, int64_t n, int rows, int n_v, const void* V,
+                       const RowSel* rs, float* part, int nchunk, float* out, hipStream_t st) {
+  const int G = rows / n_v;
+  // chunks past the keys (ck rounds up) write zero partials
+  const int64_t ck = ceil_div(ceil_div(n, nchunk), kGemmKeys) * kGemmKeys;
+  dim3 grid(nchunk, static_cast<unsigned>(ceil_div(G, kGemmRows)), n_v);
+  const hipError_t e = launch(vsum_gemm_kernel<T, D>, grid, dim3(256), 0, st, scores, n, G,
+                              static_cast<const T*>(V), rs, part, nchunk, ck);
+  if (e != hipSuccess) return e;
+  return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, static_cast<const float*>(part),
+                nchunk, D, 1, out, static_cast<float*>(nullptr), static_cast<double*>(nullptr));
+}
+
 template <typename T, int D>
 hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const void* V,
                     const RowSel* rs, float* part, int nchunk, float* out, float* dense,
                     double* err, hipStream_t st) {
   const int G = rows / n_v;
+  if (G >= kGemmRows && dense == nullptr && err == nullptr)
+    return launch_gemm<T, D>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
   if (G == 1)
     return launch_t<T, D, 1>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
   if (G == 2)
@@ -426,6 +564,16 @@ int stream_nchunk(int64_t n, int groups, int blocks) {
 }
 
 int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
+  const int G = rows / n_v;
+  if (G >= kGemmRows) {
+    // The MFMA stream: about two blocks per compute unit over the row tiles,
+    // chunks of at least 512 keys (fp32 sums within a chunk stay short).
+    const int64_t tiles = static_cast<int64_t>(n_v) * ceil_div(G, kGemmRows);
+    int64_t want = ceil_div(2 * kNumCUs, tiles);
+    const int64_t most = ceil_div(n, 512);
+    if (want > most) want = most;
+    return static_cast<int>(want < 1 ? 1 : want);
+  }
   // Blocks per group: about one block per compute unit in total (measured
   // fastest on MI355X: each block streams several tiles and amortises its
   // reduction epilogue), and never more blocks than tiles.

@@ -379,6 +379,29 @@ def test_bf16_values_on_logits_path(ct):
     _logits_case(ct, L, V, 0.01, "bf16 V, 4 value heads", n_v=4, out_rtol=1e-5)
 
 
+@pytest.mark.parametrize("seq", [600, 1000])
+def test_all_queries_beyond_the_encoder(ct, seq):
+    # every query of a head against more than 512 keys: the general path with
+    # groups of `seq` rows per KV head (the MFMA value stream); sampled rows
+    wl = workloads.encoder(batch=1, heads=2, seq=seq)
+    rows = np.concatenate([np.arange(0, 2 * seq, 7), [2 * seq - 1]])
+    check_decode(ct, wl, 0.01, f"all queries, {seq} keys", rows=rows)
+
+
+@pytest.mark.parametrize("dv,vdt", [(64, "f32"), (128, "bf16"), (128, "f32")])
+def test_logits_wide_groups(ct, dv, vdt):
+    # groups of 100 rows per V take the MFMA value stream: ragged row tiles,
+    # an odd key count (no 16-byte logit loads) and both value types
+    rng = np.random.default_rng(77)
+    R, n, n_v = 200, 4097, 2
+    L = (rng.standard_normal((R, n)) * 2.0).astype(np.float32)
+    V = rng.standard_normal((n_v, n, dv)).astype(np.float32)
+    if vdt == "bf16":
+        V = workloads.bf16_rne(V)
+    _logits_case(ct, L, V, 0.05, f"wide groups dv={dv} {vdt}", n_v=n_v,
+                 out_rtol=OUT_RTOL_F32 if vdt == "f32" else OUT_RTOL_BF16)
+
+
 # ---------------------------------------------------------------------------
 # logit sweep workloads
 # ---------------------------------------------------------------------------
