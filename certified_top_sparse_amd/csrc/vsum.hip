@@ -337,12 +337,12 @@ hipError_t launch_t(const float* scores, int64_t n, int rows, int n_v, const voi
 // A[i][k] in lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane
 // j + 16 (i / 4), element i % 4.  In step s of a 64-key super-step, k slot
 // kk holds key 16 kk + s, so each lane reads 16 consecutive logits of its
-// row; the super-step's V rows are staged in LDS at row 4 s + kk, with a
-// stride of D + 16 floats so the two 32-lane halves of a read hit disjoint
-// banks.
+// row; the super-step's V rows are staged in LDS at row 4 s + kk with the
+// D / 16 values a lane multiplies in one step side by side ([col % 16][col /
+// 16]), so a step's B operands are one or two 16-byte reads per lane, the
+// wave reading 1 KB contiguous.
 constexpr int kGemmRows = 64;
 constexpr int kGemmKeys = 64;
-constexpr int kGemmPad = 16;
 
 typedef float gemm_f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256) void vsum_gemm_kernel(
   constexpr int EPL = VSlice<T>::kElems;
   constexpr int VLOADS = kGemmKeys * D / EPL / 256;  // 16-byte V loads per thread and super-step
   static_assert(VLOADS * 256 * EPL == kGemmKeys * D, "whole V tile per super-step");
-  __shared__ float s_v[kGemmKeys][D + kGemmPad];
+  __shared__ float s_v[kGemmKeys][16][CT];
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -421,15 +421,26 @@ __global__ __launch_bounds__(256) void vsum_gemm_kernel(
       float x[EPL];
       VSlice<T>::load(vv[u], x);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_v[4 * (key & 15) + (key >> 4)][f % D + e] = x[e];
+      for (int e = 0; e < EPL; ++e) {
+        const int col = f % D + e;
+        s_v[4 * (key & 15) + (key >> 4)][col & 15][col >> 4] = x[e];
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
+      float b[CT];
+#pragma unroll
+      for (int c4 = 0; c4 < CT; c4 += 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(&s_v[4 * s + kk][li][c4]);
+        b[c4] = v4.x;
+        b[c4 + 1] = v4.y;
+        b[c4 + 2] = v4.z;
+        b[c4 + 3] = v4.w;
+      }
 #pragma unroll
       for (int c = 0; c < CT; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[s], s_v[4 * s + kk][16 * c + li], acc[c],
-                                                      0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[s], b[c], acc[c], 0, 0, 0);
     }
   }
 
