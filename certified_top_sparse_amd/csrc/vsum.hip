@@ -577,10 +577,10 @@ int stream_nchunk(int64_t n, int groups, int blocks) {
 int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
   const int G = rows / n_v;
   if (G >= kGemmRows) {
-    // The MFMA stream: about two blocks per compute unit over the row tiles,
+    // The MFMA stream: about four blocks per compute unit over the row tiles,
     // chunks of at least 512 keys (fp32 sums within a chunk stay short).
     const int64_t tiles = static_cast<int64_t>(n_v) * ceil_div(G, kGemmRows);
-    int64_t want = ceil_div(2 * kNumCUs, tiles);
+    int64_t want = ceil_div(4 * kNumCUs, tiles);
     const int64_t most = ceil_div(n, 512);
     if (want > most) want = most;
     return static_cast<int>(want < 1 ? 1 : want);
