@@ -136,3 +136,15 @@ def test_bound_with_certificate(ct):
 def test_bound_extreme_eps(ct, eps):
     check_bound(ct, workloads.gqa_decode(n=3000, n_q=16, n_kv=1, temp_range=(0.5, 8.0)), eps,
                 f"eps={eps}, group of 16")
+
+
+def test_bound_is_deterministic(ct):
+    # integer atomics and fixed-order sums: two calls agree bit for bit
+    wl = workloads.gqa_decode(n=9000, temp_range=(0.5, 4.0))
+    _say("bound determinism n=9000")
+    args = (dev(wl["q"]), dev(wl["K"]), dev(wl["V"]), 0.05)
+    a = ct.ctopk_certify_ex(*args, head_scale=dev(wl["head_scale"]), want_mask=True, bound=True)
+    b = ct.ctopk_certify_ex(*args, head_scale=dev(wl["head_scale"]), want_mask=True, bound=True)
+    torch.cuda.synchronize()
+    for key in ("out", "k_eps", "tau", "sel_mask"):
+        assert torch.equal(a[key], b[key]), key

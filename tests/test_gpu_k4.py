@@ -195,3 +195,18 @@ def test_candidates_caller_workspace_and_repeat(ct):
     b = ct.ctopk_candidates_k4(q, K, K4, ks, kr, T)
     torch.cuda.synchronize()
     assert torch.equal(a["sel_mask"], b["sel_mask"]) and torch.equal(a["count"], b["count"])
+
+
+def test_candidates_are_deterministic(ct):
+    wl = workloads.gqa_decode(n=9000, n_q=16, n_kv=2)
+    _say("candidates determinism n=9000")
+    q, K = dev(wl["q"]), dev(wl["K"])
+    K4, ks, kr = ct.ctopk_quantize_k4(K)
+    K4b, ksb, krb = ct.ctopk_quantize_k4(K)
+    T = dev(np.linspace(-1.0, 2.0, 16).astype(np.float32))
+    a = ct.ctopk_candidates_k4(q, K, K4, ks, kr, T, want_bounds=True)
+    b = ct.ctopk_candidates_k4(q, K, K4b, ksb, krb, T, want_bounds=True)
+    torch.cuda.synchronize()
+    assert torch.equal(K4, K4b) and torch.equal(ks, ksb) and torch.equal(kr, krb)
+    for key in ("sel_mask", "count", "rescored", "bounds"):
+        assert torch.equal(a[key], b[key]), key

@@ -402,6 +402,17 @@ def test_logits_wide_groups(ct, dv, vdt):
                  out_rtol=OUT_RTOL_F32 if vdt == "f32" else OUT_RTOL_BF16)
 
 
+def test_wide_group_stream_is_deterministic(ct):
+    rng = np.random.default_rng(78)
+    L = dev((rng.standard_normal((256, 3000)) * 2.0).astype(np.float32))
+    V = dev(rng.standard_normal((1, 3000, 64)).astype(np.float32))
+    _say("wide-group value stream determinism")
+    a = ct.ctopk_certify_logits(L, V, 0.02)
+    b = ct.ctopk_certify_logits(L, V, 0.02)
+    torch.cuda.synchronize()
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["k_eps"], b["k_eps"])
+
+
 # ---------------------------------------------------------------------------
 # logit sweep workloads
 # ---------------------------------------------------------------------------
