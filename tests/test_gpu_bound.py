@@ -148,3 +148,25 @@ def test_bound_is_deterministic(ct):
     torch.cuda.synchronize()
     for key in ("out", "k_eps", "tau", "sel_mask"):
         assert torch.equal(a[key], b[key]), key
+
+
+def test_bound_on_all_queries_shape(ct):
+    # all queries of a head (groups of 512 rows): the bound plan's value stream
+    # is the MFMA one for wide groups
+    wl = workloads.encoder(batch=1, heads=1)
+    check_bound(ct, wl, 0.05, "all queries, 512 keys")
+
+
+def test_bound_with_caller_workspace(ct):
+    wl = workloads.gqa_decode(n=5000)
+    _say("bound with caller workspace")
+    need = ct.ctopk_workspace_bytes(5000, 128, 32, 8)
+    raw = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + need]
+    args = (dev(wl["q"]), dev(wl["K"]), dev(wl["V"]), 0.05)
+    a = ct.ctopk_certify_ex(*args, head_scale=dev(wl["head_scale"]), workspace=ws, bound=True)
+    b = ct.ctopk_certify_ex(*args, head_scale=dev(wl["head_scale"]), bound=True)
+    torch.cuda.synchronize()
+    for key in ("out", "k_eps", "tau"):
+        assert torch.equal(a[key], b[key]), key
