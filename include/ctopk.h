@@ -119,11 +119,14 @@ typedef struct ctopk_args {
  * is the library's reading).  With the keys in consecutive blocks B of 64
  * (maxima M_B, m the row maximum), the softmax mass of the keys scoring below
  * t is at most U(t) = sum_{M_B < t} |B| e^{M_B - m} + sum_{M_B >= t} (|B| - 1)
- * e^{t - m}; the call keeps every key scoring at or above the largest fp32 t
- * with U(t) <= eps * Z.  Outputs then mean: k_eps = number of keys kept (at
- * least the minimal k), tau = U(t) / Z (an upper bound on the truncation's
- * TV, <= eps), out = the renormalised output over the kept keys, sel_mask =
- * the kept keys.  Decode shapes with n <= 262144; the score scan also
+ * e^{t - m}; the call keeps every key scoring at or above an fp32 t with
+ * U(t) <= eps * Z, the largest such t that a search of up to six rounds of 64
+ * candidates finds (on the shapes tested, the largest to fp32 resolution).
+ * Outputs then mean: k_eps = number of keys kept (at least the minimal k),
+ * tau = U(t) / Z with the block masses rounded up (an upper bound on the
+ * truncation's TV, <= eps), out = the renormalised output over the kept keys,
+ * sel_mask = the kept keys.  Any shape the general path takes, with
+ * n <= 262144 (the encoder-shaped fused path is not used); the score scan also
  * records each block's softmax mass, from which Z follows, and no key-by-key
  * select runs.
  */
