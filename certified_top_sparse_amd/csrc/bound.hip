@@ -66,16 +66,6 @@ struct BoundShared {
   int list[kBoundMaxTiles];
 };
 
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const uint32_t lo = static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xFFFFFFFFu), CTRL, 0xF, 0xF, false));
-  const uint32_t hi = static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xF, 0xF, false));
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-}
-
 __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFu), l));
@@ -85,23 +75,6 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 
 __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Sum over each row of 16 lanes, in every lane of the row: quad exchanges,
-// then the mirror patterns that pair each lane with one in the other half
-// (every lane of a row ends with the bitwise-same value, a + b == b + a).
-__device__ __forceinline__ double row_sum_f64(double v) {
-  v += dpp_f64<kDppXor1>(v);
-  v += dpp_f64<kDppXor2>(v);
-  v += dpp_f64<kDppHalfMirror>(v);
-  v += dpp_f64<kDppMirror>(v);
-  return v;
-}
-
-// Sum over the 64 lanes in a fixed tree, the same value in every lane.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  v = row_sum_f64(v);
-  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32_dpp(uint32_t v) {

@@ -125,6 +125,91 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xFFFFFFFFu), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xF, 0xF, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Sum over each row of 16 lanes, in every lane of the row: quad exchanges,
+// then the mirror patterns that pair each lane with one in the other half
+// (every lane of a row ends with the bitwise-same value, a + b == b + a).
+__device__ __forceinline__ double row_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-row adds (gfx950): v_permlane16_swap exchanges rows 0 <-> 1 and
+// 2 <-> 3 of a wave between its two operands, v_permlane32_swap the two
+// 32-lane halves; each is one VALU instruction with no LDS traffic.  Given
+// the same value twice, the two results hold, in both lanes of a pair (l and
+// l ^ 16, or l and l ^ 32), that pair's two values, so their sum is the
+// bitwise-same number in both lanes.  Every lane of the wave must be active.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xrow16_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float xrow32_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ double join_f64(uint32_t hi, uint32_t lo) {
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ double xrow16_sum(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  return join_f64(ph[0], pl[0]) + join_f64(ph[1], pl[1]);
+}
+
+__device__ __forceinline__ double xrow32_sum(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return join_f64(ph[0], pl[0]) + join_f64(ph[1], pl[1]);
+}
+
+// Sum over the 64 lanes in a fixed tree, (row 0 + row 1) + (row 2 + row 3)
+// of the row sums, the same value in every lane.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  return xrow32_sum(xrow16_sum(row_sum_f64(v)));
+}
+
+// Sum over the lanes that share their position modulo S (S = 8, 16 or 32:
+// lanes l ^ 8 within a row, then across rows), in every lane, in a fixed
+// tree.  Every lane of the wave must be active.
+constexpr int kDppRowRor8 = 0x128;  // lane i <- lane (i + 8) mod 16 within each 16
+template <int S, typename A>
+__device__ __forceinline__ A stride_sum(A v) {
+  static_assert(S == 8 || S == 16 || S == 32, "lane stride");
+  if constexpr (S == 8) {
+    if constexpr (sizeof(A) == 8) {
+      v += dpp_f64<kDppRowRor8>(v);
+    } else {
+      v += dpp<kDppRowRor8>(v);
+    }
+  }
+  if constexpr (S <= 16) v = xrow16_sum(v);
+  return xrow32_sum(v);
+}
+
 // ---------------------------------------------------------------------------
 // wave64 reductions (xor butterflies)
 // ---------------------------------------------------------------------------

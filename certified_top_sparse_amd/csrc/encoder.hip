@@ -8,13 +8,15 @@
 // at most eps, tau is that mass, and the output is the softmax average of V
 // over the head, renormalised over the head.
 //
-// One workgroup = 4 wavefronts = 64 query rows of one KV head.  Per wave: 16
-// query rows; lane (r, g) = (lane % 16, lane / 16) holds row r and the keys
-// 16 t + 4 g + e (t < NT tiles, e < 4), which is the fp32 result layout of a
-// 16x16x32 bf16 MFMA computing S^T = K Q^T.  A row's scores therefore live in
-// four lanes, 4 NT registers each, and never leave registers.
+// One workgroup = 8 wavefronts = 64 query rows of one KV head: four row
+// groups of 16 rows, each row's keys split into two halves of NT / 2 tiles,
+// one wave per (row group, half).  Lane (r, g) = (lane % 16, lane / 16) of a
+// wave holds row r and the keys kh * 8 NT + 16 t + 4 g + e (t < NT / 2, e < 4),
+// which is the fp32 result layout of a 16x16x32 bf16 MFMA computing
+// S^T = K Q^T.  A row's scores therefore live in four lanes of each of two
+// waves, 2 NT registers per lane, and never leave registers.
 //
-//  1. S^T = K Q^T on MFMA; K is staged through LDS in chunks that the four
+//  1. S^T = K Q^T on MFMA; K is staged through LDS in chunks that the eight
 //     waves share.
 //  2. Per row: max and min, weights w = exp(s - max), Z; then the certified
 //     cut by a mass-weighted bin descent: fp64 LDS histograms of weight mass

@@ -196,13 +196,13 @@ __global__ __launch_bounds__(kFixThreads) void tail_fix_kernel(
     }
   }
 
-  // Workgroup sums in a fixed order, then the chunk's head partial.
+  // Workgroup sums in a fixed order, then the chunk's head partial: the row
+  // groups of a wave by cross-lane adds (every lane ends with the sum), the
+  // waves through LDS.
 #pragma unroll
-  for (int o = LPR; o < kWave; o <<= 1)
+  for (int j = 0; j < GB; ++j)
 #pragma unroll
-    for (int j = 0; j < GB; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], o, kWave);
+    for (int e = 0; e < EPL; ++e) acc[j][e] = stride_sum<LPR>(acc[j][e]);
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < GB; ++j)
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kFixThreads) void tail_fix_kernel(
   }
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
-    const double s = wave_sum(ws[j]);
+    const double s = wave_sum_f64(ws[j]);
     if (lane == 0) s_ws[wave][j] = s;
   }
   __syncthreads();
