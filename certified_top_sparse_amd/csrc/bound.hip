@@ -77,56 +77,6 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32_dpp(uint32_t v) {
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppXor1, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppXor2, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppHalfMirror, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppMirror, 0xF, 0xF, false));
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)) +
-         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)) +
-         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)) +
-         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
-}
-
-// Inclusive prefix sums across the 64 lanes with DPP: shifts by 1, 2, 4 and 8
-// within each row of 16 (lanes shifted in from outside the row add 0), then
-// each row takes the running total of the rows before it (row broadcasts of
-// lanes 15 and 31).
-constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
-constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
-  const uint32_t lo = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v));
-  const uint32_t hi = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v >> 32));
-  return (static_cast<unsigned long long>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ unsigned long long wave_incl_scan_u64_dpp(unsigned long long v) {
-  v += dpp_u64<kDppRowShr1, 0xF>(v);
-  v += dpp_u64<kDppRowShr2, 0xF>(v);
-  v += dpp_u64<kDppRowShr4, 0xF>(v);
-  v += dpp_u64<kDppRowShr8, 0xF>(v);
-  v += dpp_u64<kDppRowBcast15, 0xA>(v);
-  v += dpp_u64<kDppRowBcast31, 0xC>(v);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan_u32_dpp(uint32_t v) {
-  v += dpp_u32<kDppRowShr1, 0xF>(v);
-  v += dpp_u32<kDppRowShr2, 0xF>(v);
-  v += dpp_u32<kDppRowShr4, 0xF>(v);
-  v += dpp_u32<kDppRowShr8, 0xF>(v);
-  v += dpp_u32<kDppRowBcast15, 0xA>(v);
-  v += dpp_u32<kDppRowBcast31, 0xC>(v);
-  return v;
-}
-
 // Workgroup sum in a fixed order (each wave's sum, then the per-wave sums
 // across the lanes of one DPP row), the same value in every thread.
 __device__ double block_sum(double v, BoundShared& sh) {

@@ -210,6 +210,110 @@ __device__ __forceinline__ A stride_sum(A v) {
   return xrow32_sum(v);
 }
 
+__device__ __forceinline__ uint32_t wave_sum_u32_dpp(uint32_t v) {
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppXor1, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppXor2, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppHalfMirror, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kDppMirror, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+}
+
+// Inclusive prefix sums across the 64 lanes with DPP: shifts by 1, 2, 4 and 8
+// within each row of 16 (lanes shifted in from outside the row add 0), then
+// each row takes the running total of the rows before it (row broadcasts of
+// lanes 15 and 31).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64_dpp(unsigned long long v) {
+  v += dpp_u64<kDppRowShr1, 0xF>(v);
+  v += dpp_u64<kDppRowShr2, 0xF>(v);
+  v += dpp_u64<kDppRowShr4, 0xF>(v);
+  v += dpp_u64<kDppRowShr8, 0xF>(v);
+  v += dpp_u64<kDppRowBcast15, 0xA>(v);
+  v += dpp_u64<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32_dpp(uint32_t v) {
+  v += dpp_u32<kDppRowShr1, 0xF>(v);
+  v += dpp_u32<kDppRowShr2, 0xF>(v);
+  v += dpp_u32<kDppRowShr4, 0xF>(v);
+  v += dpp_u32<kDppRowShr8, 0xF>(v);
+  v += dpp_u32<kDppRowBcast15, 0xA>(v);
+  v += dpp_u32<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+// Inclusive prefix sum of fp64 values across the 64 lanes, in the same
+// pattern as the integer scans above (a fixed tree; lanes shifted in from
+// outside a row, and rows a broadcast skips, add +0.0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64_bc(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  return join_f64(dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(u >> 32)),
+                  dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(u)));
+}
+
+__device__ __forceinline__ double wave_incl_scan_f64_dpp(double v) {
+  v += dpp_f64_bc<kDppRowShr1, 0xF>(v);
+  v += dpp_f64_bc<kDppRowShr2, 0xF>(v);
+  v += dpp_f64_bc<kDppRowShr4, 0xF>(v);
+  v += dpp_f64_bc<kDppRowShr8, 0xF>(v);
+  v += dpp_f64_bc<kDppRowBcast15, 0xA>(v);
+  v += dpp_f64_bc<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+// Minimum and maximum of 64-bit keys over the 64 lanes, in every lane (DPP
+// within rows, then the cross-row swaps).  Every lane must be active.
+template <bool MAX>
+__device__ __forceinline__ unsigned long long pick_u64(unsigned long long a, unsigned long long b) {
+  return MAX ? (a > b ? a : b) : (a < b ? a : b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64_row(unsigned long long v) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF, false));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+template <bool MAX>
+__device__ __forceinline__ unsigned long long wave_pick_u64(unsigned long long v) {
+  v = pick_u64<MAX>(v, dpp_u64_row<kDppXor1>(v));
+  v = pick_u64<MAX>(v, dpp_u64_row<kDppXor2>(v));
+  v = pick_u64<MAX>(v, dpp_u64_row<kDppHalfMirror>(v));
+  v = pick_u64<MAX>(v, dpp_u64_row<kDppMirror>(v));
+  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  v = pick_u64<MAX>((static_cast<unsigned long long>(b[0]) << 32) | a[0],
+                    (static_cast<unsigned long long>(b[1]) << 32) | a[1]);
+  const uint32_t lo2 = static_cast<uint32_t>(v), hi2 = static_cast<uint32_t>(v >> 32);
+  const auto c = __builtin_amdgcn_permlane32_swap(lo2, lo2, false, false);
+  const auto e = __builtin_amdgcn_permlane32_swap(hi2, hi2, false, false);
+  return pick_u64<MAX>((static_cast<unsigned long long>(e[0]) << 32) | c[0],
+                       (static_cast<unsigned long long>(e[1]) << 32) | c[1]);
+}
+
 // ---------------------------------------------------------------------------
 // wave64 reductions (xor butterflies)
 // ---------------------------------------------------------------------------

@@ -140,8 +140,8 @@ __device__ void hist_wave_totals(ResolveShared& sh, int nb, bool by_mass) {
   const int b0 = 2 * t;
   const double m = (b0 < nb ? sh.hm[b0] : 0.0) + (b0 + 1 < nb ? sh.hm[b0 + 1] : 0.0);
   const uint32_t c = bin_count(sh, b0, nb, by_mass) + bin_count(sh, b0 + 1, nb, by_mass);
-  const double wm = wave_sum(m);
-  const uint32_t wc = wave_sum_u32(c);
+  const double wm = wave_sum_f64(m);
+  const uint32_t wc = wave_sum_u32_dpp(c);
   if ((t & 63) == 0) {
     sh.wd[t >> 6] = wm;
     sh.wc[t >> 6] = wc;
@@ -179,8 +179,8 @@ __device__ int select_bin(ResolveShared& sh, int nb, bool by_mass, double R, dou
     const uint32_t c1 = bin_count(sh, b0 + 1, nb, by_mass);
     const double m0 = b0 < nb ? sh.hm[b0] : 0.0;
     const double m1 = b0 + 1 < nb ? sh.hm[b0 + 1] : 0.0;
-    const double im = wave_incl_scan(m0 + m1, lane);
-    const uint32_t ic = wave_incl_scan_u32(c0 + c1, lane);
+    const double im = wave_incl_scan_f64_dpp(m0 + m1);
+    const uint32_t ic = wave_incl_scan_u32_dpp(c0 + c1);
     double em = __shfl_up(im, 1, kWave);
     uint32_t ec = __shfl_up(ic, 1, kWave);
     if (lane == 0) {
@@ -509,15 +509,10 @@ __device__ __forceinline__ void resolve_row(
         }
       }
     });
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const unsigned long long a = __shfl_xor(kmn, o, kWave);
-      const unsigned long long c = __shfl_xor(kmx, o, kWave);
-      kmn = a < kmn ? a : kmn;
-      kmx = c > kmx ? c : kmx;
-    }
+    kmn = wave_pick_u64<false>(kmn);
+    kmx = wave_pick_u64<true>(kmx);
     if (count_below) {
-      nbelow = wave_sum_u32(nbelow);
+      nbelow = wave_sum_u32_dpp(nbelow);
       if (lane == 0) sh.wc[wave] = nbelow;
     }
     if (lane == 0 && kmn <= kmx) {

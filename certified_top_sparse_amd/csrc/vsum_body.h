@@ -278,21 +278,15 @@ __device__ __forceinline__ void value_stream_block(
     hook(ln);
   }
 
-  // Workgroup sums: row groups of a wave (xor butterfly over lane / LPR), then
-  // the waves in order through LDS.
+  // Workgroup sums: row groups of a wave (lanes that share lane % LPR, by
+  // cross-lane adds), then the waves in order through LDS.
 #pragma unroll
-  for (int o = LPR; o < kWave; o <<= 1) {
+  for (int j = 0; j < GB; ++j)
 #pragma unroll
-    for (int j = 0; j < GB; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], o, kWave);
-    if constexpr (TAIL) {
-#pragma unroll
-      for (int j = 0; j < GB; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acct[j][e] += __shfl_xor(acct[j][e], o, kWave);
+    for (int e = 0; e < EPL; ++e) {
+      acc[j][e] = stride_sum<LPR>(acc[j][e]);
+      if constexpr (TAIL) acct[j][e] = stride_sum<LPR>(acct[j][e]);
     }
-  }
 #pragma unroll
   for (int o = GB; o < kWave; o <<= 1) {
     wsum += __shfl_xor(wsum, o, kWave);
