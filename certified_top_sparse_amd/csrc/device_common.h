@@ -154,37 +154,67 @@ __device__ __forceinline__ double row_sum_f64(double v) {
 // l ^ 16, or l and l ^ 32), that pair's two values, so their sum is the
 // bitwise-same number in both lanes.  Every lane of the wave must be active.
 // ---------------------------------------------------------------------------
+// The two values of the lane pair (l, l ^ X), X = 16 or 32, in both lanes
+// of the pair (the order of the two is the same in both lanes).
+template <int X>
+__device__ __forceinline__ uint2 lane_pair(uint32_t v) {
+  static_assert(X == 16 || X == 32, "cross-row pair");
+  if constexpr (X == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return make_uint2(p[0], p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return make_uint2(p[0], p[1]);
+  }
+}
+
+// The value of lane l ^ X, as __shfl_xor(v, X) for X = 16 or 32: of the
+// pair's two values the one that is not this lane's own (equal values: the
+// same number either way).
+template <int X>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const uint2 p = lane_pair<X>(v);
+  return p.x == v ? p.y : p.x;
+}
+template <int X>
+__device__ __forceinline__ int xor_lane(int v) {
+  return static_cast<int>(xor_lane<X>(static_cast<uint32_t>(v)));
+}
+template <int X>
+__device__ __forceinline__ float xor_lane(float v) {
+  return __uint_as_float(xor_lane<X>(__float_as_uint(v)));
+}
+template <int X>
+__device__ __forceinline__ double xor_lane(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = xor_lane<X>(static_cast<uint32_t>(u));
+  const uint32_t hi = xor_lane<X>(static_cast<uint32_t>(u >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
 __device__ __forceinline__ float xrow16_sum(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint2 p = lane_pair<16>(__float_as_uint(v));
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
 }
 
 __device__ __forceinline__ float xrow32_sum(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint2 p = lane_pair<32>(__float_as_uint(v));
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
 }
 
 __device__ __forceinline__ double join_f64(uint32_t hi, uint32_t lo) {
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
-__device__ __forceinline__ double xrow16_sum(double v) {
+template <int X>
+__device__ __forceinline__ double xrow_sum_f64(double v) {
   const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
-  const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-  const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-  return join_f64(ph[0], pl[0]) + join_f64(ph[1], pl[1]);
+  const uint2 pl = lane_pair<X>(static_cast<uint32_t>(u));
+  const uint2 ph = lane_pair<X>(static_cast<uint32_t>(u >> 32));
+  return join_f64(ph.x, pl.x) + join_f64(ph.y, pl.y);
 }
-
-__device__ __forceinline__ double xrow32_sum(double v) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
-  const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-  const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-  return join_f64(ph[0], pl[0]) + join_f64(ph[1], pl[1]);
-}
+__device__ __forceinline__ double xrow16_sum(double v) { return xrow_sum_f64<16>(v); }
+__device__ __forceinline__ double xrow32_sum(double v) { return xrow_sum_f64<32>(v); }
 
 // Sum over the 64 lanes in a fixed tree, (row 0 + row 1) + (row 2 + row 3)
 // of the row sums, the same value in every lane.
@@ -302,16 +332,14 @@ __device__ __forceinline__ unsigned long long wave_pick_u64(unsigned long long v
   v = pick_u64<MAX>(v, dpp_u64_row<kDppXor2>(v));
   v = pick_u64<MAX>(v, dpp_u64_row<kDppHalfMirror>(v));
   v = pick_u64<MAX>(v, dpp_u64_row<kDppMirror>(v));
-  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-  const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-  v = pick_u64<MAX>((static_cast<unsigned long long>(b[0]) << 32) | a[0],
-                    (static_cast<unsigned long long>(b[1]) << 32) | a[1]);
-  const uint32_t lo2 = static_cast<uint32_t>(v), hi2 = static_cast<uint32_t>(v >> 32);
-  const auto c = __builtin_amdgcn_permlane32_swap(lo2, lo2, false, false);
-  const auto e = __builtin_amdgcn_permlane32_swap(hi2, hi2, false, false);
-  return pick_u64<MAX>((static_cast<unsigned long long>(e[0]) << 32) | c[0],
-                       (static_cast<unsigned long long>(e[1]) << 32) | c[1]);
+  const uint2 a = lane_pair<16>(static_cast<uint32_t>(v));
+  const uint2 b = lane_pair<16>(static_cast<uint32_t>(v >> 32));
+  v = pick_u64<MAX>((static_cast<unsigned long long>(b.x) << 32) | a.x,
+                    (static_cast<unsigned long long>(b.y) << 32) | a.y);
+  const uint2 c = lane_pair<32>(static_cast<uint32_t>(v));
+  const uint2 e = lane_pair<32>(static_cast<uint32_t>(v >> 32));
+  return pick_u64<MAX>((static_cast<unsigned long long>(e.x) << 32) | c.x,
+                       (static_cast<unsigned long long>(e.y) << 32) | c.y);
 }
 
 // ---------------------------------------------------------------------------

@@ -76,22 +76,31 @@ static_assert(2 * Geo<128>::kChunk * Geo<128>::kKStride * 2 <= kEncSmem, "K stag
 static_assert(2 * 128 * (Geo<128>::kChunk + 8) * 2 <= kEncSmem, "V stage");
 static_assert(4 * 16 * 128 * 4 <= kEncSmem, "half combine");
 
-// Reductions over the four lanes (r, 0..3) of a row within one wave.
+// Reductions over the four lanes (r, 0..3) of a row within one wave (lanes
+// r + 16 g), with the cross-row swaps; every lane of the wave must be active.
+template <typename Op>
+__device__ __forceinline__ uint32_t row_reduce(uint32_t v, Op op) {
+  uint2 p = lane_pair<16>(v);
+  v = op(p.x, p.y);
+  p = lane_pair<32>(v);
+  return op(p.x, p.y);
+}
 __device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, kWave));
-  return fmaxf(v, __shfl_xor(v, 32, kWave));
+  return __uint_as_float(row_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 __device__ __forceinline__ float row_min(float v) {
-  v = fminf(v, __shfl_xor(v, 16, kWave));
-  return fminf(v, __shfl_xor(v, 32, kWave));
+  return __uint_as_float(row_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 __device__ __forceinline__ int row_sum(int v) {
-  v += __shfl_xor(v, 16, kWave);
-  return v + __shfl_xor(v, 32, kWave);
+  return static_cast<int>(
+      row_reduce(static_cast<uint32_t>(v), [](uint32_t a, uint32_t b) { return a + b; }));
 }
 __device__ __forceinline__ uint32_t row_or(uint32_t v) {
-  v |= __shfl_xor(v, 16, kWave);
-  return v | __shfl_xor(v, 32, kWave);
+  return row_reduce(v, [](uint32_t a, uint32_t b) { return a | b; });
 }
 
 // Bin of a score at one level.  Both forms are non-decreasing in s, so every
@@ -249,8 +258,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   double zp = 0.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) zp += hrow[16 * g + j];
-  const double Z = (__shfl(zp, r, kWave) + __shfl(zp, r + 16, kWave)) +
-                   (__shfl(zp, r + 32, kWave) + __shfl(zp, r + 48, kWave));
+  const double Z = xrow32_sum(xrow16_sum(zp));  // (g0 + g1) + (g2 + g3)
   const double thr = eps * Z;
 
   bool active = true;
@@ -295,8 +303,12 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       hl[j] = hrow[16 * g + j];
       S += hl[j];
     }
-    const double S0 = __shfl(S, r, kWave), S1 = __shfl(S, r + 16, kWave),
-                 S2 = __shfl(S, r + 32, kWave);
+    // the row's partial sums of the four lanes g = 0..3, in every lane
+    const double Sx = xor_lane<16>(S);               // lane g ^ 1
+    const double Sa = (g & 1) ? Sx : S;              // lane g & 2
+    const double Sb = (g & 1) ? S : Sx;              // lane (g & 2) + 1
+    const double Sa2 = xor_lane<32>(Sa), Sb2 = xor_lane<32>(Sb);
+    const double S0 = g < 2 ? Sa : Sa2, S1 = g < 2 ? Sb : Sb2, S2 = g < 2 ? Sa2 : Sa;
     double Pc = P;
     if (g > 0) Pc += S0;
     if (g > 1) Pc += S1;
@@ -311,10 +323,17 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
       Pc += hl[j];
     }
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const int ob = __shfl_xor(best, off, kWave);
-      const double oP = __shfl_xor(bestP, off, kWave);
+    {
+      const int ob = xor_lane<16>(best);
+      const double oP = xor_lane<16>(bestP);
+      if (ob > best) {
+        best = ob;
+        bestP = oP;
+      }
+    }
+    {
+      const int ob = xor_lane<32>(best);
+      const double oP = xor_lane<32>(bestP);
       if (ob > best) {
         best = ob;
         bestP = oP;
