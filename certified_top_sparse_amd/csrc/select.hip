@@ -250,13 +250,7 @@ __device__ void finish_small(ResolveShared& sh, int c, float m, double R, double
       ++nlower;
     }
   }
-  uint64_t best = (lane < c && R + lower <= epsZ) ? k : 0ull;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t other = static_cast<uint64_t>(
-        __shfl_xor(static_cast<long long>(best), o, kWave));
-    best = other > best ? other : best;
-  }
+  const uint64_t best = wave_pick_u64<true>((lane < c && R + lower <= epsZ) ? k : 0ull);
   if (lane < c && k == best) {
     sh.thr = k;
     sh.fin_R = R + lower;
@@ -284,8 +278,9 @@ __device__ float bin_floor(int b, float lo, float inv) {
     const bool ge = p == H || lin_bin(ukey_to_float(p), lo, inv) >= b;
     const uint64_t bal = __ballot(ge);  // lane 63 tests H, so never empty
     const int j = __ffsll(static_cast<long long>(bal)) - 1;  // first point at or past
-    H = __shfl(p, j, kWave);
-    L = j > 0 ? __shfl(p, j - 1, kWave) : L;
+    // j is wave-uniform: scalar lane reads
+    H = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(p), j));
+    L = j > 0 ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(p), j - 1)) : L;
   }
   return ukey_to_float(H);
 }
@@ -498,7 +493,7 @@ __device__ __forceinline__ void resolve_row(
         const int leader = __ffsll(static_cast<long long>(bal)) - 1;
         uint32_t base = 0u;
         if (lane == leader) base = atomicAdd(&sh.ncand, static_cast<uint32_t>(__popcll(bal)));
-        base = __shfl(base, leader, kWave);
+        base = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), leader));
         if (in) {
           const uint32_t slot =
               base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
