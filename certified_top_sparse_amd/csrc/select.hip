@@ -436,7 +436,7 @@ __device__ __forceinline__ void resolve_row(
   }
   __syncthreads();
 
-  // Z = total weight: wave totals (butterflies) added in wave order.
+  // Z = total weight: wave totals (fixed DPP trees) added in wave order.
   hist_wave_totals(sh, kBins, true);
   double Z = 0.0;
   for (int w = 0; w < kResolveWaves; ++w) Z += sh.wd[w];
@@ -476,18 +476,23 @@ __device__ __forceinline__ void resolve_row(
     }
     __syncthreads();
     const float f0 = sh.f0, f1 = sh.f1;
-    uint32_t nbelow = 0u;
+    uint32_t nbelow = 0u;  // wave-uniform: counted from lane masks on the scalar unit
     unsigned long long kmn = ~0ull, kmx = 0ull;
     E.for_each_all([&](int64_t i, float s, bool valid) {
-      // bitwise, not short-circuit: no branch per key
-      nbelow += (valid & (s < f0)) ? 1u : 0u;
+      // One lane mask per comparison (each a single vector compare), combined
+      // on the scalar unit; bitwise, not short-circuit: no branch per key.
+      const uint64_t mv = __builtin_amdgcn_ballot_w64(valid);
+      const uint64_t mge = __builtin_amdgcn_ballot_w64(s >= f0);
+      nbelow += static_cast<uint32_t>(__popcll(mv & __builtin_amdgcn_ballot_w64(s < f0)));
+      uint64_t bal = mv & mge & __builtin_amdgcn_ballot_w64(s < f1);
       bool in = valid & (s >= f0) & (s < f1);
       uint64_t k = 0ull;
       if constexpr (kPrefix) {
         k = key64(s, static_cast<uint32_t>(i));
-        in = in & prefix_match(k, prefix, plen);
+        const bool pm = prefix_match(k, prefix, plen);
+        in = in & pm;
+        bal &= __builtin_amdgcn_ballot_w64(pm);
       }
-      const uint64_t bal = __ballot(in);
       if (bal != 0ull) {
         if constexpr (!kPrefix) k = key64(s, static_cast<uint32_t>(i));
         const int leader = __ffsll(static_cast<long long>(bal)) - 1;
@@ -506,10 +511,7 @@ __device__ __forceinline__ void resolve_row(
     });
     kmn = wave_pick_u64<false>(kmn);
     kmx = wave_pick_u64<true>(kmx);
-    if (count_below) {
-      nbelow = wave_sum_u32_dpp(nbelow);
-      if (lane == 0) sh.wc[wave] = nbelow;
-    }
+    if (count_below && lane == 0) sh.wc[wave] = nbelow;
     if (lane == 0 && kmn <= kmx) {
       atomicMin(&sh.kmin, kmn);
       atomicMax(&sh.kmax, kmx);
