@@ -96,21 +96,6 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of L consecutive lanes (L a power of two <= 64);
-// on return every lane of a group holds the group's sum.  After the two quad
-// steps all lanes of a quad agree, so the mirror patterns (which pair each
-// lane with one in the other half) complete the 8- and 16-lane sums.
-template <int L>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (L >= 2) v += dpp<kDppXor1>(v);
-  if constexpr (L >= 4) v += dpp<kDppXor2>(v);
-  if constexpr (L >= 8) v += dpp<kDppHalfMirror>(v);
-  if constexpr (L >= 16) v += dpp<kDppMirror>(v);
-  if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
-  if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
 // Maximum over the 64 lanes, returned in every lane (DPP within rows of 16,
 // then the four row results through scalar lane reads).
 __device__ __forceinline__ float wave_max_dpp(float v) {
@@ -215,6 +200,21 @@ __device__ __forceinline__ double xrow_sum_f64(double v) {
 }
 __device__ __forceinline__ double xrow16_sum(double v) { return xrow_sum_f64<16>(v); }
 __device__ __forceinline__ double xrow32_sum(double v) { return xrow_sum_f64<32>(v); }
+
+// Sum over aligned groups of L consecutive lanes (L a power of two <= 64);
+// on return every lane of a group holds the group's sum.  After the two quad
+// steps all lanes of a quad agree, so the mirror patterns (which pair each
+// lane with one in the other half) complete the 8- and 16-lane sums.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (L >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (L >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (L >= 32) v = xrow16_sum(v);
+  if constexpr (L >= 64) v = xrow32_sum(v);
+  return v;
+}
 
 // Sum over the 64 lanes in a fixed tree, (row 0 + row 1) + (row 2 + row 3)
 // of the row sums, the same value in every lane.
@@ -340,46 +340,6 @@ __device__ __forceinline__ unsigned long long wave_pick_u64(unsigned long long v
   const uint2 e = lane_pair<32>(static_cast<uint32_t>(v >> 32));
   return pick_u64<MAX>((static_cast<unsigned long long>(e.x) << 32) | c.x,
                        (static_cast<unsigned long long>(e.y) << 32) | c.y);
-}
-
-// ---------------------------------------------------------------------------
-// wave64 reductions (xor butterflies)
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-// Inclusive prefix sums across the 64 lanes (Hillis-Steele over shuffles).
-__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    double t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
 }
 
 // Per-row scalars handed from the selection to the output kernel.

@@ -38,8 +38,8 @@ __device__ __forceinline__ float group_max(float v) {
   if constexpr (L >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
   if constexpr (L >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
   if constexpr (L >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-  if constexpr (L >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
-  if constexpr (L >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  if constexpr (L >= 32) v = fmaxf(v, xor_lane<16>(v));
+  if constexpr (L >= 64) v = fmaxf(v, xor_lane<32>(v));
   return v;
 }
 
@@ -238,12 +238,9 @@ __global__ __launch_bounds__(256) void k4_scan_kernel(
     }
   }
   // row totals over the four lane groups (lanes i, i + 16, i + 32, i + 48)
-  qs += __shfl_xor(qs, 16, 64);
-  qs += __shfl_xor(qs, 32, 64);
-  q1 += __shfl_xor(q1, 16, 64);
-  q1 += __shfl_xor(q1, 32, 64);
-  q2 += __shfl_xor(q2, 16, 64);
-  q2 += __shfl_xor(q2, 32, 64);
+  qs = xrow32_sum(xrow16_sum(qs));
+  q1 = xrow32_sum(xrow16_sum(q1));
+  q2 = xrow32_sum(xrow16_sum(q2));
 
 #pragma unroll
   for (int tt = 0; tt < kK4TilesPerWave; ++tt) {

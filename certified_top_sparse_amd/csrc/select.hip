@@ -126,7 +126,7 @@ struct ResolveShared {
 
 // Wave totals of the current histogram (nb <= kBins bins in sh.hc / sh.hm):
 // thread t holds bins 2t and 2t + 1, so wave w covers bins [128 w, 128 w + 128).
-// Every lane of a wave gets the same butterfly sum; sh.wd / sh.wc hold them.
+// Every lane of a wave gets the same fixed-tree sum; sh.wd / sh.wc hold them.
 // With by_mass the histogram holds masses only and a bin counts as non-empty
 // when its mass is positive (bins of weight-0 keys, which underflowed, lie
 // below every positive bin and never hold the cut).

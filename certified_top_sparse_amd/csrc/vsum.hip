@@ -299,7 +299,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict_
     }
   }
   if (ns == 2 && err != nullptr) {  // uniform: the whole block reduces ||mu_t - mu_h||^2
-    e2 = wave_sum(e2);
+    e2 = wave_sum_f64(e2);
     if ((t & 63) == 0) s_e2[t >> 6] = e2;
     __syncthreads();
     if (t == 0) {
@@ -455,8 +455,7 @@ __global__ __launch_bounds__(256) void vsum_gemm_kernel(
       for (int c = 0; c < CT; ++c) p[16 * c + li] = acc[c][e];
     }
   }
-  wsum += __shfl_xor(wsum, 16, 64);
-  wsum += __shfl_xor(wsum, 32, 64);
+  wsum = xrow32_sum(xrow16_sum(wsum));
   if (kk == 0 && row_live)
     part[(static_cast<size_t>(row) * nchunk + chunk) * (D + 1) + D] = wsum;
 }

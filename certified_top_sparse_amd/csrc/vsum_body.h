@@ -288,10 +288,12 @@ __device__ __forceinline__ void value_stream_block(
       if constexpr (TAIL) acct[j][e] = stride_sum<LPR>(acct[j][e]);
     }
 #pragma unroll
-  for (int o = GB; o < kWave; o <<= 1) {
+  for (int o = GB; o < 16; o <<= 1) {
     wsum += __shfl_xor(wsum, o, kWave);
     if constexpr (TAIL) wsumt += __shfl_xor(wsumt, o, kWave);
   }
+  wsum = xrow32_sum(xrow16_sum(wsum));
+  if constexpr (TAIL) wsumt = xrow32_sum(xrow16_sum(wsumt));
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < GB; ++j)
