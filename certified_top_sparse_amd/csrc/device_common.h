@@ -140,7 +140,7 @@ __device__ __forceinline__ double row_sum_f64(double v) {
 // bitwise-same number in both lanes.  Every lane of the wave must be active.
 // ---------------------------------------------------------------------------
 // The two values of the lane pair (l, l ^ X), X = 16 or 32, in both lanes
-// of the pair (the order of the two is the same in both lanes).
+// of the pair (callers use them in ways that do not depend on their order).
 template <int X>
 __device__ __forceinline__ uint2 lane_pair(uint32_t v) {
   static_assert(X == 16 || X == 32, "cross-row pair");

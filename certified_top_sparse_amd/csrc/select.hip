@@ -476,7 +476,7 @@ __device__ __forceinline__ void resolve_row(
     }
     __syncthreads();
     const float f0 = sh.f0, f1 = sh.f1;
-    uint32_t nbelow = 0u;  // wave-uniform: counted from lane masks on the scalar unit
+    uint32_t nbelow = 0u;  // counted from lane masks; lane 0 holds the wave's count
     unsigned long long kmn = ~0ull, kmx = 0ull;
     E.for_each_all([&](int64_t i, float s, bool valid) {
       // One lane mask per comparison (each a single vector compare), combined
