@@ -236,9 +236,10 @@ __device__ __forceinline__ double readlane_f64(double v, int j) {
 
 // One wave ends the search over c <= 64 keys (all in the current range): the
 // cut key is the largest whose lower candidates carry mass <= epsZ - R.
-__device__ void finish_small(ResolveShared& sh, int c, float m, double R, double epsZ) {
+__device__ void finish_small(ResolveShared& sh, const uint64_t* keys, int c, float m, double R,
+                             double epsZ) {
   const int lane = threadIdx.x & 63;
-  const uint64_t k = lane < c ? sh.small[lane] : 0ull;
+  const uint64_t k = lane < c ? keys[lane] : 0ull;
   const double w = lane < c ? static_cast<double>(weight(key64_score(k), m)) : 0.0;
   double lower = 0.0;
   uint32_t nlower = 0u;
@@ -546,6 +547,9 @@ __device__ __forceinline__ void resolve_row(
   uint32_t cnt_in = collect(true, std::false_type{});
   uint32_t ncand = min(cnt_in, static_cast<uint32_t>(kCandCap));
   bool in_lds = cnt_in <= static_cast<uint32_t>(kCandCap);
+  // The LDS list holds exactly the keys of the current range (every key of it
+  // matches the prefix) until a digit level narrows the range.
+  bool cand_exact = in_lds;
   if (in_lds) {  // skip the leading bits all candidates share
     const uint64_t diff = static_cast<uint64_t>(sh.kmin) ^ static_cast<uint64_t>(sh.kmax);
     plen = diff == 0 ? 64 : __clzll(static_cast<long long>(diff));
@@ -564,6 +568,7 @@ __device__ __forceinline__ void resolve_row(
       cnt_in = collect(false, std::true_type{});
       ncand = min(cnt_in, static_cast<uint32_t>(kCandCap));
       in_lds = true;
+      cand_exact = true;
       // Skip the leading bits all candidates share.
       const uint64_t diff = static_cast<uint64_t>(sh.kmin) ^ static_cast<uint64_t>(sh.kmax);
       const int common = diff == 0 ? 64 : __clzll(static_cast<long long>(diff));
@@ -575,18 +580,24 @@ __device__ __forceinline__ void resolve_row(
       __syncthreads();
     }
     if (in_lds && cnt_in <= static_cast<uint32_t>(kSmallCand)) {
-      // Gather the range's keys and let wave 0 finish.
-      if (t == 0) sh.nsmall = 0u;
-      __syncthreads();
-      for (uint32_t c = t; c < ncand; c += kResolveThreads) {
-        const uint64_t k = sh.cand[c];
-        if (prefix_match(k, prefix, plen)) {
-          const uint32_t slot = atomicAdd(&sh.nsmall, 1u);
-          if (slot < static_cast<uint32_t>(kSmallCand)) sh.small[slot] = k;
+      if (cand_exact) {  // the list is exactly the range: wave 0 finishes from it
+        if (wave == 0) finish_small(sh, sh.cand, static_cast<int>(ncand), m, R, epsZ);
+      } else {  // gather the range's keys from the list, then wave 0 finishes
+        if (t == 0) sh.nsmall = 0u;
+        __syncthreads();
+        for (uint32_t c = t; c < ncand; c += kResolveThreads) {
+          const uint64_t k = sh.cand[c];
+          if (prefix_match(k, prefix, plen)) {
+            const uint32_t slot = atomicAdd(&sh.nsmall, 1u);
+            if (slot < static_cast<uint32_t>(kSmallCand)) sh.small[slot] = k;
+          }
         }
+        __syncthreads();
+        if (wave == 0)
+          finish_small(sh, sh.small,
+                       static_cast<int>(min(sh.nsmall, static_cast<uint32_t>(kSmallCand))), m, R,
+                       epsZ);
       }
-      __syncthreads();
-      if (wave == 0) finish_small(sh, static_cast<int>(min(sh.nsmall, static_cast<uint32_t>(kSmallCand))), m, R, epsZ);
       __syncthreads();
       R = sh.fin_R;
       below += sh.fin_below;
@@ -637,6 +648,7 @@ __device__ __forceinline__ void resolve_row(
     below += C;
     prefix = (prefix << wdt) | static_cast<uint64_t>(bs);
     plen += wdt;
+    cand_exact = false;  // the list may now hold keys outside the narrowed range
     __syncthreads();
   }
   if (!done) {
