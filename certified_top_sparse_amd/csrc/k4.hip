@@ -1,9 +1,11 @@
-// 4-bit key copy with deterministic score bounds, shared across a GQA group,
-// and exact candidate generation from it ("Certified Sparse Attention via
-// Perturbed Retrieval", arXiv 2610.24991, Abstract: the scan generates the
-// candidates exactly while reading every key; the paperfoot.com page on it,
-// "Limitations and Discussion": the 4-bit scan is a fixed share of the bytes
-// of dense attention).  The pages print no formula; this library's reading:
+// 4-bit key copy and exact candidate generation from it.  Source: the page
+// "Certified Sparse Attention via Perturbed Retrieval" (arXiv 2610.24991),
+// Abstract -- its method passes over every key once in a 4-bit form whose
+// score error is bounded deterministically, one pass serving all query heads
+// of a grouped-query group, and recovers the exact candidate set; the
+// paperfoot.com page on it ("Limitations and Discussion") gives that pass as a
+// fixed fraction of dense attention's bytes.  Neither page prints a formula;
+// this library's reading:
 //
 //   copy     per key: a = amax / 7 and codes c = clamp(rint(k / a), -7, 7) in
 //            fp32 (two's-complement nibbles, element 2j in the low half of

@@ -209,11 +209,12 @@ CTOPK_API size_t ctopk_logits_workspace_bytes(int64_t n, int32_t dv, int32_t row
 CTOPK_API int ctopk_validate(const ctopk_args* a);
 
 /*
- * 4-bit key copy and exact candidate generation ("Certified Sparse Attention
- * via Perturbed Retrieval", arXiv 2610.24991, Abstract: a 4-bit scan with
- * deterministic bounds, shared across a GQA group, generates candidates
- * exactly while reading every key; the page prints no formula, so the copy
- * and the bound below are the library's reading).
+ * 4-bit key copy and exact candidate generation.  The Abstract of
+ * "Certified Sparse Attention via Perturbed Retrieval" (arXiv 2610.24991)
+ * describes one pass over all keys in a 4-bit form, with a deterministic
+ * bound on each score's error and one pass per grouped-query group, that
+ * yields the exact candidate set; it gives no formula, so the copy and the
+ * bound below are this library's reading.
  *
  * ctopk_quantize_k4 -- builds the copy of K [n_kv_heads, n, d] (dtype bf16 or
  * fp32, d 64 or 128, 16-byte aligned): per key a = amax / 7 (fp32, rounded to

@@ -42,10 +42,10 @@ Readings where the page leaves a step open:
 
 4-bit key copy and score bounds.  A second page ("Certified Sparse
 Attention via Perturbed Retrieval", arXiv 2610.24991: its Abstract, and the
-"Limitations and Discussion" figure quoted on the paperfoot.com page) names a
-4-bit key scan with deterministic score bounds, shared across a GQA group,
-that generates candidates exactly while reading every key, and prints no
-formula.  Readings taken:
+"Limitations and Discussion" figure quoted on the paperfoot.com page)
+describes a pass over all keys in a 4-bit form, with a deterministic bound on
+each score's error and one pass per grouped-query group, from which the exact
+candidate set follows; it gives no formula.  Readings taken:
 
 * each key k_i (a row of d values) gets a scale a_i = amax_i / 7 and codes
   c_ij = clamp(rint(k_ij / a_i), -7, 7), computed in float32 as written (the
@@ -422,10 +422,8 @@ def certify_bound(S, V, eps: float, row_to_v=None, block: int = BOUND_BLOCK):
 
 
 # ---------------------------------------------------------------------------
-# 4-bit key copy with deterministic score bounds ("Certified Sparse Attention
-# via Perturbed Retrieval", arXiv 2610.24991, Abstract: a 4-bit scan with
-# deterministic bounds shared across a GQA group generates the candidates
-# exactly but reads every key)
+# 4-bit key copy with deterministic score bounds (reading of the Abstract of
+# "Certified Sparse Attention via Perturbed Retrieval", arXiv 2610.24991)
 # ---------------------------------------------------------------------------
 K4_LEVEL = 7  # codes in [-7, 7]
 

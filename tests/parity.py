@@ -92,3 +92,61 @@ def score_band(q64: np.ndarray, K64: np.ndarray, scale: float, d: int) -> float:
     (a loose Higham-style bound)."""
     mag = np.abs(K64) @ np.abs(q64)
     return float(4.0 * d * 2.0 ** -24 * abs(scale) * mag.max())
+
+
+def check_topk_properties(gpu: dict, S: np.ndarray, eps: float, V64=None, row_to_v=None,
+                          out_rtol=None, label=""):
+    """Sort-free check, on every row of S (fp64 scores that the device used
+    exactly, e.g. given fp32 logits), that the device's (k_eps, tau, sel_mask)
+    is the certified minimal Top-k: the mask holds k_eps keys and is a top set
+    in the order (score descending, index ascending among equal scores); its
+    dropped mass T equals tau to TAU_ATOL and is <= eps; putting back the last
+    kept key would exceed eps (T + P_last > eps), so no smaller k qualifies.
+    These three facts determine k_eps and the head uniquely, so they are the
+    definition restated without a sort.  Rows within 1e-6 eps of the boundary
+    on either side are counted, not failed.  With V64, out must equal the
+    renormalised output over the device's own head to out_rtol.  Returns a
+    report dict."""
+    S = np.asarray(S, dtype=np.float64)
+    R, n = S.shape
+    k = np.asarray(gpu["k_eps"]).astype(np.int64)
+    mask = np.asarray(gpu["sel_mask"], dtype=bool)
+    assert mask.shape == (R, n), (mask.shape, S.shape)
+    assert (mask.sum(1) == k).all(), f"{label}: mask popcount differs from k_eps"
+    assert (k >= 1).all() and (k <= n).all(), f"{label}: k_eps out of range"
+    m = S.max(1, keepdims=True)
+    w = np.exp(S - m)
+    Z = w.sum(1)
+    T = np.where(mask, 0.0, w).sum(1) / Z
+    smin = np.where(mask, S, np.inf).min(1)
+    dmax = np.where(mask, -np.inf, S).max(1)
+    idx = np.arange(n)[None, :]
+    at_min = S == smin[:, None]
+    kept_tie_last = np.where(mask & at_min, idx, -1).max(1)
+    drop_tie_first = np.where(~mask & at_min, idx, n).min(1)
+    top = (dmax < smin) | ((dmax == smin) & (drop_tie_first > kept_tie_last))
+    assert top.all(), f"{label}: device head is not a top set on rows {np.nonzero(~top)[0][:10]}"
+    T_prev = T + np.exp(smin - m[:, 0]) / Z
+    band = 1e-6 * eps
+    near = (np.abs(T - eps) <= band) | (np.abs(T_prev - eps) <= band)
+    bad = ~near & ~((T <= eps) & (T_prev > eps))
+    assert not bad.any(), (
+        f"{label}: not the minimal certified k on rows {np.nonzero(bad)[0][:10]}: "
+        f"T={T[bad][:5]} T_prev={T_prev[bad][:5]}")
+    tdiff = np.abs(np.asarray(gpu["tau"], dtype=np.float64) - T)
+    assert (tdiff <= TAU_ATOL).all(), f"{label}: tau off by {tdiff.max():.3e}"
+    rep = {"label": label, "rows": int(R), "near_boundary": int(near.sum()),
+           "tau_max_abs_err": float(tdiff.max())}
+    if V64 is not None:
+        if row_to_v is None:
+            row_to_v = np.zeros(R, dtype=np.int64)
+        wh = np.where(mask, w, 0.0)
+        o = np.empty((R, V64.shape[-1]))
+        for g in np.unique(row_to_v):
+            sel = row_to_v == g
+            o[sel] = wh[sel] @ V64[g]
+        o /= wh.sum(1)[:, None]
+        err = rel_l2(gpu["out"], o)
+        assert (err <= out_rtol).all(), f"{label}: out rel L2 {err.max():.3e} on its own head"
+        rep["out_max_rel_l2_own_head"] = float(err.max())
+    return rep

@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import workloads
-from parity import (OUT_RTOL_BF16, OUT_RTOL_F32, compare, rel_l2, score_band, unpack_mask)
+from parity import (OUT_RTOL_BF16, OUT_RTOL_F32, check_topk_properties, compare, rel_l2,
+                    score_band, unpack_mask)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -414,46 +415,98 @@ def test_wide_group_stream_is_deterministic(ct):
 
 
 # ---------------------------------------------------------------------------
-# logit sweep workloads
+# logit sweep workloads: every (sigma, n, eps) cell on the device, all 1024
+# rows, against the Abstract's Gaussian design rule
+# k_eps / n ~ Phi_c(sigma + Phi^{-1}(eps))
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("sigma", workloads.LOGIT_SIGMAS)
-@pytest.mark.parametrize("n", [4096, 65536])
-def test_logit_sweep(ct, sigma, n):
-    wl = workloads.logit_sweep(sigma, n)
-    L = dev(wl["logits"])
-    V = dev(wl["V"])
-    rows = np.arange(0, 1024, 16)
-    S = wl["logits"][rows].astype(np.float64)
-    V64 = wl["V"].astype(np.float64)
-    for eps in workloads.LOGIT_EPS:
-        _say(f"logit_sweep sigma={sigma} n={n} eps={eps}")
-        res = ct.ctopk_certify_logits(L, V, eps, want_mask=True)
-        torch.cuda.synchronize()
-        g = to_np(res)
-        g["sel_mask"] = unpack_mask(g["sel_mask"], n)
-        ref = oracle.certify_scores(S, V64, eps)
-        rep = compare(g, ref, S, V64, np.zeros(1024, dtype=np.int64), eps, OUT_RTOL_F32,
-                      rows=rows, label=f"logit sweep sigma={sigma} n={n} eps={eps}")
-        print(rep, flush=True)
-        frac = g["k_eps"].mean() / n
-        pred = oracle.gaussian_design_rule(sigma, eps)
-        print(f"k/n={frac:.4f} rule={pred:.4f}", flush=True)
+_SWEEP = {}
 
 
-def test_logit_sweep_largest(ct):
-    n = 1048576
-    wl = workloads.logit_sweep(2.0, n)
-    _say("logit_sweep sigma=2 n=2^20 rows=1024 eps=0.01 (full size)")
-    res = ct.ctopk_certify_logits(dev(wl["logits"]), dev(wl["V"]), 0.01, want_mask=True)
+def _sweep_inputs(sigma, n):
+    # host copies: the smaller workloads are kept, the n = 2^20 one (4 GiB)
+    # only for the sigma in use
+    key = (sigma, n)
+    if key not in _SWEEP:
+        if n > 65536:
+            for old in [k for k in _SWEEP if k[1] > 65536]:
+                del _SWEEP[old]
+        _SWEEP[key] = workloads.logit_sweep(sigma, n)
+    return _SWEEP[key]
+
+
+def _sweep_run(ct, sigma, n, eps):
+    wl = _sweep_inputs(sigma, n)
+    _say(f"logit_sweep sigma={sigma} n={n} eps={eps} rows={wl['rows']}")
+    res = ct.ctopk_certify_logits(dev(wl["logits"]), dev(wl["V"]), eps, want_mask=True)
     torch.cuda.synchronize()
     g = to_np(res)
     g["sel_mask"] = unpack_mask(g["sel_mask"], n)
-    rows = np.array([0, 311, 777, 1023])
+    del res
+    torch.cuda.empty_cache()
+    return wl, g
+
+
+def _design_rule_gap(g, n, sigma, eps):
+    frac = float(np.mean(g["k_eps"] / n))
+    pred = oracle.gaussian_design_rule(sigma, eps)
+    print(f"[design rule] sigma={sigma} n={n} eps={eps} k/n={frac:.4f} "
+          f"(sd {float(np.std(g['k_eps'] / n)):.4f}) rule={pred:.4f} gap={frac - pred:+.4f}", flush=True)
+    return frac - pred
+
+
+@pytest.mark.parametrize("eps", workloads.LOGIT_EPS)
+@pytest.mark.parametrize("sigma", workloads.LOGIT_SIGMAS)
+@pytest.mark.parametrize("n", [4096, 65536])
+def test_logit_sweep(ct, n, sigma, eps):
+    """All 1024 rows: the sort-free minimality check (top set, T_k <= eps <
+    T_{k-1}, tau) and out on the device's own head; the fp64 oracle on every
+    row at n = 4096 and on every 16th row at n = 65536; for sigma <= 2 the mean
+    k/n within 0.005 of the design rule."""
+    wl, g = _sweep_run(ct, sigma, n, eps)
+    S = wl["logits"].astype(np.float64)
+    V64 = wl["V"].astype(np.float64)
+    rep = check_topk_properties(g, S, eps, V64=V64, out_rtol=OUT_RTOL_F32,
+                                label=f"sweep sigma={sigma} n={n} eps={eps}")
+    print(rep, flush=True)
+    rows = np.arange(0, 1024, 1 if n == 4096 else 16)
+    ref = oracle.certify_scores(S[rows], V64, eps)
+    rep = compare(g, ref, S[rows], V64, np.zeros(1024, dtype=np.int64), eps, OUT_RTOL_F32,
+                  rows=rows, label=f"sweep vs oracle sigma={sigma} n={n} eps={eps}")
+    print(rep, flush=True)
+    gap = _design_rule_gap(g, n, sigma, eps)
+    if sigma <= 2.0:
+        assert abs(gap) <= 0.005, gap
+
+
+@pytest.mark.parametrize("eps", workloads.LOGIT_EPS)
+@pytest.mark.parametrize("sigma", workloads.LOGIT_SIGMAS)
+def test_logit_sweep_largest(ct, sigma, eps):
+    """n = 2^20, all 1024 rows on the device: the oracle on 8 sampled rows,
+    the sort-free minimality check on 128 rows, and the design rule on the
+    mean over all rows (sigma <= 2: within 0.005; sigma 3 and 4: the gap to the
+    rule is smaller than at n = 4096, the Abstract's rule being a large-n
+    limit)."""
+    n = 1048576
+    wl, g = _sweep_run(ct, sigma, n, eps)
+    rows = np.array([0, 137, 311, 500, 641, 777, 901, 1023])
     S = wl["logits"][rows].astype(np.float64)
     V64 = wl["V"].astype(np.float64)
-    ref = oracle.certify_scores(S, V64, 0.01)
-    rep = compare(g, ref, S, V64, np.zeros(1024, dtype=np.int64), 0.01, OUT_RTOL_F32, rows=rows,
-                  label="logit sweep n=2^20")
+    ref = oracle.certify_scores(S, V64, eps)
+    rep = compare(g, ref, S, V64, np.zeros(1024, dtype=np.int64), eps, OUT_RTOL_F32, rows=rows,
+                  label=f"sweep vs oracle sigma={sigma} n=2^20 eps={eps}")
     print(rep, flush=True)
-    frac = g["k_eps"].mean() / n
-    assert abs(frac - oracle.gaussian_design_rule(2.0, 0.01)) < 0.005
+    del S, ref
+    prop = np.arange(0, 1024, 8)
+    for c in range(0, len(prop), 32):
+        r = prop[c:c + 32]
+        sub = {"k_eps": g["k_eps"][r], "tau": g["tau"][r], "sel_mask": g["sel_mask"][r]}
+        rep = check_topk_properties(sub, wl["logits"][r].astype(np.float64), eps,
+                                    label=f"sweep sigma={sigma} n=2^20 eps={eps} rows {r[0]}..")
+    print(rep, flush=True)
+    gap = _design_rule_gap(g, n, sigma, eps)
+    if sigma <= 2.0:
+        assert abs(gap) <= 0.005, gap
+    else:
+        _, g_small = _sweep_run(ct, sigma, 4096, eps)
+        gap_small = _design_rule_gap(g_small, 4096, sigma, eps)
+        assert abs(gap) < abs(gap_small), (gap, gap_small)

@@ -162,6 +162,78 @@ def test_equal_scores_exact_boundary_is_flagged():
     assert int(r["k_eps"][0]) in (75, 76)
 
 
+def _scores_from_probs(p):
+    # scores whose softmax is p (up to rounding of log and exp, ~1e-16)
+    return np.log(np.asarray(p, dtype=np.float64))[None]
+
+
+def test_near_boundary_flag_from_the_previous_tail_only():
+    # P = (3/4 - d, 1/4 + d, ...) with eps = 1/4: T_1 = 1/4 + d > eps, so k_eps = 2,
+    # and T_2 = 0.05 is far from eps; only T_{k_eps - 1} lies within 1e-6 eps
+    # of eps, so the flag must come from that side (an index slip that reads
+    # T_{k_eps} or T_{k_eps + 1} there leaves the row unflagged)
+    d = 1e-8
+    eps = 0.25
+    r = oracle.certify_scores(_scores_from_probs([0.75 - d, 0.2 + d, 0.03, 0.02]),
+                              np.ones((1, 4, 1)), eps)
+    assert int(r["k_eps"][0]) == 2
+    assert abs(r["tau"][0] - 0.05) < 1e-14
+    assert abs(r["T_prev"][0] - (0.25 + d)) < 1e-14
+    assert r["near_boundary"][0]
+
+
+def test_near_boundary_flag_from_the_certified_tail_only():
+    # T_1 = 1/4 - d <= eps = 1/4 gives k_eps = 1 with tau within 1e-6 eps of eps,
+    # while T_0 = 1 is far away
+    d = 1e-8
+    r = oracle.certify_scores(_scores_from_probs([0.75 + d, 0.2 - d, 0.03, 0.02]),
+                              np.ones((1, 4, 1)), 0.25)
+    assert int(r["k_eps"][0]) == 1
+    assert abs(r["T_prev"][0] - 1.0) < 1e-14
+    assert r["near_boundary"][0]
+
+
+def test_rows_away_from_the_boundary_are_not_flagged():
+    # T_1 = 0.3 and T_2 = 0.1 around eps = 0.25: both sides far from eps
+    r = oracle.certify_scores(_scores_from_probs([0.7, 0.2, 0.06, 0.04]), np.ones((1, 4, 1)), 0.25)
+    assert int(r["k_eps"][0]) == 2
+    assert abs(r["T_prev"][0] - 0.3) < 1e-14 and abs(r["tau"][0] - 0.1) < 1e-14
+    assert not r["near_boundary"][0]
+    # a relative gap just above the 1e-6 band on the previous side is not flagged either
+    d = 3e-7
+    r = oracle.certify_scores(_scores_from_probs([0.75 - d, 0.2 + d, 0.03, 0.02]),
+                              np.ones((1, 4, 1)), 0.25)
+    assert int(r["k_eps"][0]) == 2 and not r["near_boundary"][0]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_cut_score_of_the_golden_cases(case):
+    # s* is the score of the last key the certified head keeps: the smallest
+    # weight among the case's hand-derived head, as a log
+    w = np.array(case["log_weights"], dtype=np.float64)
+    r = oracle.certify_scores(np.log(w)[None], np.array(case["V"], dtype=np.float64)[None],
+                              case["eps"])
+    assert r["s_star"][0] == math.log(min(w[case["head"]]))
+
+
+def test_cut_score_two_level_closed_form():
+    # m keys at a and n - m at b: the cut score is a while k_eps <= m and b after;
+    # eps = 0.44 puts the cut on exactly the m-th key (T_{m-1} > eps >= T_m), where
+    # the next key in the order scores b
+    n, m, a, b = 200, 13, 2.0, -1.0
+    rng = np.random.default_rng(5)
+    s = np.full(n, b)
+    s[rng.permutation(n)[:m]] = a
+    Z = m * math.exp(a) + (n - m) * math.exp(b)
+    assert ((n - m) * math.exp(b) / Z <= 0.44 < (math.exp(a) + (n - m) * math.exp(b)) / Z)
+    V = np.zeros((1, n, 1))
+    for eps, k_cf, s_cf in ((0.44, m, a), (0.6, None, a), (0.3, None, b)):
+        r = oracle.certify_scores(s[None], V, eps)
+        if k_cf is not None:
+            assert int(r["k_eps"][0]) == k_cf
+        assert r["s_star"][0] == s_cf
+
+
 def test_signed_zero_scores_tie():
     s = np.array([[-0.0, 0.0, -0.0, 0.0]])
     r = oracle.certify_scores(s, np.eye(4)[None], 0.3)
