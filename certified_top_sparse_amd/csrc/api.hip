@@ -141,6 +141,36 @@ int cached_workspace(size_t need, hipStream_t st, void** out) {
   return CTOPK_OK;
 }
 
+// Scratch of ctopk_certify_noalloc: one fixed device array per GPU (every
+// device that loads the library holds its own copy).  In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address is
+// looked up once per device with hipGetSymbolAddress and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[CTOPK_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddrs {
+  std::mutex mu;
+  std::vector<void*> ptr;  // per device; nullptr until looked up
+};
+ScratchAddrs g_scratch;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CTOPK_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  if (static_cast<int>(g_scratch.ptr.size()) <= dev) g_scratch.ptr.resize(dev + 1, nullptr);
+  if (g_scratch.ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CTOPK_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s",
+                  hipGetErrorString(e));
+    g_scratch.ptr[dev] = p;
+  }
+  *out = g_scratch.ptr[dev];
+  return CTOPK_OK;
+}
+
 int check_eps(double eps) {
   if (!(eps > 0.0 && eps < 1.0) || !isfinite(eps))
     return fail(CTOPK_ERR_EPS, "eps must be a finite number in (0, 1), got %g", eps);
@@ -404,6 +434,45 @@ int ctopk_certify(const void* q, const void* K, const void* V, int64_t n, int32_
   a.out = out;
   a.k_eps = k_eps;
   a.tau = tau;
+  return ctopk_certify_ex(&a, stream);
+}
+
+int ctopk_certify_noalloc(const void* q, const void* K, const void* V, int64_t n, int32_t d,
+                          int32_t n_q_heads, int32_t n_kv_heads, double eps,
+                          ctopk_stream_t stream, float* out, int32_t* k_eps, double* tau) {
+  ctopk_args a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.K = K;
+  a.V = V;
+  a.dtype = CTOPK_BF16;
+  a.n = n;
+  a.d = d;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.eps = eps;
+  a.out = out;
+  a.k_eps = k_eps;
+  a.tau = tau;
+  {
+    CallEvents events;  // an armed event list applies to this call even if it fails here
+    int rc = validate_args(&a);
+    if (rc != CTOPK_OK) return rc;
+    const size_t need = ctopk_workspace_bytes(n, d, n_q_heads, n_kv_heads, CTOPK_BF16);
+    if (need > static_cast<size_t>(CTOPK_NOALLOC_SCRATCH_BYTES))
+      return fail(CTOPK_ERR_WORKSPACE,
+                  "these sizes need %zu bytes of scratch, more than the fixed %zu-byte array of "
+                  "ctopk_certify_noalloc",
+                  need, static_cast<size_t>(CTOPK_NOALLOC_SCRATCH_BYTES));
+    void* p = nullptr;
+    rc = scratch_address(&p);
+    if (rc != CTOPK_OK) return rc;
+    a.workspace = p;
+    a.workspace_bytes = CTOPK_NOALLOC_SCRATCH_BYTES;
+    // hand the armed events on to the call below
+    for (int i = 0; i < g_call_n; ++i) g_armed_ev[i] = g_call_ev[i];
+    g_armed_n = g_call_n;
+  }
   return ctopk_certify_ex(&a, stream);
 }
 

@@ -44,6 +44,7 @@ EXPORTED = (
     "ctopk_logits_workspace_bytes", "ctopk_validate", "ctopk_last_error_string",
     "ctopk_version", "ctopk_record_kernel_events", "ctopk_plan", "ctopk_quantize_k4",
     "ctopk_candidates_k4", "ctopk_validate_k4", "ctopk_k4_workspace_bytes",
+    "ctopk_certify_noalloc",
 )
 
 
@@ -124,6 +125,8 @@ def load(path: str = LIB_PATH):
                              ctypes.c_double, ctypes.c_size_t)
     lib.ctopk_certify.argtypes = [vp, vp, vp, i64, i32, i32, i32, f64, vp, vp, vp, vp]
     lib.ctopk_certify.restype = ctypes.c_int
+    lib.ctopk_certify_noalloc.argtypes = [vp, vp, vp, i64, i32, i32, i32, f64, vp, vp, vp, vp]
+    lib.ctopk_certify_noalloc.restype = ctypes.c_int
     lib.ctopk_certify_ex.argtypes = [ctypes.POINTER(CtopkArgs), vp]
     lib.ctopk_certify_ex.restype = ctypes.c_int
     lib.ctopk_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
@@ -241,6 +244,24 @@ def ctopk_certify(q, K, V, eps, out=None, k_eps=None, tau=None, stream=None):
     _check(lib.ctopk_certify(_ptr(q), _ptr(K), _ptr(V), n, d, n_q, n_kv, float(eps),
                              _stream(stream), _ptr(out), _ptr(k_eps), _ptr(tau)))
     return out, k_eps, tau
+
+
+def ctopk_certify_noalloc(q, K, V, eps, out, k_eps, tau, stream=None):
+    """ctopk_certify with the library's fixed scratch array instead of an
+    allocated workspace (no device allocation by the library); the caller
+    passes the outputs.  Returns (out, k_eps, tau)."""
+    lib = load()
+    for name, t in (("q", q), ("K", K), ("V", V), ("out", out), ("k_eps", k_eps),
+                    ("tau", tau)):
+        _require_cuda_contig(name, t)
+    n_q, d = q.shape
+    n_kv, n, _ = K.shape
+    _check(lib.ctopk_certify_noalloc(_ptr(q), _ptr(K), _ptr(V), n, d, n_q, n_kv, float(eps),
+                                     _stream(stream), _ptr(out), _ptr(k_eps), _ptr(tau)))
+    return out, k_eps, tau
+
+
+CTOPK_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 
 def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=None,

@@ -81,6 +81,27 @@ CTOPK_API int ctopk_certify(const void* q, const void* K, const void* V, int64_t
                   int32_t n_q_heads, int32_t n_kv_heads, double eps, ctopk_stream_t stream,
                   float* out, int32_t* k_eps, double* tau);
 
+/*
+ * ctopk_certify_noalloc -- ctopk_certify for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, outputs and kernels as
+ * ctopk_certify; the scratch memory is instead one fixed device array of
+ * CTOPK_NOALLOC_SCRATCH_BYTES bytes owned by the library (one per GPU, held
+ * until the process ends; its address is looked up once per device on the
+ * first call there).  The call makes no hipMalloc or hipFree and calls no
+ * allocating library routine.  Returns CTOPK_ERR_WORKSPACE, before anything
+ * is enqueued, when ctopk_workspace_bytes(n, d, n_q_heads, n_kv_heads,
+ * CTOPK_BF16) exceeds that size, and the other statuses as ctopk_certify.
+ * Every call on a GPU uses that GPU's one array, so calls that overlap on a
+ * GPU (on different streams, or from several host threads) race; calls
+ * ordered on one stream do not.  Nothing in the array needs to start at zero.
+ */
+#define CTOPK_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+CTOPK_API int ctopk_certify_noalloc(const void* q, const void* K, const void* V, int64_t n,
+                                    int32_t d, int32_t n_q_heads, int32_t n_kv_heads, double eps,
+                                    ctopk_stream_t stream, float* out, int32_t* k_eps,
+                                    double* tau);
+
 /* Full-form arguments of ctopk_certify_ex. */
 typedef struct ctopk_args {
   const void* q;            /* [n_q_heads, d], dtype                                   */
@@ -284,7 +305,8 @@ CTOPK_API size_t ctopk_k4_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t 
  * ctopk_record_kernel_events -- instrumentation for benchmarks and profilers.
  *
  * Arms the calling thread so that its NEXT ctopk_certify, ctopk_certify_ex,
- * ctopk_certify_logits or ctopk_candidates_k4 call attaches the event pair (events[2i],
+ * ctopk_certify_noalloc, ctopk_certify_logits or ctopk_candidates_k4 call
+ * attaches the event pair (events[2i],
  * events[2i+1]) -- hipEvent_t handles created by the caller -- to the i-th
  * kernel it launches: the events take that kernel's start and end times on
  * the call's stream (hipExtLaunchKernel), so hipEventElapsedTime on a pair is

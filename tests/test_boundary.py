@@ -288,3 +288,25 @@ def test_k4_entry_points_reject_before_any_gpu_call(lib):
                                  None) == cb.CTOPK_ERR_UNSUPPORTED
     assert lib.ctopk_quantize_k4(vp(A16), cb.CTOPK_BF16, 1 << 30, 128, 32, vp(A16), vp(A16),
                                  vp(A16), None) == cb.CTOPK_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_sizes_beyond_its_array_on_the_host(lib):
+    # the fixed scratch array of ctopk_certify_noalloc is checked before any
+    # HIP call, so this runs without a GPU
+    n_q, n_kv, n, d = 128, 32, 131072, 128
+    assert ct.ctopk_workspace_bytes(n, d, n_q, n_kv) > ct.CTOPK_NOALLOC_SCRATCH_BYTES
+    vp = ctypes.c_void_p
+    rc = lib.ctopk_certify_noalloc(vp(A16), vp(A16 * 2), vp(A16 * 3), n, d, n_q, n_kv, 0.01, None,
+                                   vp(A16 * 4), vp(A16 * 5), vp(A16 * 6))
+    assert rc == cb.CTOPK_ERR_WORKSPACE
+    assert "scratch" in ct.ctopk_last_error_string()
+    # and the usual argument checks come first
+    rc = lib.ctopk_certify_noalloc(vp(A16), vp(A16 * 2), vp(A16 * 3), n, d, n_q, n_kv, 1.5, None,
+                                   vp(A16 * 4), vp(A16 * 5), vp(A16 * 6))
+    assert rc == cb.CTOPK_ERR_EPS
+
+
+def test_noalloc_array_size_matches_the_header(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define CTOPK_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m and int(m.group(1)) * 1024 * 1024 == ct.CTOPK_NOALLOC_SCRATCH_BYTES
