@@ -50,11 +50,11 @@ PEAK_HBM_GBPS = 8000.0
 # otherwise its event pair is recorded back to back and times no kernel.
 KERNELS_BY_PLAN = {
     2: ("score_scan", "hist0", "resolve", "vsum", "finalize"),
-    3: ("score_scan", "hist0", "select_dense", "tail", "finalize"),
+    3: ("score_scan", "hist0", "select_spec"),
     4: ("score_scan", "hist0", "bound", "vsum", "finalize"),
 }
 # The kernel of each plan that streams the V rows of the head sets.
-V_KERNEL = {2: "vsum", 3: "select_dense", 4: "vsum"}
+V_KERNEL = {2: "vsum", 3: "select_spec", 4: "vsum"}
 PLAN_NAMES = {1: "encoder", 2: "decode", 3: "decode_overlap", 4: "decode_bound"}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_gqa_decode_n32768.md")
 CSRC = os.path.join(ROOT, "certified_top_sparse_amd", "csrc")
@@ -65,9 +65,8 @@ KERNEL_SOURCES = {
     "score_scan": ("score_scan.hip", "scan_dot.h") + _COMMON,
     "k4_scan": ("k4.hip", "scan_dot.h") + _COMMON,
     "k4_rescore": ("k4.hip", "scan_dot.h") + _COMMON,
-    "select_dense": ("select.hip", "vsum_body.h") + _COMMON,
+    "select_spec": ("select.hip", "vsum_body.h") + _COMMON,
     "resolve": ("select.hip", "vsum_body.h") + _COMMON,
-    "tail": ("vsum.hip", "vsum_body.h") + _COMMON,
     "vsum": ("vsum.hip", "vsum_body.h") + _COMMON,
     "bound": ("bound.hip",) + _COMMON,
 }

@@ -68,13 +68,16 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr int64_t kMaxN = 2147483647LL;
 constexpr int64_t kMaxElems = 1LL << 36;  // rows * n
 
-// Scratch layout shared by both paths (every region is fully written before
-// it is read within a call, so nothing needs zeroing).
+// Scratch layout shared by both paths.  Every region is fully written before
+// it is read within a call, except `sync` (the overlapped plan's published
+// head masses and cuts), which the score scan of the same call zeroes; so
+// nothing needs clearing between calls.
 struct Layout {
-  size_t rowsel = 0, blkstat = 0, blkz = 0, part = 0, pmass = 0;
+  size_t rowsel = 0, blkstat = 0, blkz = 0, part = 0, pmass = 0, sync = 0;
   size_t scores = 0, total = 0;
+  size_t sync_bytes = 0;
   int nblk = 0, nchunk = 0, hchunk = 0;
-  int dchunk = 0;  // dense-stream chunks of the overlapped decode path (0: not taken)
+  int dchunk = 0;  // value-stream chunks of the overlapped decode plan (0: not taken)
 };
 
 Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
@@ -82,9 +85,9 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   L.nblk = decode ? static_cast<int>(ctopk::ceil_div(n, ctopk::kScanTile)) : 0;
   L.nchunk = ctopk::vsum_nchunk(n, rows, n_v, v_dtype, dv);
   L.hchunk = (decode && n > ctopk::resolve_register_row()) ? ctopk::hist_nchunk(n, rows) : 0;
-  L.dchunk = decode ? ctopk::select_dense_nchunk(n, rows, n_v, v_dtype, dv) : 0;
-  // partial slots per row: head + tail per value-stream chunk, or dense +
-  // head per dense chunk
+  L.dchunk = decode ? ctopk::select_spec_nchunk(n, rows, n_v, v_dtype, dv) : 0;
+  // partial slots per row: head + tail per value-stream chunk, or one per
+  // chunk of the overlapped plan's stream
   const size_t pslots = 2 * static_cast<size_t>(L.nchunk > L.dchunk ? L.nchunk : L.dchunk);
   size_t off = 0;
   L.rowsel = off;
@@ -97,6 +100,9 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   off += up(static_cast<size_t>(rows) * pslots * (dv + 1) * sizeof(float));
   L.pmass = off;
   off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(double));
+  L.sync = off;  // CutPub [rows]
+  L.sync_bytes = L.dchunk > 0 ? up(static_cast<size_t>(rows) * sizeof(ctopk::CutPub)) : 0;
+  off += L.sync_bytes;
   L.scores = off;
   off += up(decode ? static_cast<size_t>(rows) * static_cast<size_t>(n) * sizeof(float) : 0);
   L.total = off;
@@ -229,7 +235,7 @@ int plan_of(const ctopk_args* a) {
   if (certificate) return CTOPK_PLAN_DECODE;
   if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads))
     return CTOPK_PLAN_ENCODER;
-  if (ctopk::select_dense_nchunk(a->n, a->n_q_heads, a->n_kv_heads, a->dtype, a->d) > 0)
+  if (ctopk::select_spec_nchunk(a->n, a->n_q_heads, a->n_kv_heads, a->dtype, a->d) > 0)
     return CTOPK_PLAN_DECODE_OVERLAP;
   return CTOPK_PLAN_DECODE;
 }
@@ -369,9 +375,13 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   ctopk::RowSel* rs = reinterpret_cast<ctopk::RowSel*>(ws + L.rowsel);
   const int rows = a->n_q_heads;
 
+  const bool overlap = plan == CTOPK_PLAN_DECODE_OVERLAP;
   rc = hip_check(ctopk::launch_score_scan(a->q, a->K, a->dtype, a->d, a->head_scale,
                                           default_scale, a->n, rows, a->n_kv_heads, scores,
-                                          blkstat, blkz, nullptr, 0, st),
+                                          blkstat, blkz, overlap ? ws + L.sync : nullptr,
+                                          overlap ? L.sync_bytes : 0, overlap ? a->out : nullptr,
+                                          overlap ? static_cast<size_t>(rows) * a->d * sizeof(float) : 0,
+                                          st),
                  "score_scan launch");
   if (rc != CTOPK_OK) return rc;
   if (L.hchunk > 0 && plan != CTOPK_PLAN_DECODE_BOUND) {  // long rows: level 0 from many blocks per row
@@ -382,20 +392,15 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   } else {
     ctopk::skip_kernel_events(st);
   }
-  if (plan == CTOPK_PLAN_DECODE_OVERLAP) {
-    // The select beside the dense value stream in one launch, then the tail
-    // pass and the combine.
-    float* dpart = part;
-    float* hpart = part + static_cast<size_t>(rows) * L.dchunk * (a->d + 1);
-    rc = hip_check(ctopk::launch_select_dense(scores, a->n, rows, blkstat, L.nblk, a->eps, rs,
-                                              a->k_eps, a->tau, a->lse, a->sel_mask,
-                                              a->n_kv_heads, a->V, a->dtype, a->d, dpart,
-                                              L.dchunk, st),
+  if (overlap) {
+    // The select beside the value stream over provisional heads, corrected
+    // and added into out inside the same launch (out zeroed by the scan).
+    rc = hip_check(ctopk::launch_select_spec(scores, a->n, rows, blkstat, L.nblk, a->eps, rs,
+                                             a->k_eps, a->tau, a->lse, a->sel_mask,
+                                             a->n_kv_heads, a->V, a->dtype, a->d, L.dchunk,
+                                             reinterpret_cast<ctopk::CutPub*>(ws + L.sync),
+                                             a->out, st),
                    "select launch");
-    if (rc != CTOPK_OK) return rc;
-    rc = hip_check(ctopk::launch_tail_fix(scores, a->n, rows, a->n_kv_heads, a->V, a->dtype,
-                                          a->d, rs, a->k_eps, dpart, hpart, L.dchunk, a->out, st),
-                   "tail pass launch");
     if (rc != CTOPK_OK) return rc;
     return ok();
   }

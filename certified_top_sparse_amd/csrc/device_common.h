@@ -342,6 +342,16 @@ __device__ __forceinline__ unsigned long long wave_pick_u64(unsigned long long v
                        (static_cast<unsigned long long>(e.y) << 32) | c.y);
 }
 
+// What the select of a row hands to the value stream of the same launch:
+// the head's softmax mass (relative to the row maximum, fp64) and the cut
+// key64, written in that order with device-scope stores; both are non-zero
+// once written (the head holds at least the row's maximum, weight 1), and
+// zero before.
+struct CutPub {
+  uint64_t cut;
+  double den;
+};
+
 // Per-row scalars handed from the selection to the output kernel.
 struct RowSel {
   float m;        // row maximum of the fp32 scores (weight reference)

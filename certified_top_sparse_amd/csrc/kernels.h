@@ -21,8 +21,8 @@ constexpr int kScanTile = 64;
 constexpr int kVsumTile = 256;
 // Largest candidate set the resolve kernel keeps in LDS.
 constexpr int kCandCap = 8192;
-// Most keys per chunk of the tail pass of the overlapped decode plan (its key
-// list lives in LDS).
+// Most keys per chunk of the value stream of the overlapped decode plan (the
+// keys its correction needs are listed in LDS).
 constexpr int kFixKeys = 2048;
 // Most score-scan tiles per row for the blockwise bound (staged in LDS).
 constexpr int kBoundMaxTiles = 4096;
@@ -52,11 +52,13 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shme
 
 // K1: scores[h, i] = scale_h * <q_h, K[h / G, i]> and blkstat[h, tile] =
 // (min, max) over the tile; with blkz non-NULL also blkz[h, tile] = the sum
-// over the tile of exp(s - its max).  Also zeroes `zero_bytes` at `zero_base`.
+// over the tile of exp(s - its max).  Also zeroes `zero_bytes` at `zero_base`
+// and `zero_bytes2` at `zero_base2` (multiples of 16 bytes; NULL: nothing).
 hipError_t launch_score_scan(const void* q, const void* K, int dtype, int d,
                              const float* head_scale, float default_scale, int64_t n,
                              int n_q, int n_kv, float* scores, float2* blkstat, float* blkz,
-                             void* zero_base, size_t zero_bytes, hipStream_t st);
+                             void* zero_base, size_t zero_bytes, void* zero_base2,
+                             size_t zero_bytes2, hipStream_t st);
 
 // Level 0 of the select for long decode rows, many blocks per row: row
 // (min, max) from blkstat, weights w = exp(s - max), and an fp64 mass
@@ -96,23 +98,21 @@ hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const 
 // kVsumTile keys per chunk, never more chunks than tiles).
 int stream_nchunk(int64_t n, int groups, int blocks);
 
-// Decode rows the select holds in registers can run beside a dense value
-// stream: select_dense_nchunk gives that stream's chunks per group (0 when
-// the shape does not qualify: rows of 16K..32K keys, at least half of the
-// compute units left beside the rows' workgroups, and chunks of at most
-// kFixKeys keys).  launch_select_dense runs the select (as launch_resolve with
-// register rows) and writes the dense partials dpart [rows, nchunk, dv + 1]
-// (sum of w v and of w over every key of a chunk); launch_tail_fix turns them
-// into head partials in part (same layout) and runs the finalize (out).
-int select_dense_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv);
-hipError_t launch_select_dense(const float* scores, int64_t n, int rows, const float2* blkstat,
-                               int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
-                               double* lse, uint32_t* sel_mask, int n_v, const void* V,
-                               int v_dtype, int dv, float* dpart, int nchunk, hipStream_t st);
-hipError_t launch_tail_fix(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                           int v_dtype, int dv, const RowSel* rs, const int32_t* k_eps,
-                           const float* dpart, float* part, int nchunk, float* out,
-                           hipStream_t st);
+// Decode rows the select holds in registers can run beside the value stream
+// in one launch: select_spec_nchunk gives that stream's chunks per group (0
+// when the shape does not qualify: rows of 16K..32K keys, at least half of
+// the compute units left beside the rows' workgroups, and chunks of at most
+// kFixKeys keys).  launch_select_spec runs the select (as launch_resolve with
+// register rows; each row's head mass and cut are published in pub[row]) and
+// a stream over a provisional head per chunk, corrected by the exact cut,
+// whose chunk sums are added, divided by the head mass, into out with
+// device-scope float atomics.  pub [rows] and out must be zero at launch.
+int select_spec_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv);
+hipError_t launch_select_spec(const float* scores, int64_t n, int rows, const float2* blkstat,
+                              int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                              double* lse, uint32_t* sel_mask, int n_v, const void* V,
+                              int v_dtype, int dv, int nchunk, CutPub* pub, float* out,
+                              hipStream_t st);
 
 // Blockwise deterministic bound, one workgroup per row: from the scan's tile
 // (min, max) and tile masses blkz, the largest threshold whose bound on the

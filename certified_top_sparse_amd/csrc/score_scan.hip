@@ -34,7 +34,8 @@ template <typename T, int D, int GB, bool HS>
 __global__ __launch_bounds__(256) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ K, const float* __restrict__ head_scale,
     float default_scale, int64_t n, int G, int nblk, float* __restrict__ scores,
-    float2* __restrict__ blkstat, float* __restrict__ blkz, void* zero_base, size_t zero_bytes) {
+    float2* __restrict__ blkstat, float* __restrict__ blkz, void* zero_base, size_t zero_bytes,
+    void* zero_base2, size_t zero_bytes2) {
   constexpr int EPL = Slice<T>::kElems;
   constexpr int LPR = D / EPL;
   constexpr int RPW = kWave / LPR;
@@ -77,9 +78,12 @@ __global__ __launch_bounds__(256) void score_scan_kernel(
       sc[j] = default_scale;
     }
   }
-  zero_slice(zero_base, zero_bytes,
-             (static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x,
-             static_cast<size_t>(gridDim.x) * gridDim.y * gridDim.z);
+  {
+    const size_t bl = (static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const size_t nb = static_cast<size_t>(gridDim.x) * gridDim.y * gridDim.z;
+    zero_slice(zero_base, zero_bytes, bl, nb);
+    zero_slice(zero_base2, zero_bytes2, bl, nb);
+  }
 
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
@@ -122,25 +126,26 @@ __global__ __launch_bounds__(256) void score_scan_kernel(
 template <typename T, int D, int GB>
 hipError_t launch_t(const void* q, const void* K, const float* head_scale, float default_scale,
                     int64_t n, int n_q, int n_kv, float* scores, float2* blkstat, float* blkz,
-                    void* zb, size_t zbytes, hipStream_t st) {
+                    void* zb, size_t zbytes, void* zb2, size_t zbytes2, hipStream_t st) {
   const int G = n_q / n_kv;
   const int nblk = static_cast<int>(ceil_div(n, kScanTile));
   dim3 grid(nblk, n_kv, static_cast<unsigned>(ceil_div(G, GB)));
   if (head_scale != nullptr)
     return launch(score_scan_kernel<T, D, GB, true>, grid, dim3(256), 0, st,
                   static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale,
-                  n, G, nblk, scores, blkstat, blkz, zb, zbytes);
+                  n, G, nblk, scores, blkstat, blkz, zb, zbytes, zb2, zbytes2);
   return launch(score_scan_kernel<T, D, GB, false>, grid, dim3(256), 0, st,
                 static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale, n,
-                G, nblk, scores, blkstat, blkz, zb, zbytes);
+                G, nblk, scores, blkstat, blkz, zb, zbytes, zb2, zbytes2);
 }
 
 template <typename T, int D>
 hipError_t launch_d(const void* q, const void* K, const float* hs, float ds, int64_t n, int n_q,
                     int n_kv, float* scores, float2* bs, float* bz, void* zb, size_t zbytes,
-                    hipStream_t st) {
+                    void* zb2, size_t zbytes2, hipStream_t st) {
   const int G = n_q / n_kv;
-#define CTOPK_SCAN(GB) launch_t<T, D, GB>(q, K, hs, ds, n, n_q, n_kv, scores, bs, bz, zb, zbytes, st)
+#define CTOPK_SCAN(GB) \
+  launch_t<T, D, GB>(q, K, hs, ds, n, n_q, n_kv, scores, bs, bz, zb, zbytes, zb2, zbytes2, st)
   if (G == 1) return CTOPK_SCAN(1);
   if (G == 2) return CTOPK_SCAN(2);
   if (G <= 4) return CTOPK_SCAN(4);
@@ -153,19 +158,20 @@ hipError_t launch_d(const void* q, const void* K, const float* hs, float ds, int
 hipError_t launch_score_scan(const void* q, const void* K, int dtype, int d,
                              const float* head_scale, float default_scale, int64_t n, int n_q,
                              int n_kv, float* scores, float2* blkstat, float* blkz,
-                             void* zero_base, size_t zero_bytes, hipStream_t st) {
+                             void* zero_base, size_t zero_bytes, void* zero_base2,
+                             size_t zero_bytes2, hipStream_t st) {
   if (dtype == 1) {
     if (d == 128)
       return launch_d<uint16_t, 128>(q, K, head_scale, default_scale, n, n_q, n_kv, scores,
-                                     blkstat, blkz, zero_base, zero_bytes, st);
+                                     blkstat, blkz, zero_base, zero_bytes, zero_base2, zero_bytes2, st);
     return launch_d<uint16_t, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
-                                  blkz, zero_base, zero_bytes, st);
+                                  blkz, zero_base, zero_bytes, zero_base2, zero_bytes2, st);
   }
   if (d == 128)
     return launch_d<float, 128>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat,
-                                blkz, zero_base, zero_bytes, st);
+                                blkz, zero_base, zero_bytes, zero_base2, zero_bytes2, st);
   return launch_d<float, 64>(q, K, head_scale, default_scale, n, n_q, n_kv, scores, blkstat, blkz,
-                             zero_base, zero_bytes, st);
+                             zero_base, zero_bytes, zero_base2, zero_bytes2, st);
 }
 
 }  // namespace ctopk

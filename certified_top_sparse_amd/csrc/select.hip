@@ -387,7 +387,7 @@ __device__ __forceinline__ void resolve_row(
     const float2* __restrict__ blkstat, int nblk, const double* __restrict__ pmass, int npart,
     double eps, RowSel* __restrict__ rs, int32_t* __restrict__ k_eps, double* __restrict__ tau,
     double* __restrict__ lse, uint32_t* __restrict__ sel_mask, void* zero_base,
-    size_t zero_bytes) {
+    size_t zero_bytes, CutPub* publish = nullptr) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -471,19 +471,19 @@ __device__ __forceinline__ void resolve_row(
   }
   double R = S;
   uint64_t below = 0;
-  uint64_t prefix = 0;
-  int plen = 0;
-  bool done = false;
-
-  // Copies the keys of the current range (bin b0 and the prefix) into LDS,
-  // up to kCandCap of them, with one LDS atomic per wave and step; returns
-  // how many there are.  With count_below it also adds the number of keys in
-  // lower bins to `below`.
   // Bin b0 is the score range [f0, f1) (two waves search in parallel).
   if (wave < 2) {
     const float f = bin_floor(b0 + wave, lo, inv);
     if (lane == 0) (wave == 0 ? sh.f0 : sh.f1) = f;
   }
+  uint64_t prefix = 0;
+  int plen = 0;
+  bool done = false;
+
+  // Copies the keys of the current range (the score range [f0, f1) and the
+  // prefix) into LDS, up to kCandCap of them, with one LDS atomic per wave
+  // and step; returns how many there are.  With count_below it also adds the
+  // number of keys below f0 to `below`.
   auto collect = [&](bool count_below, auto with_prefix) -> uint32_t {
     // Only passes after the first (plen > 0) match the key prefix; the first
     // builds key64 only in waves that hold a candidate.
@@ -657,6 +657,18 @@ __device__ __forceinline__ void resolve_row(
     __syncthreads();
   }
   const uint64_t thr = sh.thr;
+  // Other workgroups of the launch may wait for the cut: the head's mass,
+  // then the cut, with device-scope stores, the second only after the first
+  // has completed (both non-zero: the head holds the row maximum, and every
+  // finite score's key64 has a non-zero upper word).
+  if (publish != nullptr && t == 0) {
+    const double den = Z - R;
+    __hip_atomic_store(&publish->den, den > 0.0 ? den : 1.0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __hip_atomic_store(&publish->cut, thr != 0ull ? thr : 1ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   if (t == 0) {
     rs[row].m = m;
@@ -695,77 +707,357 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
 }
 
 // The select of every row and, on the compute units it leaves idle, the
-// dense value stream: workgroups [0, rows) each select one row; the others
-// each sum w v over one chunk of keys for GB query heads of one V head, with
-// weights exp(s - m) from the row maximum alone (no cut needed).  One launch
-// places both, so they run side by side.
+// value stream, in one launch.  Workgroups [0, rows) each select one row and
+// publish its head's mass and cut (pub[row]).  The others each own one chunk
+// of keys of GB query heads of one V head and:
+//   1. guess each head's cut from 512 of its scores (64 evenly spaced runs of
+//      8 consecutive keys; one wave per head bisects the sample's score range
+//      for the value below which the sample's softmax mass first exceeds eps
+//      of its total) -- a provisional head {key64 >= spec};
+//   2. stream V over the chunk summing w v for the provisional head
+//      (w = exp(s - m), m the row maximum from the scan's tile pairs, the same
+//      m and weights the select uses), keeping the chunk's scores in LDS,
+//      while the select runs;
+//   3. wait for the published mass and cut (a bounded spin on pub[]; the
+//      select workgroups have the lowest ids, so they were dispatched first,
+//      and they wait on nothing) and add, signed, w v of the keys between the
+//      two thresholds (+ for head keys the guess left out, - for the others;
+//      listed in key order in LDS), so the lane sums become the head's sums;
+//   4. reduce them over the workgroup and add num / den into out with
+//      device-scope float atomics (out is zeroed before the launch).
+// out is thus a sum of one term per chunk in arrival order: reproducible to
+// fp32 rounding of those terms, not bit for bit.  A timed-out wait adds NaN.
+// pub[] and out must be zero at launch (the score scan zeroes both).
+constexpr int kSpecRuns = 64;       // sample runs per head (one per lane)
+constexpr int kSpecRunKeys = 8;     // consecutive keys per run
+constexpr int kSpecRounds = 10;     // bisection rounds of the guess
+constexpr int kSpinLimit = 1 << 21;  // polls of about a microsecond: ~2 s, never reached
+
 template <typename T, int D, int GB>
-union SelectDenseSmem {
-  ResolveShared r;
-  StreamSmem<T, D, GB, kStreamDense, kResolveWaves> v;
+struct SpecSmem {
+  union {
+    StreamSmem<T, D, GB, kStreamGiven, kResolveWaves> v;
+    struct {
+      int idx[kFixKeys];
+      float w[kFixKeys][GB];
+      uint32_t cnt[kFixKeys / kResolveThreads][kResolveWaves];
+    } band;
+  };
+  float stash[GB * kFixKeys];  // the chunk's scores, [head][key in chunk]
+  float mx[GB][kResolveWaves];
+  uint64_t spec[GB];
+  uint64_t exact[GB];
+  double den[GB];
+};
+
+// Steps 3 and 4 above, run by value_stream_block after the stream with every
+// lane's sums (acc[j][e]: head j, V elements seg * EPL + e of the rows the
+// lane handles).
+template <typename T, int D, int GB>
+struct SpecFinish {
+  SpecSmem<T, D, GB>* sm;
+  const T* V;
+  const CutPub* pub;
+  const float* m;
+  float* out;
+  int64_t c0;
+  int len, h0, nh;
+
+  template <typename L>
+  __device__ __forceinline__ void operator()(L& ln) const {
+    using Acc = typename AccOf<T>::type;
+    constexpr int NT = kResolveThreads, NW = kResolveWaves;
+    constexpr int KPT = kFixKeys / NT;
+    constexpr int EPL = VSlice<T>::kElems, LPR = D / EPL, RPW = kWave / LPR, STEP = NW * RPW;
+    static_assert(kFixKeys % NT == 0, "whole keys per thread");
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    __syncthreads();  // every wave is past its stream loop: the staging LDS is free
+    if (t < nh) {
+      // Both words non-zero: both stores have landed (each word has one
+      // writer, and zero is only its value before that store).
+      uint64_t c = 0ull;
+      double dn = 0.0;
+      for (int it = 0; it < kSpinLimit; ++it) {
+        c = __hip_atomic_load(&pub[h0 + t].cut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dn = __hip_atomic_load(&pub[h0 + t].den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (c != 0ull && dn != 0.0) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      const bool got = c != 0ull && dn != 0.0;
+      sm->exact[t] = got ? c : ~0ull;
+      sm->den[t] = got ? dn : __longlong_as_double(0x7FF8000000000000LL);  // NaN: no cut arrived
+    }
+    __syncthreads();
+    // Keys between the guess and the cut, with signed weights per head.
+    float wv[KPT][GB];
+    bool sel[KPT];
+    uint64_t bal[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int i = t + u * NT;
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < GB; ++j) {
+        float w = 0.0f;
+        if (j < nh && i < len) {
+          const float s = sm->stash[j * kFixKeys + i];
+          const uint64_t k = key64(s, static_cast<uint32_t>(c0 + i));
+          const bool in_spec = k >= sm->spec[j];
+          const bool in_head = k >= sm->exact[j];
+          if (in_spec != in_head) {
+            w = weight(s, m[j]);
+            w = in_head ? w : -w;
+            any = true;
+          }
+        }
+        wv[u][j] = w;
+      }
+      sel[u] = any;
+      bal[u] = __ballot(any);
+      if (lane == 0) sm->band.cnt[u][wave] = static_cast<uint32_t>(__popcll(bal[u]));
+    }
+    __syncthreads();
+    uint32_t base = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      uint32_t before = 0u, all = 0u;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t c = sm->band.cnt[u][w];
+        before += w < wave ? c : 0u;
+        all += c;
+      }
+      if (sel[u]) {
+        const uint32_t slot =
+            base + before +
+            __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal[u] >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[u]), 0u));
+        sm->band.idx[slot] = t + u * NT;
+#pragma unroll
+        for (int j = 0; j < GB; ++j) sm->band.w[slot][j] = wv[u][j];
+      }
+      base += all;
+    }
+    const int nb = static_cast<int>(base);
+    __syncthreads();
+    // Gather the listed V rows into this lane's sums (entry e = k STEP +
+    // RPW wave + rg).
+    const int seg = lane % LPR, rg = lane / LPR;
+    constexpr int ITB = 4;
+    for (int k0 = 0; k0 * STEP < nb; k0 += ITB) {
+      uint4 u[ITB];
+#pragma unroll
+      for (int it = 0; it < ITB; ++it) {
+        const int e = min((k0 + it) * STEP + RPW * wave + rg, nb - 1);
+        const int64_t r = c0 + sm->band.idx[e];
+        u[it] = *reinterpret_cast<const uint4*>(V + r * D + seg * EPL);
+      }
+#pragma unroll
+      for (int it = 0; it < ITB; ++it) {
+        const int e = (k0 + it) * STEP + RPW * wave + rg;
+        const bool valid = e < nb;
+        const int ec = min(e, nb - 1);
+        float v[EPL];
+        VSlice<T>::load(u[it], v);
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+          const Acc w = valid ? static_cast<Acc>(sm->band.w[ec][j]) : Acc(0);
+#pragma unroll
+          for (int e2 = 0; e2 < EPL; ++e2) ln.acc[j][e2] += w * static_cast<Acc>(v[e2]);
+        }
+      }
+    }
+    // Workgroup sums: the row groups of a wave by cross-lane adds, then the
+    // waves in order through LDS; each column's num / den into out.
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
+    __syncthreads();  // the list is read: its LDS takes the reduction
+    if (rg == 0) {
+#pragma unroll
+      for (int j = 0; j < GB; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sm->v.red[0][wave][j * D + seg * EPL + e] = ln.acc[j][e];
+    }
+    __syncthreads();
+    for (int col = t; col < nh * D; col += NT) {
+      const int j = col / D;
+      double sum = 0.0;
+#pragma unroll
+      for (int g = 0; g < NW; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
+      unsafeAtomicAdd(out + static_cast<size_t>(h0 + j) * D + (col - j * D),
+                      static_cast<float>(sum / sm->den[j]));
+    }
+  }
 };
 
 template <typename T, int D, int GB>
-__global__ __launch_bounds__(kResolveThreads) void select_dense_kernel(
+__device__ __forceinline__ void spec_stream_block(
+    SpecSmem<T, D, GB>& sm, const float* __restrict__ scores, int64_t n, int G,
+    const T* __restrict__ V, const float2* __restrict__ blkstat, int nblk, double eps, int tpb,
+    int chunk, int vh, int hz, const CutPub* __restrict__ pub, float* __restrict__ out) {
+  constexpr int NT = kResolveThreads, NW = kResolveWaves;
+  static_assert(kSpecRuns == kWave, "one sample run per lane");
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int h0 = vh * G + hz * GB;
+  const int nh = min(GB, G - hz * GB);
+
+  // Wave j < nh loads head j's sample (run of lane l at l (n - 8) / 63, or
+  // keys l + 64 u of short rows); every thread loads its share of the scan's
+  // tile maxima.  Both are issued before any arithmetic.
+  float sv[kSpecRunKeys];
+  const bool sampler = wave < nh;
+  if (sampler) {
+    const float* srow = scores + static_cast<size_t>(h0 + wave) * static_cast<size_t>(n);
+    if (n >= kSpecRuns * kSpecRunKeys) {
+      const int64_t p = static_cast<int64_t>(lane) * (n - kSpecRunKeys) / (kSpecRuns - 1);
+#pragma unroll
+      for (int u = 0; u < kSpecRunKeys; ++u) sv[u] = srow[p + u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSpecRunKeys; ++u) {
+        const int64_t i = lane + static_cast<int64_t>(kWave) * u;
+        sv[u] = i < n ? srow[i] : -INFINITY;  // -inf: weight 0, never below a finite t
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < GB; ++j) {
+    const float2* bs = blkstat + static_cast<size_t>(h0 + min(j, nh - 1)) * nblk;
+    float vmax = -INFINITY;
+    for (int b = t; b < nblk; b += NT) vmax = fmaxf(vmax, bs[b].y);
+    vmax = wave_max_dpp(vmax);
+    if (lane == 0) sm.mx[j][wave] = vmax;
+  }
+  if (sampler) {
+    // Bisection over the sample's range for the largest value t with the
+    // sample's mass below t at most eps of its total (fp32; only a guess).
+    float smax = -INFINITY, smin = INFINITY;
+#pragma unroll
+    for (int u = 0; u < kSpecRunKeys; ++u) {
+      smax = fmaxf(smax, sv[u]);
+      smin = sv[u] > -INFINITY ? fminf(smin, sv[u]) : smin;
+    }
+    smax = wave_max_dpp(smax);
+    smin = -wave_max_dpp(-smin);
+    float wsv[kSpecRunKeys];
+    float tot = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kSpecRunKeys; ++u) {
+      wsv[u] = sv[u] > -INFINITY ? weight(sv[u], smax) : 0.0f;
+      tot += wsv[u];
+    }
+    const float lim = static_cast<float>(eps) * group_sum<kWave>(tot);
+    float lo = smin, hi = smax;
+    for (int r = 0; r < kSpecRounds; ++r) {
+      const float mid = 0.5f * (lo + hi);
+      float below = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kSpecRunKeys; ++u) below += sv[u] < mid ? wsv[u] : 0.0f;
+      if (group_sum<kWave>(below) > lim) {
+        hi = mid;
+      } else {
+        lo = mid;
+      }
+    }
+    if (lane == 0) {
+      const uint64_t spec = lo > smin ? static_cast<uint64_t>(ukey(lo)) << 32 : 0ull;
+      sm.spec[wave] = spec;
+      sm.v.thr[wave] = spec;
+    }
+  } else if (wave == nh && lane < GB - nh) {  // unused head slots keep nothing
+    sm.spec[nh + lane] = ~0ull;
+    sm.v.thr[nh + lane] = ~0ull;
+  }
+  __syncthreads();
+  float mx[GB];
+#pragma unroll
+  for (int j = 0; j < GB; ++j) {
+    float b = sm.mx[j][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) b = fmaxf(b, sm.mx[j][w]);
+    mx[j] = b;
+  }
+  if (t < GB) sm.v.m[t] = mx[t];
+  __syncthreads();
+
+  const int64_t c0 = static_cast<int64_t>(chunk) * tpb * kVsumTile;
+  const int len = static_cast<int>(min(n - c0, static_cast<int64_t>(tpb) * kVsumTile));
+  const T* Vb = V + static_cast<size_t>(vh) * static_cast<size_t>(n) * D;
+  SpecFinish<T, D, GB> fin{&sm, Vb, pub, mx, out, c0, len, h0, nh};
+  value_stream_block<T, D, GB, kStreamGiven, NW>(sm.v, scores, n, G, V, nullptr, nullptr, 0, tpb,
+                                                 chunk, vh, hz, fin, sm.stash);
+}
+
+template <typename T, int D, int GB>
+union SelectSpecSmem {
+  ResolveShared r;
+  SpecSmem<T, D, GB> s;
+};
+
+template <typename T, int D, int GB>
+__global__ __launch_bounds__(kResolveThreads) void select_spec_kernel(
     const float* __restrict__ scores, int64_t n, const float2* __restrict__ blkstat, int nblk,
     double eps, RowSel* __restrict__ rs, int32_t* __restrict__ k_eps, double* __restrict__ tau,
     double* __restrict__ lse, uint32_t* __restrict__ sel_mask, int rows, int G,
-    const T* __restrict__ V, float* __restrict__ dpart, int nchunk, int tpb, int nz) {
-  __shared__ SelectDenseSmem<T, D, GB> sm;
+    const T* __restrict__ V, int nchunk, int tpb, int nz, CutPub* pub, float* __restrict__ out) {
+  __shared__ SelectSpecSmem<T, D, GB> sm;
   const int b = static_cast<int>(blockIdx.x);
   if (b < rows) {
     resolve_row<kResolveRegRow / kResolveThreads>(sm.r, b, scores, n, blkstat, nblk, nullptr, 0,
-                                                  eps, rs, k_eps, tau, lse, sel_mask, nullptr, 0);
+                                                  eps, rs, k_eps, tau, lse, sel_mask, nullptr, 0,
+                                                  pub + b);
     return;
   }
   const int db = b - rows;
   const int grp = db / nchunk;
-  value_stream_block<T, D, GB, kStreamDense, kResolveWaves>(sm.v, scores, n, G, V, nullptr,
-                                                            blkstat, nblk, dpart, nchunk, tpb,
-                                                            db % nchunk, grp / nz, grp % nz);
+  spec_stream_block<T, D, GB>(sm.s, scores, n, G, V, blkstat, nblk, eps, tpb, db % nchunk,
+                              grp / nz, grp % nz, pub, out);
 }
 
 template <typename T, int D, int GB>
-hipError_t select_dense_t(const float* scores, int64_t n, int rows, const float2* blkstat,
-                          int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
-                          double* lse, uint32_t* sel_mask, int n_v, const void* V, float* dpart,
-                          int nchunk, hipStream_t st) {
+hipError_t select_spec_t(const float* scores, int64_t n, int rows, const float2* blkstat,
+                         int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                         double* lse, uint32_t* sel_mask, int n_v, const void* V, int nchunk,
+                         CutPub* pub, float* out, hipStream_t st) {
   const int G = rows / n_v;
   const int nz = static_cast<int>(ceil_div(G, GB));
   const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
   const unsigned grid = static_cast<unsigned>(rows + n_v * nz * nchunk);
-  return launch(select_dense_kernel<T, D, GB>, dim3(grid), dim3(kResolveThreads), 0, st, scores,
+  return launch(select_spec_kernel<T, D, GB>, dim3(grid), dim3(kResolveThreads), 0, st, scores,
                 n, blkstat, nblk, eps, rs, k_eps, tau, lse, sel_mask, rows, G,
-                static_cast<const T*>(V), dpart, nchunk, tpb, nz);
+                static_cast<const T*>(V), nchunk, tpb, nz, pub, out);
 }
 
 template <typename T, int D>
-hipError_t select_dense_d(const float* scores, int64_t n, int rows, const float2* blkstat,
-                          int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
-                          double* lse, uint32_t* sel_mask, int n_v, const void* V, float* dpart,
-                          int nchunk, hipStream_t st) {
+hipError_t select_spec_d(const float* scores, int64_t n, int rows, const float2* blkstat,
+                         int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                         double* lse, uint32_t* sel_mask, int n_v, const void* V, int nchunk,
+                         CutPub* pub, float* out, hipStream_t st) {
   const int G = rows / n_v;
-#define CTOPK_SD(GB)                                                                            \
-  select_dense_t<T, D, GB>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse, sel_mask, \
-                           n_v, V, dpart, nchunk, st)
-  if (G == 1) return CTOPK_SD(1);
-  if (G == 2) return CTOPK_SD(2);
+#define CTOPK_SS(GB)                                                                           \
+  select_spec_t<T, D, GB>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse, sel_mask, \
+                          n_v, V, nchunk, pub, out, st)
+  if (G == 1) return CTOPK_SS(1);
+  if (G == 2) return CTOPK_SS(2);
   if constexpr (kGroupMax<T, D> == 4) {
-    return CTOPK_SD(4);
+    return CTOPK_SS(4);
   } else {
-    if (G <= 4) return CTOPK_SD(4);
-    return CTOPK_SD(8);
+    if (G <= 4) return CTOPK_SS(4);
+    return CTOPK_SS(8);
   }
-#undef CTOPK_SD
+#undef CTOPK_SS
 }
 
 }  // namespace
 
-int select_dense_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
+int select_spec_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
   // Rows held in registers by the widest register-row select, and at least
-  // half the compute units left beside the select's workgroups: the dense
-  // stream then takes at most about twice as long as a stream over the whole
-  // chip, which the select's own time covers.
+  // half the compute units left beside the select's workgroups: the stream
+  // then takes at most about twice as long as a stream over the whole chip,
+  // which the select's own time covers.  At most one workgroup per compute
+  // unit in total, so the whole launch is resident at once.
   if (n <= 16 * kResolveThreads || n > kResolveRegRow) return 0;
   const int spare = kNumCUs - rows;
   if (spare < kNumCUs / 2) return 0;
@@ -775,26 +1067,27 @@ int select_dense_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv) {
   if (want > tiles) want = tiles;
   if (want < 1) return 0;
   const int64_t tpb = ceil_div(tiles, want);
-  if (tpb * kVsumTile > kFixKeys) return 0;  // the tail pass lists a chunk in LDS
+  if (tpb * kVsumTile > kFixKeys) return 0;  // a chunk's correction list lives in LDS
   return static_cast<int>(ceil_div(tiles, tpb));
 }
 
-hipError_t launch_select_dense(const float* scores, int64_t n, int rows, const float2* blkstat,
-                               int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
-                               double* lse, uint32_t* sel_mask, int n_v, const void* V,
-                               int v_dtype, int dv, float* dpart, int nchunk, hipStream_t st) {
+hipError_t launch_select_spec(const float* scores, int64_t n, int rows, const float2* blkstat,
+                              int nblk, double eps, RowSel* rs, int32_t* k_eps, double* tau,
+                              double* lse, uint32_t* sel_mask, int n_v, const void* V,
+                              int v_dtype, int dv, int nchunk, CutPub* pub, float* out,
+                              hipStream_t st) {
   if (v_dtype == 1) {
     if (dv == 128)
-      return select_dense_d<uint16_t, 128>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau,
-                                           lse, sel_mask, n_v, V, dpart, nchunk, st);
-    return select_dense_d<uint16_t, 64>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
-                                        sel_mask, n_v, V, dpart, nchunk, st);
+      return select_spec_d<uint16_t, 128>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau,
+                                           lse, sel_mask, n_v, V, nchunk, pub, out, st);
+    return select_spec_d<uint16_t, 64>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
+                                        sel_mask, n_v, V, nchunk, pub, out, st);
   }
   if (dv == 128)
-    return select_dense_d<float, 128>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
-                                      sel_mask, n_v, V, dpart, nchunk, st);
-  return select_dense_d<float, 64>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
-                                   sel_mask, n_v, V, dpart, nchunk, st);
+    return select_spec_d<float, 128>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
+                                      sel_mask, n_v, V, nchunk, pub, out, st);
+  return select_spec_d<float, 64>(scores, n, rows, blkstat, nblk, eps, rs, k_eps, tau, lse,
+                                   sel_mask, n_v, V, nchunk, pub, out, st);
 }
 
 int resolve_register_row() { return kResolveRegRow; }

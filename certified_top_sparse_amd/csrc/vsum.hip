@@ -8,12 +8,12 @@
 //
 // Two ways to the same sums (HBM-bound either way):
 //   * after the select: vsum_kernel streams V once with each key's head
-//     weights (the stream body is in vsum_body.h);
-//   * beside the select (select.hip): a dense stream (every key, weights from
-//     the row maximum alone) runs in the select's own launch on the compute
-//     units the select leaves idle; tail_fix_kernel then turns each chunk's
-//     dense sums into head sums (dense minus the tail, or the head directly,
-//     per head group) and the finalize below combines them.
+//     weights (the stream body is in vsum_body.h) and the finalize below
+//     combines the chunks;
+//   * beside the select (select.hip): a stream over a provisional head runs in
+//     the select's own launch on the compute units the select leaves idle,
+//     corrects its sums by the keys between the provisional and the exact cut,
+//     and the last chunk of each head group combines the partials.
 // Chunk sums go to per-(head, chunk) partials, and finalize_kernel adds them
 // in chunk order in fp64 and writes out, so results are bitwise reproducible.
 
@@ -35,204 +35,10 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
     const RowSel* __restrict__ rs, float* __restrict__ part, int nchunk, int tpb) {
   constexpr int MODE = TAIL ? kStreamHeadTail : kStreamHead;
   __shared__ StreamSmem<T, D, GB, MODE, kVsumWaves> sm;
-  value_stream_block<T, D, GB, MODE, kVsumWaves>(sm, scores, n, G, V, rs, nullptr, 0, part,
+  value_stream_block<T, D, GB, MODE, kVsumWaves>(sm, scores, n, G, V, rs, part,
                                                  nchunk, tpb, static_cast<int>(blockIdx.x),
                                                  static_cast<int>(blockIdx.y),
                                                  static_cast<int>(blockIdx.z));
-}
-
-// Turns one chunk's dense sums into head sums, for the head group's mode
-// (group_tail_mode): each thread classifies its keys of the chunk (at most
-// kFixKeys) against every head's cut; the keys the mode needs are listed in
-// LDS in key order (a deterministic compaction), their V rows gathered, and
-//   tail mode: part = dense - sum over tail keys of w v (and of w);
-//   head mode: part = sum over head keys of w v (the dense sums go unused).
-// Writes part [rows, nchunk, D + 1] in the layout finalize_kernel reads.
-constexpr int kFixThreads = 512;
-constexpr int kFixWaves = kFixThreads / kWave;
-
-template <typename T, int D, int GB>
-__global__ __launch_bounds__(kFixThreads) void tail_fix_kernel(
-    const float* __restrict__ scores, int64_t n, int G, const T* __restrict__ V,
-    const RowSel* __restrict__ rs, const int32_t* __restrict__ k_eps,
-    const float* __restrict__ dpart, float* __restrict__ part, int nchunk, int tpb) {
-  using Acc = typename AccOf<T>::type;
-  constexpr int EPL = VSlice<T>::kElems;
-  constexpr int LPR = D / EPL;
-  constexpr int RPW = kWave / LPR;
-  constexpr int KPT = kFixKeys / kFixThreads;  // keys per thread
-  constexpr int STEP = kFixWaves * RPW;        // rows per workgroup and slot
-  // V rows in flight per lane: as many as the accumulators leave registers for
-  constexpr int kAccRegs = GB * EPL * static_cast<int>(sizeof(Acc)) / 4;
-  constexpr int ITER = kAccRegs <= 16 ? 16 : (sizeof(Acc) == 4 ? 8 : 4);
-  constexpr int NDP = (GB * (D + 1) + kFixThreads - 1) / kFixThreads;  // partials per thread
-  static_assert(kFixKeys % kFixThreads == 0, "whole keys per thread");
-  __shared__ int s_idx[kFixKeys];
-  __shared__ float s_w[kFixKeys][GB];
-  __shared__ uint32_t s_cnt[KPT][kFixWaves];
-  __shared__ Acc s_red[kFixWaves][GB * D];
-  __shared__ double s_ws[kFixWaves][GB];
-
-  const int chunk = blockIdx.x;
-  const int vh = blockIdx.y;
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
-  const int wave = t / kWave;
-  const int h0 = vh * G + static_cast<int>(blockIdx.z) * GB;
-  const int nh = min(GB, G - static_cast<int>(blockIdx.z) * GB);
-  const uint32_t vmask = (1u << nh) - 1u;
-  const int64_t c0 = static_cast<int64_t>(chunk) * tpb * kVsumTile;
-  // keys of this chunk (the host keeps tpb * kVsumTile <= kFixKeys and c0 < n)
-  const int len = static_cast<int>(min(n - c0, static_cast<int64_t>(tpb) * kVsumTile));
-
-  // Every load that does not depend on another is issued first: the chunk's
-  // dense partials (needed last), the heads' cuts and the keys' scores.
-  float dp[NDP];
-#pragma unroll
-  for (int k = 0; k < NDP; ++k) {
-    const int idx = min(t + k * kFixThreads, GB * (D + 1) - 1);
-    const int j = min(idx / (D + 1), nh - 1);
-    dp[k] = dpart[(static_cast<size_t>(h0 + j) * nchunk + chunk) * (D + 1) + idx % (D + 1)];
-  }
-  float sv[KPT][GB];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int64_t key = c0 + min(t + u * kFixThreads, len - 1);
-#pragma unroll
-    for (int j = 0; j < GB; ++j)
-      sv[u][j] = scores[static_cast<size_t>(h0 + min(j, nh - 1)) * static_cast<size_t>(n) + key];
-  }
-  uint64_t thr[GB];
-  float m[GB];
-#pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    const RowSel r = rs[h0 + min(j, nh - 1)];
-    thr[j] = r.thr;
-    m[j] = r.m;
-  }
-  const bool tail_mode = group_tail_mode(k_eps, h0, nh, n);  // workgroup-uniform
-
-  // Classify (bit j of hb: the key is in head j's head set) and list the
-  // keys the mode needs: local key i = u * 512 + 64 w + lane goes after every
-  // key of smaller (u, w) and the lower lanes of its wave.
-  uint32_t hb[KPT];
-  bool sel[KPT];
-  uint64_t bal[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int i = t + u * kFixThreads;
-    uint32_t bits = 0u;
-#pragma unroll
-    for (int j = 0; j < GB; ++j)
-      if (key64(sv[u][j], static_cast<uint32_t>(c0 + i)) >= thr[j]) bits |= 1u << j;
-    hb[u] = bits & vmask;
-    sel[u] = i < len && (tail_mode ? hb[u] != vmask : hb[u] != 0u);
-    bal[u] = __ballot(sel[u]);
-    if (lane == 0) s_cnt[u][wave] = static_cast<uint32_t>(__popcll(bal[u]));
-  }
-  __syncthreads();
-  double ws[GB];
-#pragma unroll
-  for (int j = 0; j < GB; ++j) ws[j] = 0.0;
-  uint32_t base = 0u;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    uint32_t before = 0u, all = 0u;
-#pragma unroll
-    for (int w = 0; w < kFixWaves; ++w) {
-      const uint32_t c = s_cnt[u][w];
-      before += w < wave ? c : 0u;
-      all += c;
-    }
-    if (sel[u]) {
-      const uint32_t slot =
-          base + before +
-          __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal[u] >> 32),
-                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[u]), 0u));
-      s_idx[slot] = t + u * kFixThreads;
-#pragma unroll
-      for (int j = 0; j < GB; ++j) {
-        const bool in_head = ((hb[u] >> j) & 1u) != 0u;
-        const bool take = j < nh && (tail_mode ? !in_head : in_head);
-        const float w = take ? weight(sv[u][j], m[j]) : 0.0f;
-        s_w[slot][j] = w;
-        ws[j] += static_cast<double>(w);
-      }
-    }
-    base += all;
-  }
-  const int L = static_cast<int>(base);
-  __syncthreads();
-
-  // Gather the listed V rows: entry e = k * STEP + RPW * wave + rg.
-  const int seg = lane % LPR;
-  const int rg = lane / LPR;
-  const T* Vb = V + static_cast<size_t>(vh) * static_cast<size_t>(n) * D;
-  Acc acc[GB][EPL];
-#pragma unroll
-  for (int j = 0; j < GB; ++j)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[j][e] = Acc(0);
-  for (int k0 = 0; k0 * STEP < L; k0 += ITER) {
-    uint4 u[ITER];
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int e = min((k0 + it) * STEP + RPW * wave + rg, L - 1);
-      const int64_t r = c0 + s_idx[e];
-      u[it] = *reinterpret_cast<const uint4*>(Vb + r * D + seg * EPL);
-    }
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int e = (k0 + it) * STEP + RPW * wave + rg;
-      const int ec = min(e, L - 1);
-      float v[EPL];
-      VSlice<T>::load(u[it], v);
-#pragma unroll
-      for (int j = 0; j < GB; ++j) {
-        const Acc w = e < L ? static_cast<Acc>(s_w[ec][j]) : Acc(0);
-#pragma unroll
-        for (int e2 = 0; e2 < EPL; ++e2) acc[j][e2] += w * static_cast<Acc>(v[e2]);
-      }
-    }
-  }
-
-  // Workgroup sums in a fixed order, then the chunk's head partial: the row
-  // groups of a wave by cross-lane adds (every lane ends with the sum), the
-  // waves through LDS.
-#pragma unroll
-  for (int j = 0; j < GB; ++j)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[j][e] = stride_sum<LPR>(acc[j][e]);
-  if (rg == 0) {
-#pragma unroll
-    for (int j = 0; j < GB; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_red[wave][j * D + seg * EPL + e] = acc[j][e];
-  }
-#pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    const double s = wave_sum_f64(ws[j]);
-    if (lane == 0) s_ws[wave][j] = s;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < NDP; ++k) {
-    const int idx = t + k * kFixThreads;
-    const int j = idx / (D + 1);
-    const int e = idx - j * (D + 1);
-    if (idx < GB * (D + 1) && j < nh) {
-      double sum = 0.0;
-      if (e < D) {
-#pragma unroll
-        for (int w = 0; w < kFixWaves; ++w) sum += static_cast<double>(s_red[w][j * D + e]);
-      } else {
-#pragma unroll
-        for (int w = 0; w < kFixWaves; ++w) sum += s_ws[w][j];
-      }
-      const size_t off = (static_cast<size_t>(h0 + j) * nchunk + chunk) * (D + 1) + e;
-      part[off] = static_cast<float>(tail_mode ? static_cast<double>(dp[k]) - sum : sum);
-    }
-  }
 }
 
 // out[h, e] = sum_c part[h, c, e] / sum_c part[h, c, dv], fp64 sums in a fixed
@@ -494,54 +300,7 @@ hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const voi
   }
 }
 
-template <typename T, int D, int GB>
-hipError_t fix_t(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                 const RowSel* rs, const int32_t* k_eps, const float* dpart, float* part,
-                 int nchunk, float* out, hipStream_t st) {
-  const int G = rows / n_v;
-  const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
-  dim3 grid(nchunk, n_v, static_cast<unsigned>(ceil_div(G, GB)));
-  const hipError_t e = launch(tail_fix_kernel<T, D, GB>, grid, dim3(kFixThreads), 0, st, scores,
-                              n, G, static_cast<const T*>(V), rs, k_eps, dpart, part, nchunk, tpb);
-  if (e != hipSuccess) return e;
-  return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, static_cast<const float*>(part),
-                nchunk, D, 1, out, static_cast<float*>(nullptr), static_cast<double*>(nullptr));
-}
-
-template <typename T, int D>
-hipError_t fix_d(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                 const RowSel* rs, const int32_t* k_eps, const float* dpart, float* part,
-                 int nchunk, float* out, hipStream_t st) {
-  const int G = rows / n_v;
-#define CTOPK_FIX(GB) \
-  fix_t<T, D, GB>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st)
-  if (G == 1) return CTOPK_FIX(1);
-  if (G == 2) return CTOPK_FIX(2);
-  if constexpr (kGroupMax<T, D> == 4) {
-    return CTOPK_FIX(4);
-  } else {
-    if (G <= 4) return CTOPK_FIX(4);
-    return CTOPK_FIX(8);
-  }
-#undef CTOPK_FIX
-}
-
 }  // namespace
-
-hipError_t launch_tail_fix(const float* scores, int64_t n, int rows, int n_v, const void* V,
-                           int v_dtype, int dv, const RowSel* rs, const int32_t* k_eps,
-                           const float* dpart, float* part, int nchunk, float* out,
-                           hipStream_t st) {
-  if (v_dtype == 1) {
-    if (dv == 128)
-      return fix_d<uint16_t, 128>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out,
-                                  st);
-    return fix_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st);
-  }
-  if (dv == 128)
-    return fix_d<float, 128>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st);
-  return fix_d<float, 64>(scores, n, rows, n_v, V, rs, k_eps, dpart, part, nchunk, out, st);
-}
 
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
                        int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,

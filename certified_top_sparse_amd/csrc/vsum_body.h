@@ -1,5 +1,6 @@
 // The value stream's per-workgroup body, shared by the stand-alone value
-// stream kernel and by the kernel that runs the select beside a dense stream.
+// stream kernel and by the kernel that runs the select beside a stream over
+// provisional heads.
 //
 // A workgroup of NW waves owns up to GB query heads of one V head and `tpb`
 // consecutive tiles of kVsumTile keys; each wave streams its kVsumTile / NW
@@ -64,9 +65,13 @@ template <typename T, int D>
 constexpr int kGroupMax = (sizeof(typename AccOf<T>::type) == 8 && D == 128) ? 4 : 8;
 
 // What a stream sums: the head only (weights of keys outside the head are
-// 0); head and tail separately; or every key (the untruncated numerator,
-// which needs only the row maximum, so it can run before the select ends).
-enum StreamMode { kStreamHead = 0, kStreamHeadTail = 1, kStreamDense = 2 };
+// 0); head and tail separately; or the keys at or above per-head thresholds
+// the caller puts in StreamSmem::thr (a provisional head, with the row maxima
+// in StreamSmem::m), whose scores are also copied to the caller's LDS array
+// `stash` ([GB][kFixKeys], by the key's place in the chunk; chunks of at most
+// kFixKeys keys) and whose lane sums go to the hook alone: the hook finishes
+// them, and no partials are written.
+enum StreamMode { kStreamHead = 0, kStreamHeadTail = 1, kStreamGiven = 3 };
 
 template <typename T, int D, int GB, int MODE, int NW>
 struct StreamShape {
@@ -89,7 +94,8 @@ struct StreamSmem {
   typename S::Acc red[S::NS][NW][GB * D];
   double wsum[S::NS][NW][GB];
   float w[NW][S::PASS][GB];  // wave-private weight staging
-  float mx[GB][NW];          // dense mode: per-wave maxima of the row maxima
+  uint64_t thr[GB];          // given mode: key64 thresholds per head
+  float m[GB];               // given mode: row maxima per head
 };
 
 // What a lane holds when the stream loop ends: acc[j][e] sums w v for head
@@ -107,39 +113,18 @@ struct NoHook {
   __device__ __forceinline__ void operator()(L&) const {}
 };
 
-// Per head group (GB query heads of one V head), the dense stream's sums turn
-// into head sums one of two ways, fixed for the whole group from the select's
-// head sizes k_j (so every workgroup makes the same choice without a pass
-// over the keys):
-//   tail sums: head = dense - sum over tail keys of w v (and of w); taken
-//              when the tails together hold no more keys than the largest
-//              head, so the V rows gathered are at most those of the head;
-//   head sums: head = sum over head keys of w v (the dense sums go unused).
-__device__ __forceinline__ bool group_tail_mode(const int32_t* __restrict__ k_eps, int h0, int nh,
-                                                int64_t n) {
-  int64_t tails = 0, kmax = 0;
-  for (int j = 0; j < nh; ++j) {
-    const int64_t k = k_eps[h0 + j];
-    tails += n - k;
-    kmax = k > kmax ? k : kmax;
-  }
-  return tails <= kmax;
-}
-
 // One workgroup of the stream: chunk `chunk` of V head `vh`, query heads
 // vh * G + hz * GB + [0, GB).  Head and tail modes take each head's maximum
-// and cut from rs; the dense mode takes the maximum from the score scan's
-// per-tile (min, max) pairs (blkstat, nblk per row), which is exactly the
-// row maximum the select uses.  `hook` sees every lane's sums (StreamLane)
+// and cut from rs; the given mode takes them from StreamSmem.  `hook` sees every lane's sums (StreamLane)
 // after the stream and before the workgroup reduction and may change them.
 // Partials: part[(head, chunk)] holds NS blocks of [D numerators | weight
 // sum].
 template <typename T, int D, int GB, int MODE, int NW, typename Hook = NoHook>
 __device__ __forceinline__ void value_stream_block(
     StreamSmem<T, D, GB, MODE, NW>& sm, const float* __restrict__ scores, int64_t n, int G,
-    const T* __restrict__ V, const RowSel* __restrict__ rs, const float2* __restrict__ blkstat,
-    int nblk, float* __restrict__ part, int nchunk, int tpb, int chunk, int vh, int hz,
-    Hook hook = Hook()) {
+    const T* __restrict__ V, const RowSel* __restrict__ rs, float* __restrict__ part, int nchunk,
+    int tpb, int chunk, int vh, int hz,
+    Hook hook = Hook(), float* stash = nullptr) {
   using S = StreamShape<T, D, GB, MODE, NW>;
   using Acc = typename S::Acc;
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, PASS = S::PASS, ITER = S::ITER;
@@ -161,21 +146,9 @@ __device__ __forceinline__ void value_stream_block(
   const int hw = lane % GB;
   uint64_t thr = ~0ull;
   float m = 0.0f;
-  if constexpr (MODE == kStreamDense) {
-    thr = 0ull;  // every key is kept
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-      const float2* bs = blkstat + static_cast<size_t>(h0 + min(j, nh - 1)) * nblk;
-      float v = -INFINITY;
-      for (int b = t; b < nblk; b += NT) v = fmaxf(v, bs[b].y);
-      v = wave_max_dpp(v);
-      if (lane == 0) sm.mx[j][wave] = v;
-    }
-    __syncthreads();
-    float mj = sm.mx[hw][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) mj = fmaxf(mj, sm.mx[hw][w]);
-    m = mj;
+  if constexpr (MODE == kStreamGiven) {
+    thr = hw < nh ? sm.thr[hw] : ~0ull;
+    m = sm.m[hw];
   } else {
     // That head's selection parameters are read with workgroup-uniform addresses.
 #pragma unroll
@@ -236,6 +209,9 @@ __device__ __forceinline__ void value_stream_block(
           const float w = kept ? weight(s[q], m) : 0.0f;
           wsum += static_cast<double>(w);
           sm.w[wave][key][hw] = w;
+          if constexpr (MODE == kStreamGiven) {  // the chunk's scores, kept for the caller
+            if (r < n) stash[hw * kFixKeys + tb * kVsumTile + wave * PASS + key] = s[q];
+          }
         }
       }
     }
@@ -277,6 +253,7 @@ __device__ __forceinline__ void value_stream_block(
     StreamLane<T, D, GB> ln{acc, wsum, m};
     hook(ln);
   }
+  if constexpr (MODE == kStreamGiven) return;  // the hook finished the sums
 
   // Workgroup sums: row groups of a wave (lanes that share lane % LPR, by
   // cross-lane adds), then the waves in order through LDS.

@@ -172,13 +172,14 @@ CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
  *   CTOPK_PLAN_DECODE: score scan; level-0 histogram (only for rows of more
  *     than 32768 keys); select; value stream over the head; combine;
  *   CTOPK_PLAN_DECODE_OVERLAP: score scan; one launch in which the select runs
- *     beside a dense value stream (sum of w v over every key, which needs only
- *     the row maximum); tail pass (per chunk of keys: the dense sums minus the
- *     tail keys' w v or, for head groups whose heads are short, the head keys'
- *     w v directly); combine.  Taken for decode rows of 16385..32768 keys when
- *     at least half of the compute units (128) remain beside one workgroup per
- *     query row and the dense stream's chunks hold at most 2048 keys, and
- *     never for calls that ask for out_err or out_dense;
+ *     beside the value stream: each stream workgroup guesses every head's cut
+ *     from a sample of the scores, sums w v over the keys above its guess while
+ *     the select runs, then waits for the select's exact cut, corrects its sums
+ *     by the keys between the guess and the cut, and the last workgroup of
+ *     each head group combines the chunks into out.  Taken for decode rows of
+ *     16385..32768 keys when at least half of the compute units (128) remain
+ *     beside one workgroup per query row and the stream's chunks hold at most
+ *     2048 keys, and never for calls that ask for out_err or out_dense;
  *   CTOPK_PLAN_DECODE_BOUND (calls with CTOPK_FLAG_BOUND): score scan with
  *     per-block masses; the blockwise bound (one workgroup per row, in place
  *     of the select); value stream over the kept keys; combine.
@@ -314,8 +315,9 @@ CTOPK_API size_t ctopk_k4_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t 
  * plan (ctopk_plan); the decode plans take the score scan's pair, then the
  * level-0 histogram's (when the plan launches none, its pair is recorded back
  * to back on the stream and measures only the stream's own gap between the
- * two records, not a kernel), then one pair per remaining kernel (three in
- * every decode plan).  Logits
+ * two records, not a kernel), then one pair per remaining kernel (select,
+ * value stream and combine in the decode and bound plans; the one launch of
+ * select and stream in the overlapped plan).  Logits
  * path: select, value stream, output combine.  Candidates: 4-bit scan, then
  * rescoring with the counts.  Kernels past count/2 pairs run
  * without events; pairs left over are

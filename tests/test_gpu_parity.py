@@ -180,19 +180,30 @@ def test_caller_workspace_matches_cached(ct):
     assert np.allclose(a["tau"], b["tau"], rtol=1e-14, atol=0)
 
 
-def test_determinism(ct):
-    wl = workloads.gqa_decode(n=20000)
-    _say("determinism gqa_decode n=20000")
+@pytest.mark.parametrize("n", [20000, 40000])
+def test_determinism(ct, n):
+    # k, the head and tau repeat bit for bit on every plan; out too on the
+    # serial plan (n = 40000), and to fp32 rounding of its per-chunk terms on
+    # the overlapped one (n = 20000), which adds them with float atomics in
+    # arrival order
+    wl = workloads.gqa_decode(n=n)
+    overlap = plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_OVERLAP
+    assert overlap == (n <= 32768)
+    _say(f"determinism gqa_decode n={n}")
     a = run_decode(ct, wl, 0.01)
     b = run_decode(ct, wl, 0.01)
-    for key in ("k_eps", "out", "sel_mask"):
+    for key in ("k_eps", "sel_mask"):
         assert np.array_equal(a[key], b[key])
     assert np.allclose(a["tau"], b["tau"], rtol=1e-13, atol=0)
+    if overlap:
+        assert rel_l2(a["out"], b["out"]).max() <= 1e-6
+    else:
+        assert np.array_equal(a["out"], b["out"])
 
 
 # ---------------------------------------------------------------------------
-# overlapped plan: the select beside a dense value stream, then the tail
-# correction (dense minus tail, or the head directly, per chunk)
+# overlapped plan: the select beside a value stream over guessed heads, each
+# chunk corrected by the keys between its guess and the exact cut
 # ---------------------------------------------------------------------------
 def plan_of(ct, wl):
     q, K, V = dev(wl["q"][:1]), dev(wl["K"][:1, :1]), dev(wl["V"][:1, :1])
@@ -222,11 +233,36 @@ def test_overlap_shapes(ct, d, dtype, G):
 
 @pytest.mark.parametrize("eps", [0.001, 0.3, 0.9])
 def test_overlap_eps(ct, eps):
-    # small eps: short tails (chunks subtract the tail from the dense sums);
-    # large eps: small heads (chunks sum the head directly)
+    # small eps: short tails; large eps: small heads (the guess and the cut
+    # sit far down and far up the score range)
     wl = workloads.gqa_decode(n=24577, temp_range=(0.5, 4.0))
     assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_OVERLAP
     check_decode(ct, wl, eps, "overlap gqa_decode n=24577")
+
+
+@pytest.mark.parametrize("eps", [0.01, 0.5])
+def test_overlap_guess_far_from_the_cut(ct, eps):
+    # The stream guesses each head's cut from 1024 evenly spaced scores.  Here
+    # nearly all of the mass sits in 40 keys per head that the sample never
+    # sees, so the guess keeps almost every key and the correction must take
+    # out nearly a whole chunk's worth of keys per head.
+    n, G, n_kv, d = 20000, 4, 2, 64
+    rng = np.random.default_rng(91)
+    sampled = set((np.arange(1024) * n // 1024).tolist())
+    free = np.array([i for i in range(n) if i not in sampled])
+    q = np.zeros((G * n_kv, d), dtype=np.float32)
+    K = (rng.standard_normal((n_kv, n, d)) * 0.05).astype(np.float32)
+    V = rng.standard_normal((n_kv, n, d)).astype(np.float32)
+    for h in range(G * n_kv):
+        q[h, h] = 8.0
+        pos = rng.choice(free, size=40, replace=False)
+        K[h // G, pos, h] = 12.0 + rng.standard_normal(40).astype(np.float32)
+    wl = {"q": workloads.bf16_rne(q), "K": workloads.bf16_rne(K), "V": workloads.bf16_rne(V),
+          "head_scale": np.full(G * n_kv, np.float32(1.0 / 8.0), dtype=np.float32),
+          "n_q_heads": G * n_kv, "n_kv_heads": n_kv, "n": n, "d": d, "dtype": "bf16"}
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_OVERLAP
+    g, ref, S = check_decode(ct, wl, eps, "overlap, guess far from the cut")
+    assert (ref["k_eps"] <= 40).all()
 
 
 def test_overlap_smallest_row(ct):
