@@ -657,15 +657,15 @@ __device__ __forceinline__ void resolve_row(
     __syncthreads();
   }
   const uint64_t thr = sh.thr;
-  // Other workgroups of the launch may wait for the cut: the head's mass,
-  // then the cut, with device-scope stores, the second only after the first
-  // has completed (both non-zero: the head holds the row maximum, and every
-  // finite score's key64 has a non-zero upper word).
+  // Other workgroups of the launch may wait for the cut: the head's mass and
+  // the cut, with device-scope stores.  Both words are zero before and
+  // non-zero after (the head holds the row maximum, and every finite score's
+  // key64 has a non-zero upper word), and each has this one writer, so a
+  // reader that sees both non-zero has both final values, in either order.
   if (publish != nullptr && t == 0) {
     const double den = Z - R;
     __hip_atomic_store(&publish->den, den > 0.0 ? den : 1.0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
     __hip_atomic_store(&publish->cut, thr != 0ull ? thr : 1ull, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -718,13 +718,15 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
 //      (w = exp(s - m), m the row maximum from the scan's tile pairs, the same
 //      m and weights the select uses), keeping the chunk's scores in LDS,
 //      while the select runs;
-//   3. wait for the published mass and cut (a bounded spin on pub[]; the
-//      select workgroups have the lowest ids, so they were dispatched first,
-//      and they wait on nothing) and add, signed, w v of the keys between the
-//      two thresholds (+ for head keys the guess left out, - for the others;
-//      listed in key order in LDS), so the lane sums become the head's sums;
-//   4. reduce them over the workgroup and add num / den into out with
-//      device-scope float atomics (out is zeroed before the launch).
+//   3. reduce those sums over the workgroup (fp64 per head and V element)
+//      while the select may still run, then wait for the published mass and
+//      cut (a bounded spin on pub[]; the select workgroups have the lowest
+//      ids, so they were dispatched first, and they wait on nothing);
+//   4. sum, signed, w v of the keys between the two thresholds (+ for head
+//      keys the guess left out, - for the others; listed in key order in LDS
+//      and packed into as few waves as possible), add that to the reduced
+//      sums and add num / den into out with device-scope float atomics (out
+//      is zeroed before the launch).
 // out is thus a sum of one term per chunk in arrival order: reproducible to
 // fp32 rounding of those terms, not bit for bit.  A timed-out wait adds NaN.
 // pub[] and out must be zero at launch (the score scan zeroes both).
@@ -745,6 +747,7 @@ struct SpecSmem {
   };
   float stash[GB * kFixKeys];  // the chunk's scores, [head][key in chunk]
   float mx[GB][kResolveWaves];
+  double pre[GB * D];  // the provisional head's sums, per (head, V element)
   uint64_t spec[GB];
   uint64_t exact[GB];
   double den[GB];
@@ -771,7 +774,28 @@ struct SpecFinish {
     constexpr int EPL = VSlice<T>::kElems, LPR = D / EPL, RPW = kWave / LPR, STEP = NW * RPW;
     static_assert(kFixKeys % NT == 0, "whole keys per thread");
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    const int seg = lane % LPR, rg = lane / LPR;
     __syncthreads();  // every wave is past its stream loop: the staging LDS is free
+    // The provisional head's sums over the workgroup, while the select may
+    // still run: the row groups of a wave by cross-lane adds, then the waves
+    // in order through LDS, in fp64 per (head, V element).
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
+    if (rg == 0) {
+#pragma unroll
+      for (int j = 0; j < GB; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sm->v.red[0][wave][j * D + seg * EPL + e] = ln.acc[j][e];
+    }
+    __syncthreads();
+    for (int col = t; col < nh * D; col += NT) {
+      double sum = 0.0;
+#pragma unroll
+      for (int g = 0; g < NW; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
+      sm->pre[col] = sum;
+    }
     if (t < nh) {
       // Both words non-zero: both stores have landed (each word has one
       // writer, and zero is only its value before that store).
@@ -840,21 +864,28 @@ struct SpecFinish {
     }
     const int nb = static_cast<int>(base);
     __syncthreads();
-    // Gather the listed V rows into this lane's sums (entry e = k STEP +
-    // RPW wave + rg).
-    const int seg = lane % LPR, rg = lane / LPR;
+    // The listed V rows, signed, into fresh lane sums.  Entry e goes to wave
+    // (e / PER) % NW, load it = (e % PER) / RPW of a round, row group
+    // e % RPW, so a short list occupies few waves; the others skip the
+    // reduction below.
     constexpr int ITB = 4;
-    for (int k0 = 0; k0 * STEP < nb; k0 += ITB) {
+    constexpr int PER = ITB * RPW;
+    const int nwb = min(NW, (nb + PER - 1) / PER);
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ln.acc[j][e] = Acc(0);
+    for (int k0 = wave * PER; k0 < nb; k0 += NW * PER) {
       uint4 u[ITB];
 #pragma unroll
       for (int it = 0; it < ITB; ++it) {
-        const int e = min((k0 + it) * STEP + RPW * wave + rg, nb - 1);
+        const int e = min(k0 + it * RPW + rg, nb - 1);
         const int64_t r = c0 + sm->band.idx[e];
         u[it] = *reinterpret_cast<const uint4*>(V + r * D + seg * EPL);
       }
 #pragma unroll
       for (int it = 0; it < ITB; ++it) {
-        const int e = (k0 + it) * STEP + RPW * wave + rg;
+        const int e = k0 + it * RPW + rg;
         const bool valid = e < nb;
         const int ec = min(e, nb - 1);
         float v[EPL];
@@ -867,14 +898,16 @@ struct SpecFinish {
         }
       }
     }
-    // Workgroup sums: the row groups of a wave by cross-lane adds, then the
-    // waves in order through LDS; each column's num / den into out.
+    // The band's sums over the waves that hold entries, added to the
+    // provisional ones; each column's num / den into out.
+    if (wave < nwb) {
 #pragma unroll
-    for (int j = 0; j < GB; ++j)
+      for (int j = 0; j < GB; ++j)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
+        for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
+    }
     __syncthreads();  // the list is read: its LDS takes the reduction
-    if (rg == 0) {
+    if (wave < nwb && rg == 0) {
 #pragma unroll
       for (int j = 0; j < GB; ++j)
 #pragma unroll
@@ -883,9 +916,8 @@ struct SpecFinish {
     __syncthreads();
     for (int col = t; col < nh * D; col += NT) {
       const int j = col / D;
-      double sum = 0.0;
-#pragma unroll
-      for (int g = 0; g < NW; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
+      double sum = sm->pre[col];
+      for (int g = 0; g < nwb; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
       unsafeAtomicAdd(out + static_cast<size_t>(h0 + j) * D + (col - j * D),
                       static_cast<float>(sum / sm->den[j]));
     }
