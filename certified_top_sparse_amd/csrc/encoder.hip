@@ -8,9 +8,10 @@
 // at most eps, tau is that mass, and the output is the softmax average of V
 // over the head, renormalised over the head.
 //
-// One workgroup = 8 wavefronts = 64 query rows of one KV head: four row
+// One workgroup = 4 wavefronts = 32 query rows of one KV head: two row
 // groups of 16 rows, each row's keys split into two halves of NT / 2 tiles,
-// one wave per (row group, half).  Lane (r, g) = (lane % 16, lane / 16) of a
+// one wave per (row group, half).  About 49 KiB of LDS and up to 256 VGPRs
+// (the scores stay in registers), so two workgroups share a CU.  Lane (r, g) = (lane % 16, lane / 16) of a
 // wave holds row r and the keys kh * 8 NT + 16 t + 4 g + e (t < NT / 2, e < 4),
 // which is the fp32 result layout of a 16x16x32 bf16 MFMA computing
 // S^T = K Q^T.  A row's scores therefore live in four lanes of each of two
@@ -37,9 +38,10 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kEncWaves = 8;              // 4 row groups x 2 key halves
+constexpr int kEncGroups = 2;             // row groups of 16 rows
+constexpr int kEncWaves = 2 * kEncGroups; // x 2 key halves
 constexpr int kEncThreads = kEncWaves * kWave;
-constexpr int kEncRows = 64;              // query rows per workgroup
+constexpr int kEncRows = 16 * kEncGroups; // query rows per workgroup
 constexpr int kEncMaxKeys = 512;
 constexpr int kEncMinGroup = 64;
 constexpr int kEncBins = 64;              // bins per row and level
@@ -63,7 +65,11 @@ struct GroupXchg {  // per-row values the two waves of a row group exchange
   int lcnt[2][kWave];  // candidates per lane
   uint32_t bm[16][16]; // candidate bitmap per row (tied scores)
 };
-constexpr int kEncSmem = 4 * static_cast<int>(sizeof(GroupSel));
+// The K and V stages (at most 2 x 128 x 72 bf16) share the buffer with the
+// select scratch of the row groups.
+constexpr int kEncStage = 2 * 128 * 72 * 2;
+constexpr int kEncSelect = kEncGroups * static_cast<int>(sizeof(GroupSel));
+constexpr int kEncSmem = kEncSelect > kEncStage ? kEncSelect : kEncStage;
 
 template <int D>
 struct Geo {
@@ -74,7 +80,7 @@ static_assert(2 * Geo<64>::kChunk * Geo<64>::kKStride * 2 <= kEncSmem, "K stage"
 static_assert(2 * 64 * (Geo<64>::kChunk + 8) * 2 <= kEncSmem, "V stage");
 static_assert(2 * Geo<128>::kChunk * Geo<128>::kKStride * 2 <= kEncSmem, "K stage");
 static_assert(2 * 128 * (Geo<128>::kChunk + 8) * 2 <= kEncSmem, "V stage");
-static_assert(4 * 16 * 128 * 4 <= kEncSmem, "half combine");
+static_assert(kEncGroups * 16 * 128 * 4 <= kEncSmem, "half combine");
 
 // Reductions over the four lanes (r, 0..3) of a row within one wave (lanes
 // r + 16 g), with the cross-row swaps; every lane of the wave must be active.
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int VS = CK + 8;                              // bf16 per staged V^T row
   static_assert(H % CK == 0 && TPC % 2 == 0, "chunking");
   __shared__ __align__(16) unsigned char smem[kEncSmem];
-  __shared__ GroupXchg xs[4];
+  __shared__ GroupXchg xs[kEncGroups];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rg = wave >> 1, kh = wave & 1;  // row group, key half
@@ -297,12 +303,10 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
 
     // The bin holding the cut: the largest b whose mass below is <= thr.
-    double hl[16], S = 0.0;
+    // (the lane's 16 bins are read twice from LDS rather than held in registers)
+    double S = 0.0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      hl[j] = hrow[16 * g + j];
-      S += hl[j];
-    }
+    for (int j = 0; j < 16; ++j) S += hrow[16 * g + j];
     // the row's partial sums of the four lanes g = 0..3, in every lane
     const double Sx = xor_lane<16>(S);               // lane g ^ 1
     const double Sa = (g & 1) ? Sx : S;              // lane g & 2
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
         best = 16 * g + j;
         bestP = Pc;
       }
-      Pc += hl[j];
+      Pc += hrow[16 * g + j];
     }
     {
       const int ob = xor_lane<16>(best);
