@@ -318,16 +318,27 @@ struct RowElems {
     sr = row;
     n = len;
     if constexpr (PT > 0) {  // n <= PT * kResolveThreads: 32-bit indices
-      const int last = static_cast<int>(len) - 1;
+      // Slots past n hold a copy of element i mod P, P the largest power of
+      // two <= n: their zero contributions then fall into bins spread like
+      // the row's own instead of queueing on one bin's atomics.
+      const int nn = static_cast<int>(len);
+      if (nn == PT * kResolveThreads) {
 #pragma unroll
-      for (int u = 0; u < PT; ++u)
-        v[u] = row[min(u * kResolveThreads + static_cast<int>(threadIdx.x), last)];
+        for (int u = 0; u < PT; ++u) v[u] = row[u * kResolveThreads + static_cast<int>(threadIdx.x)];
+      } else {
+        const int pmask = (1 << (31 - __clz(nn))) - 1;
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+          const int i = u * kResolveThreads + static_cast<int>(threadIdx.x);
+          v[u] = row[i < nn ? i : (i & pmask)];
+        }
+      }
     }
   }
 
   // As for_each, but every slot of a register row is visited without a
   // branch: f(i, s, valid), where slots past n (valid false) hold a copy of
-  // the row's last element and must contribute nothing.
+  // an element of the row and must contribute nothing.
   template <typename F>
   __device__ __forceinline__ void for_each_all(F&& f) {
     if constexpr (PT > 0) {
