@@ -377,6 +377,13 @@ __device__ __forceinline__ int lin_bin(float s, float lo, float inv) {
   return x < static_cast<float>(kBins) ? static_cast<int>(x) : kBins - 1;
 }
 
+// lin_bin for scores that may lie below lo (a range not taken from the row's
+// own minimum): those fall into bin 0.  Equal to lin_bin for s >= lo.
+__device__ __forceinline__ int lin_bin_clamped(float s, float lo, float inv) {
+  const float x = fmaxf((s - lo) * inv, 0.0f);
+  return x < static_cast<float>(kBins) ? static_cast<int>(x) : kBins - 1;
+}
+
 // Cooperative zeroing of a byte range by all blocks of a grid (16-byte units).
 __device__ __forceinline__ void zero_slice(void* base, size_t bytes, size_t block_linear,
                                            size_t nblocks) {

@@ -44,6 +44,9 @@ constexpr int kReadBatch = 16;
 constexpr int kSmallCand = 64;
 // Rows up to this length are held in registers by their block (32 per thread).
 constexpr int kResolveRegRow = 32 * kResolveThreads;
+// A sampled weight reference may lie this far below the row maximum: fp32
+// weights stay below e^80 and their fp64 sums far from overflow.
+constexpr float kSampledHeadroom = 80.0f;
 
 // Row (min, max) from per-tile pairs, reduced identically by every block.
 __device__ float2 row_minmax(const float2* __restrict__ bs, int nblk, float2* s_red) {
@@ -414,29 +417,52 @@ __device__ __forceinline__ void resolve_row(
     sh.kmax = 0ull;
   }
 
-  // Row (min, max).
+  // The level-0 range [lo, hi] and the weight reference m.  From the scan's
+  // tile pairs or a pass over a register row these are the row's minimum and
+  // maximum.  A row streamed from memory without tile pairs takes them from
+  // a strided sample of one key per thread, widened by half the sample's
+  // span on each side (keys outside fall into the end bins), so that level 0
+  // is its first pass over the row; that pass also finds the row's true
+  // maximum and minimum, and is redone over them if the maximum lies so far
+  // above the reference that weights could overflow.
+  auto block_minmax = [&](float vmin, float vmax) -> float2 {
+    vmax = wave_max_dpp(vmax);
+    vmin = -wave_max_dpp(-vmin);
+    if (lane == 0) sh.mm[wave] = make_float2(vmin, vmax);
+    __syncthreads();
+    float2 r = sh.mm[0];
+    for (int w = 1; w < kResolveWaves; ++w) {
+      r.x = fminf(r.x, sh.mm[w].x);
+      r.y = fmaxf(r.y, sh.mm[w].y);
+    }
+    __syncthreads();  // sh.mm is free again
+    return r;
+  };
+  const bool sampled = PT == 0 && blkstat == nullptr && npart == 0;
   float2 mm;
+  float m;
   if (blkstat != nullptr) {
     mm = row_minmax(blkstat + static_cast<size_t>(row) * nblk, nblk, sh.mm);
+    m = mm.y;
+  } else if (sampled) {
+    const int64_t stride = n > kResolveThreads ? n / kResolveThreads : 1;
+    const float sv = sr[min(static_cast<int64_t>(t) * stride, n - 1)];
+    mm = block_minmax(sv, sv);
+    m = mm.y;
+    const float half = 0.5f * (mm.y - mm.x);
+    mm.x -= half;
+    mm.y += half;
   } else {
     float vmax = -INFINITY, vmin = INFINITY;
     E.for_each([&](int64_t, float s) {
       vmax = fmaxf(vmax, s);
       vmin = fminf(vmin, s);
     });
-    vmax = wave_max_dpp(vmax);
-    vmin = -wave_max_dpp(-vmin);
-    if (lane == 0) sh.mm[wave] = make_float2(vmin, vmax);
-    __syncthreads();
-    mm = sh.mm[0];
-    for (int w = 1; w < kResolveWaves; ++w) {
-      mm.x = fminf(mm.x, sh.mm[w].x);
-      mm.y = fmaxf(mm.y, sh.mm[w].y);
-    }
+    mm = block_minmax(vmin, vmax);
+    m = mm.y;
   }
-  const float m = mm.y;
-  const float lo = mm.x;
-  const float inv = lin_scale(lo, m);
+  float lo = mm.x;
+  float inv = lin_scale(lo, mm.y);
 
   // Level-0 histogram of masses: sum of the partials in chunk order, or a
   // pass over the row (one LDS atomic per key; counts come from the pass
@@ -456,6 +482,23 @@ __device__ __forceinline__ void resolve_row(
           if (p0 + u < npart) ms += mv[u];
       }
       sh.hm[b] = ms;
+    }
+  } else if (sampled) {
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int b = t; b < kBins; b += kResolveThreads) sh.hm[b] = 0.0;
+      __syncthreads();
+      float vmax = -INFINITY, vmin = INFINITY;
+      E.for_each([&](int64_t, float s) {
+        vmax = fmaxf(vmax, s);
+        vmin = fminf(vmin, s);
+        atomicAdd(&sh.hm[lin_bin_clamped(s, lo, inv)], static_cast<double>(weight(s, m)));
+      });
+      const float2 tr = block_minmax(vmin, vmax);
+      if (pass == 1 || tr.y - m <= kSampledHeadroom) break;
+      // every thread saw the same tr: the redo is uniform over the block
+      lo = tr.x;
+      m = tr.y;
+      inv = lin_scale(lo, m);
     }
   } else {
     for (int b = t; b < kBins; b += kResolveThreads) sh.hm[b] = 0.0;

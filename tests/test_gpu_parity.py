@@ -402,6 +402,48 @@ def test_cut_bin_straddles_zero(ct, n):
         _logits_case(ct, L, V, eps, f"cut bin straddles zero n={n}")
 
 
+def _unsampled(n):
+    """Positions a streamed row's level-0 sample never reads (the sample takes
+    key t * (n // 1024) for t < 1024)."""
+    mask = np.ones(n, dtype=bool)
+    mask[np.arange(1024) * max(n // 1024, 1)] = False
+    return np.flatnonzero(mask)
+
+
+@pytest.mark.parametrize("lift", [50.0, 150.0])
+def test_streamed_row_maximum_far_above_the_sample(ct, lift):
+    """Rows streamed from memory take their level-0 range and weight reference
+    from a sample; a maximum `lift` above every sampled key either stays within
+    the weights' headroom (50) or forces level 0 to be redone over the row's
+    true range (150)."""
+    rng = np.random.default_rng(int(lift))
+    n = 40000
+    L = rng.standard_normal((4, n)).astype(np.float32)
+    off = _unsampled(n)
+    L[0, off[123]] = lift
+    L[1, off[5000]] = lift - 1.0
+    L[1, off[5001]] = lift - 1.5
+    L[2, off[-1]] = lift
+    L[3, off[:50]] = lift + rng.standard_normal(50).astype(np.float32)  # a head of 50
+    V = rng.standard_normal((1, n, 64)).astype(np.float32)
+    for eps in (0.01, 0.4):
+        _logits_case(ct, L, V, eps, f"streamed row, max {lift} above the sample")
+
+
+def test_streamed_row_cut_below_the_sampled_range(ct):
+    """Keys far below every sampled key fall into the first level-0 bin; with
+    a tiny eps the cut lies among them, so that bin is resolved by the digit
+    levels over the whole row."""
+    rng = np.random.default_rng(11)
+    n = 65536
+    L = rng.standard_normal((2, n)).astype(np.float32)
+    off = _unsampled(n)
+    L[:, off] = (-30.0 + rng.standard_normal((2, off.size))).astype(np.float32)
+    V = rng.standard_normal((1, n, 64)).astype(np.float32)
+    for eps in (1e-12, 1e-11, 0.2):
+        _logits_case(ct, L, V, eps, "streamed row, cut below the sampled range")
+
+
 def test_single_key_rows(ct):
     L = np.array([[3.0], [-2.0]], dtype=np.float32)
     V = np.ones((1, 1, 64), dtype=np.float32)
