@@ -11,7 +11,9 @@
 // The search narrows a range of the key order that contains e, level by level,
 // keeping R = mass and `below` = count of keys under the range:
 //   level 0: row maximum m (the log-sum-exp reference) and minimum, from the
-//            score scan's per-tile pairs or from a pass over given logits;
+//            score scan's per-tile pairs or from a pass over a register row
+//            (given logits streamed from memory take a sampled range and
+//            reference instead, checked against the row's true maximum);
 //            weights w = exp(s - m); an fp64 mass histogram over kBins
 //            equal-width value bins on [min, max] -- built by many blocks per
 //            row for long rows (hist0_kernel, per-chunk partials, no atomics
