@@ -342,14 +342,16 @@ __device__ __forceinline__ unsigned long long wave_pick_u64(unsigned long long v
                        (static_cast<unsigned long long>(e.y) << 32) | c.y);
 }
 
-// What the select of a row hands to the value stream of the same launch:
-// the head's softmax mass (relative to the row maximum, fp64) and the cut
-// key64, written in that order with device-scope stores; both are non-zero
-// once written (the head holds at least the row's maximum, weight 1), and
-// zero before.
+// What the select of a row hands to the value stream of the same launch,
+// each word once with a device-scope store: first the level-0 bin that
+// holds the cut, then the head's softmax mass (relative to the row maximum,
+// fp64) and the cut key64.  Every word is zero before its store and non-zero
+// after (the head holds at least the row's maximum, weight 1; ukey of a
+// float is never zero).
 struct CutPub {
-  uint64_t cut;
-  double den;
+  uint64_t cut;  // key64 of the cut
+  double den;    // the head's mass
+  uint64_t bin;  // (ukey(f0), ukey(f1)) of the level-0 bin [f0, f1) holding the cut
 };
 
 // Per-row scalars handed from the selection to the output kernel.

@@ -239,28 +239,47 @@ __device__ __forceinline__ double readlane_f64(double v, int j) {
   return __longlong_as_double(static_cast<long long>(b));
 }
 
-// One wave ends the search over c <= 64 keys (all in the current range): the
-// cut key is the largest whose lower candidates carry mass <= epsZ - R.
+// The workgroup ends the search over c <= 64 keys (all in the current range):
+// the cut key is the largest whose lower candidates carry mass <= epsZ - R.
+// Lane i of every wave holds candidate i; wave w sums, for each i, the
+// weights of candidates j of its slice [w per, w per + per) below key i, and
+// wave 0 adds the slices in wave order (sh.hm and sh.hc, free by now, hold
+// the partial masses and counts).  Called by every thread of the block.
 __device__ void finish_small(ResolveShared& sh, const uint64_t* keys, int c, float m, double R,
                              double epsZ) {
-  const int lane = threadIdx.x & 63;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  static_assert(kResolveWaves * kSmallCand <= kBins, "slice partials fit the histogram");
   const uint64_t k = lane < c ? keys[lane] : 0ull;
-  const double w = lane < c ? static_cast<double>(weight(key64_score(k), m)) : 0.0;
+  const int per = (c + kResolveWaves - 1) / kResolveWaves;
+  const int j0 = wave * per, j1 = min(c, j0 + per);
   double lower = 0.0;
   uint32_t nlower = 0u;
-  for (int j = 0; j < c; ++j) {
-    const uint64_t kj = readlane_u64(k, j);
-    const double wj = readlane_f64(w, j);
+  for (int j = j0; j < j1; ++j) {  // wave-uniform: LDS broadcast reads
+    const uint64_t kj = keys[j];
+    const double wj = static_cast<double>(weight(key64_score(kj), m));
     if (kj < k) {
       lower += wj;
       ++nlower;
     }
   }
-  const uint64_t best = wave_pick_u64<true>((lane < c && R + lower <= epsZ) ? k : 0ull);
-  if (lane < c && k == best) {
-    sh.thr = k;
-    sh.fin_R = R + lower;
-    sh.fin_below = nlower;
+  sh.hm[wave * kSmallCand + lane] = lower;
+  sh.hc[wave * kSmallCand + lane] = nlower;
+  __syncthreads();
+  if (wave == 0) {
+    double L = 0.0;
+    uint32_t N = 0u;
+    for (int g = 0; g < kResolveWaves; ++g) {
+      L += sh.hm[g * kSmallCand + lane];
+      N += sh.hc[g * kSmallCand + lane];
+    }
+    const uint64_t best = wave_pick_u64<true>((lane < c && R + L <= epsZ) ? k : 0ull);
+    if (lane < c && k == best) {
+      sh.thr = k;
+      sh.fin_R = R + L;
+      sh.fin_below = N;
+    }
   }
 }
 
@@ -532,6 +551,15 @@ __device__ __forceinline__ void resolve_row(
     const float f = bin_floor(b0 + wave, lo, inv);
     if (lane == 0) (wave == 0 ? sh.f0 : sh.f1) = f;
   }
+  // Other workgroups of the launch may use the bin before the cut is known:
+  // (ukey(f0), ukey(f1)) in one word, non-zero since ukey of a float is.
+  if (publish != nullptr) {
+    __syncthreads();
+    if (t == 0)
+      __hip_atomic_store(&publish->bin,
+                         (static_cast<uint64_t>(ukey(sh.f0)) << 32) | ukey(sh.f1),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   uint64_t prefix = 0;
   int plen = 0;
   bool done = false;
@@ -636,9 +664,9 @@ __device__ __forceinline__ void resolve_row(
       __syncthreads();
     }
     if (in_lds && cnt_in <= static_cast<uint32_t>(kSmallCand)) {
-      if (cand_exact) {  // the list is exactly the range: wave 0 finishes from it
-        if (wave == 0) finish_small(sh, sh.cand, static_cast<int>(ncand), m, R, epsZ);
-      } else {  // gather the range's keys from the list, then wave 0 finishes
+      if (cand_exact) {  // the list is exactly the range: finish from it
+        finish_small(sh, sh.cand, static_cast<int>(ncand), m, R, epsZ);
+      } else {  // gather the range's keys from the list, then finish
         if (t == 0) sh.nsmall = 0u;
         __syncthreads();
         for (uint32_t c = t; c < ncand; c += kResolveThreads) {
@@ -649,10 +677,9 @@ __device__ __forceinline__ void resolve_row(
           }
         }
         __syncthreads();
-        if (wave == 0)
-          finish_small(sh, sh.small,
-                       static_cast<int>(min(sh.nsmall, static_cast<uint32_t>(kSmallCand))), m, R,
-                       epsZ);
+        finish_small(sh, sh.small,
+                     static_cast<int>(min(sh.nsmall, static_cast<uint32_t>(kSmallCand))), m, R,
+                     epsZ);
       }
       __syncthreads();
       R = sh.fin_R;
@@ -775,14 +802,18 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
 //      m and weights the select uses), keeping the chunk's scores in LDS,
 //      while the select runs;
 //   3. reduce those sums over the workgroup (fp64 per head and V element)
-//      while the select may still run, then wait for the published mass and
-//      cut (a bounded spin on pub[]; the select workgroups have the lowest
-//      ids, so they were dispatched first, and they wait on nothing);
-//   4. sum, signed, w v of the keys between the two thresholds (+ for head
-//      keys the guess left out, - for the others; listed in key order in LDS
-//      and packed into as few waves as possible), add that to the reduced
-//      sums and add num / den into out with device-scope float atomics (out
-//      is zeroed before the launch).
+//      while the select may still run;
+//   4. wait for the level-0 bin [f0, f1) that holds the cut, which the
+//      select publishes as soon as it has it; list every key whose
+//      membership may differ from the guess's (kept by it and below f1, or
+//      left out and at or above f0; in key order in LDS, packed into as few
+//      waves as possible) and load their V rows;
+//   5. wait for the published mass and cut (bounded spins on pub[]; the
+//      select workgroups have the lowest ids, so they were dispatched first,
+//      and they wait on nothing), add, signed, w v of the listed keys the cut
+//      decides against the guess (+ for head keys the guess left out, - for
+//      the others), and add num / den into out with device-scope float
+//      atomics (out is zeroed before the launch).
 // out is thus a sum of one term per chunk in arrival order: reproducible to
 // fp32 rounding of those terms, not bit for bit.  A timed-out wait adds NaN.
 // pub[] and out must be zero at launch (the score scan zeroes both).
@@ -798,7 +829,7 @@ struct SpecSmem {
     struct {
       int idx[kFixKeys];
       float w[kFixKeys][GB];
-      uint32_t cnt[kFixKeys / kResolveThreads][kResolveWaves];
+      __attribute__((aligned(16))) uint32_t cnt[kFixKeys / kResolveThreads][kResolveWaves];
     } band;
   };
   float stash[GB * kFixKeys];  // the chunk's scores, [head][key in chunk]
@@ -807,6 +838,7 @@ struct SpecSmem {
   uint64_t spec[GB];
   uint64_t exact[GB];
   double den[GB];
+  float f0[GB], f1[GB];  // the level-0 bin [f0, f1) that holds each head's cut
 };
 
 // Steps 3 and 4 above, run by value_stream_block after the stream with every
@@ -827,7 +859,7 @@ struct SpecFinish {
     using Acc = typename AccOf<T>::type;
     constexpr int NT = kResolveThreads, NW = kResolveWaves;
     constexpr int KPT = kFixKeys / NT;
-    constexpr int EPL = VSlice<T>::kElems, LPR = D / EPL, RPW = kWave / LPR, STEP = NW * RPW;
+    constexpr int EPL = VSlice<T>::kElems, LPR = D / EPL, RPW = kWave / LPR;
     static_assert(kFixKeys % NT == 0, "whole keys per thread");
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
     const int seg = lane % LPR, rg = lane / LPR;
@@ -852,6 +884,180 @@ struct SpecFinish {
       for (int g = 0; g < NW; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
       sm->pre[col] = sum;
     }
+    // The level-0 bin [f0, f1) of each head's cut, published by its select
+    // as soon as it is known (well before the cut itself).  Keys below the
+    // bin are outside the head and keys above it inside, whatever the cut;
+    // only the bin's own keys wait for it.  Without the word (a timed-out
+    // wait) every key is treated as undecided.
+    if (t < nh) {
+      uint64_t b = 0ull;
+      for (int it = 0; it < kSpinLimit; ++it) {
+        b = __hip_atomic_load(&pub[h0 + t].bin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (b != 0ull) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      sm->f0[t] = b != 0ull ? ukey_to_float(static_cast<uint32_t>(b >> 32)) : -INFINITY;
+      sm->f1[t] = b != 0ull ? ukey_to_float(static_cast<uint32_t>(b)) : INFINITY;
+    }
+    __syncthreads();
+
+    // Lists the keys whose signed weight for some head is non-zero, in key
+    // order (sm->band.idx, sm->band.w); returns how many.  wfun(i, j)
+    // gives key i's signed weight for head j (i < len, j < nh).
+    auto compact = [&](auto wfun) -> int {
+      float wv[KPT][GB];
+      bool sel[KPT];
+      uint64_t bal[KPT];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int i = t + u * NT;
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+          const float w = (j < nh && i < len) ? wfun(i, j) : 0.0f;
+          wv[u][j] = w;
+          any = any || w != 0.0f;
+        }
+        sel[u] = any;
+        bal[u] = __ballot(any);
+        if (lane == 0) sm->band.cnt[u][wave] = static_cast<uint32_t>(__popcll(bal[u]));
+      }
+      __syncthreads();
+      uint32_t base = 0u;
+      static_assert(NW % 4 == 0, "counts read as 16-byte vectors");
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        uint32_t before = 0u, all = 0u;
+        uint4 c4[NW / 4];
+#pragma unroll
+        for (int q = 0; q < NW / 4; ++q) c4[q] = reinterpret_cast<const uint4*>(sm->band.cnt[u])[q];
+#pragma unroll
+        for (int q = 0; q < NW / 4; ++q) {
+          const uint32_t c[4] = {c4[q].x, c4[q].y, c4[q].z, c4[q].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            before += 4 * q + r < wave ? c[r] : 0u;
+            all += c[r];
+          }
+        }
+        if (sel[u]) {
+          const uint32_t slot =
+              base + before +
+              __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal[u] >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[u]), 0u));
+          sm->band.idx[slot] = t + u * NT;
+#pragma unroll
+          for (int j = 0; j < GB; ++j) sm->band.w[slot][j] = wv[u][j];
+        }
+        base += all;
+      }
+      __syncthreads();
+      return static_cast<int>(base);
+    };
+    // Listed entry e goes to wave (e / PER) % NW, load it = (e % PER) / RPW
+    // of a round, row group e % RPW, so a short list occupies few waves.
+    constexpr int ITB = 4;
+    constexpr int PER = ITB * RPW;
+    // Adds the listed rows' signed w v to the lane sums, the V rows of the
+    // first round having been loaded into u0 already when `preloaded`.
+    auto accumulate = [&](int nb, uint4 (&u0)[ITB], bool preloaded) {
+#pragma unroll
+      for (int j = 0; j < GB; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ln.acc[j][e] = Acc(0);
+      bool first = true;
+      for (int k0 = wave * PER; k0 < nb; k0 += NW * PER) {
+        uint4 u[ITB];
+#pragma unroll
+        for (int it = 0; it < ITB; ++it) {
+          if (first && preloaded) {
+            u[it] = u0[it];
+          } else {
+            const int e = min(k0 + it * RPW + rg, nb - 1);
+            const int64_t r = c0 + sm->band.idx[e];
+            u[it] = *reinterpret_cast<const uint4*>(V + r * D + seg * EPL);
+          }
+        }
+        first = false;
+#pragma unroll
+        for (int it = 0; it < ITB; ++it) {
+          const int e = k0 + it * RPW + rg;
+          const bool valid = e < nb;
+          const int ec = min(e, nb - 1);
+          float v[EPL];
+          VSlice<T>::load(u[it], v);
+#pragma unroll
+          for (int j = 0; j < GB; ++j) {
+            const Acc w = valid ? static_cast<Acc>(sm->band.w[ec][j]) : Acc(0);
+#pragma unroll
+            for (int e2 = 0; e2 < EPL; ++e2) ln.acc[j][e2] += w * static_cast<Acc>(v[e2]);
+          }
+        }
+      }
+    };
+    // The lane sums over the waves that hold the nb entries, added to the
+    // provisional sums; each column's num / den into out.
+    auto finish_out = [&](int nb) {
+      const int nwb = min(NW, (nb + PER - 1) / PER);
+      if (wave < nwb) {
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
+      }
+      __syncthreads();  // the list is read: its LDS takes the reduction
+      if (wave < nwb && rg == 0) {
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) sm->v.red[0][wave][j * D + seg * EPL + e] = ln.acc[j][e];
+      }
+      __syncthreads();
+      for (int col = t; col < nh * D; col += NT) {
+        const int j = col / D;
+        double sum = sm->pre[col];
+        for (int g = 0; g < nwb; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
+        unsafeAtomicAdd(out + static_cast<size_t>(h0 + j) * D + (col - j * D),
+                        static_cast<float>(sum / sm->den[j]));
+      }
+    };
+    auto score_of = [&](int i, int j) { return sm->stash[j * kFixKeys + i]; };
+
+    // Every key whose membership may differ from the guess's: kept by the
+    // guess and below f1 (the cut may leave it out: marked -1), or left out
+    // and at or above f0 (the cut may take it: +1); weights are computed
+    // for listed keys only, once the cut is known.  Their first round of V
+    // rows is loaded before the wait for the cut.
+    uint4 u0[ITB];
+    int nb;
+    {
+      // thresholds and this thread's scores in registers first: the list's
+      // own LDS stores would otherwise force a reload per test
+      uint64_t sp[GB];
+      float lo_f[GB], hi_f[GB], sc[KPT][GB];
+#pragma unroll
+      for (int j = 0; j < GB; ++j) {
+        sp[j] = sm->spec[j];
+        lo_f[j] = sm->f0[j];
+        hi_f[j] = sm->f1[j];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) sc[u][j] = score_of(min(t + u * NT, kFixKeys - 1), j);
+      }
+      nb = compact([&](int i, int j) -> float {
+        const float s = sc[(i - t) / NT][j];
+        const bool in_spec = key64(s, static_cast<uint32_t>(c0 + i)) >= sp[j];
+        return in_spec ? (s < hi_f[j] ? -1.0f : 0.0f) : (s >= lo_f[j] ? 1.0f : 0.0f);
+      });
+    }
+    if (nb > 0) {
+      const int k0 = wave * PER;
+#pragma unroll
+      for (int it = 0; it < ITB; ++it) {
+        const int e = min(k0 + it * RPW + rg, nb - 1);
+        const int64_t r = c0 + sm->band.idx[e];
+        u0[it] = *reinterpret_cast<const uint4*>(V + r * D + seg * EPL);
+      }
+    }
     if (t < nh) {
       // Both words non-zero: both stores have landed (each word has one
       // writer, and zero is only its value before that store).
@@ -868,115 +1074,28 @@ struct SpecFinish {
       sm->den[t] = got ? dn : __longlong_as_double(0x7FF8000000000000LL);  // NaN: no cut arrived
     }
     __syncthreads();
-    // Keys between the guess and the cut, with signed weights per head.
-    float wv[KPT][GB];
-    bool sel[KPT];
-    uint64_t bal[KPT];
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int i = t + u * NT;
-      bool any = false;
-#pragma unroll
-      for (int j = 0; j < GB; ++j) {
+    if (nb > 0) {
+      // Each listed (key, head) gets its signed weight where the cut decides
+      // against the guess (the bin decides every key outside it), else 0.
+      for (int p = t; p < nb * GB; p += NT) {
+        const int e = p / GB, j = p % GB;
+        const float mark = sm->band.w[e][j];
         float w = 0.0f;
-        if (j < nh && i < len) {
-          const float s = sm->stash[j * kFixKeys + i];
-          const uint64_t k = key64(s, static_cast<uint32_t>(c0 + i));
-          const bool in_spec = k >= sm->spec[j];
-          const bool in_head = k >= sm->exact[j];
-          if (in_spec != in_head) {
-            w = weight(s, m[j]);
-            w = in_head ? w : -w;
-            any = true;
-          }
+        if (mark != 0.0f) {
+          const int i = sm->band.idx[e];
+          const float s = score_of(i, j);
+          const bool in_head =
+              s >= sm->f1[j] ||
+              (s >= sm->f0[j] && key64(s, static_cast<uint32_t>(c0 + i)) >= sm->exact[j]);
+          const bool in_spec = mark < 0.0f;
+          if (in_head != in_spec) w = in_spec ? -weight(s, m[j]) : weight(s, m[j]);
         }
-        wv[u][j] = w;
+        sm->band.w[e][j] = w;
       }
-      sel[u] = any;
-      bal[u] = __ballot(any);
-      if (lane == 0) sm->band.cnt[u][wave] = static_cast<uint32_t>(__popcll(bal[u]));
+      __syncthreads();
+      accumulate(nb, u0, true);
     }
-    __syncthreads();
-    uint32_t base = 0u;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      uint32_t before = 0u, all = 0u;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t c = sm->band.cnt[u][w];
-        before += w < wave ? c : 0u;
-        all += c;
-      }
-      if (sel[u]) {
-        const uint32_t slot =
-            base + before +
-            __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal[u] >> 32),
-                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[u]), 0u));
-        sm->band.idx[slot] = t + u * NT;
-#pragma unroll
-        for (int j = 0; j < GB; ++j) sm->band.w[slot][j] = wv[u][j];
-      }
-      base += all;
-    }
-    const int nb = static_cast<int>(base);
-    __syncthreads();
-    // The listed V rows, signed, into fresh lane sums.  Entry e goes to wave
-    // (e / PER) % NW, load it = (e % PER) / RPW of a round, row group
-    // e % RPW, so a short list occupies few waves; the others skip the
-    // reduction below.
-    constexpr int ITB = 4;
-    constexpr int PER = ITB * RPW;
-    const int nwb = min(NW, (nb + PER - 1) / PER);
-#pragma unroll
-    for (int j = 0; j < GB; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ln.acc[j][e] = Acc(0);
-    for (int k0 = wave * PER; k0 < nb; k0 += NW * PER) {
-      uint4 u[ITB];
-#pragma unroll
-      for (int it = 0; it < ITB; ++it) {
-        const int e = min(k0 + it * RPW + rg, nb - 1);
-        const int64_t r = c0 + sm->band.idx[e];
-        u[it] = *reinterpret_cast<const uint4*>(V + r * D + seg * EPL);
-      }
-#pragma unroll
-      for (int it = 0; it < ITB; ++it) {
-        const int e = k0 + it * RPW + rg;
-        const bool valid = e < nb;
-        const int ec = min(e, nb - 1);
-        float v[EPL];
-        VSlice<T>::load(u[it], v);
-#pragma unroll
-        for (int j = 0; j < GB; ++j) {
-          const Acc w = valid ? static_cast<Acc>(sm->band.w[ec][j]) : Acc(0);
-#pragma unroll
-          for (int e2 = 0; e2 < EPL; ++e2) ln.acc[j][e2] += w * static_cast<Acc>(v[e2]);
-        }
-      }
-    }
-    // The band's sums over the waves that hold entries, added to the
-    // provisional ones; each column's num / den into out.
-    if (wave < nwb) {
-#pragma unroll
-      for (int j = 0; j < GB; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
-    }
-    __syncthreads();  // the list is read: its LDS takes the reduction
-    if (wave < nwb && rg == 0) {
-#pragma unroll
-      for (int j = 0; j < GB; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sm->v.red[0][wave][j * D + seg * EPL + e] = ln.acc[j][e];
-    }
-    __syncthreads();
-    for (int col = t; col < nh * D; col += NT) {
-      const int j = col / D;
-      double sum = sm->pre[col];
-      for (int g = 0; g < nwb; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
-      unsafeAtomicAdd(out + static_cast<size_t>(h0 + j) * D + (col - j * D),
-                      static_cast<float>(sum / sm->den[j]));
-    }
+    finish_out(nb);
   }
 };
 
