@@ -174,11 +174,16 @@ CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
  *   CTOPK_PLAN_DECODE_OVERLAP: score scan; one launch in which the select runs
  *     beside the value stream: each stream workgroup guesses every head's cut
  *     from a sample of the scores, sums w v over the keys above its guess while
- *     the select runs, then waits for the select's exact cut and head mass,
- *     corrects its sums by the keys between the guess and the cut, and adds
- *     its chunk's share of out with device-scope float atomics.  On this plan
- *     out is therefore reproducible run to run only to fp32 rounding of those
- *     per-chunk terms (k_eps, tau and sel_mask bit for bit).  Taken for decode
+ *     the select runs, lists the keys the cut may still move (from the
+ *     level-0 bin of the cut, which the select publishes first), then waits
+ *     for the select's exact cut and head mass, corrects its sums by the
+ *     listed keys the cut decides against the guess, and adds its chunk's
+ *     share of out with device-scope float atomics.  On this plan out is
+ *     therefore reproducible run to run only to fp32 rounding of those
+ *     per-chunk terms.  On every plan k_eps and sel_mask repeat run to run
+ *     except where a prefix mass lies within fp64 rounding of eps * Z (the
+ *     select's fp64 histograms are summed by LDS atomics in varying order),
+ *     and tau to fp64 rounding.  Taken for decode
  *     rows of 16385..32768 keys when at least half of the compute units (128)
  *     remain beside one workgroup per query row and the stream's chunks hold
  *     at most 2048 keys, and never for calls that ask for out_err or
