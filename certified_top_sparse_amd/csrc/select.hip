@@ -579,8 +579,40 @@ __device__ __forceinline__ void resolve_row(
     }
     __syncthreads();
     const float f0 = sh.f0, f1 = sh.f1;
-    uint32_t nbelow = 0u;  // counted from lane masks; lane 0 holds the wave's count
+    uint32_t nbelow = 0u;  // lane 0 holds the wave's count
     unsigned long long kmn = ~0ull, kmx = 0ull;
+    if constexpr (!kPrefix && PT > 0) {
+      // A register row's first pass in vector code only: per lane, the count
+      // of its keys below f0 and one bit per slot in [f0, f1); only the few
+      // lanes with such a slot then append their keys (one LDS atomic each).
+      int tt = t;
+      asm volatile("" : "+v"(tt));
+#pragma unroll
+      for (int u = 0; u < PT; ++u) asm volatile("" : "+v"(E.v[u]));
+      static_assert(PT <= 32, "one bit per slot");
+      const int nn = static_cast<int>(n);
+      uint32_t cnt = 0u, inm = 0u;
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const float sv = E.v[u];
+        const bool valid = u * kResolveThreads + tt < nn;
+        cnt += (valid & (sv < f0)) ? 1u : 0u;
+        inm |= (valid & (sv >= f0) & (sv < f1)) ? (1u << u) : 0u;
+      }
+      nbelow = wave_sum_u32_dpp(cnt);
+      if (inm != 0u) {
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+          if (inm & (1u << u)) {
+            const uint64_t k = key64(E.v[u], static_cast<uint32_t>(u * kResolveThreads + tt));
+            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+            if (slot < static_cast<uint32_t>(kCandCap)) sh.cand[slot] = k;
+            kmn = k < kmn ? k : kmn;
+            kmx = k > kmx ? k : kmx;
+          }
+        }
+      }
+    } else {
     E.for_each_all([&](int64_t i, float s, bool valid) {
       // One lane mask per comparison (each a single vector compare), combined
       // on the scalar unit; bitwise, not short-circuit: no branch per key.
@@ -612,6 +644,7 @@ __device__ __forceinline__ void resolve_row(
         }
       }
     });
+    }
     kmn = wave_pick_u64<false>(kmn);
     kmx = wave_pick_u64<true>(kmx);
     if (count_below && lane == 0) sh.wc[wave] = nbelow;
@@ -801,19 +834,18 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(
 //      (w = exp(s - m), m the row maximum from the scan's tile pairs, the same
 //      m and weights the select uses), keeping the chunk's scores in LDS,
 //      while the select runs;
-//   3. reduce those sums over the workgroup (fp64 per head and V element)
-//      while the select may still run;
-//   4. wait for the level-0 bin [f0, f1) that holds the cut, which the
+//   3. wait for the level-0 bin [f0, f1) that holds the cut, which the
 //      select publishes as soon as it has it; list every key whose
 //      membership may differ from the guess's (kept by it and below f1, or
 //      left out and at or above f0; in key order in LDS, packed into as few
 //      waves as possible) and load their V rows;
-//   5. wait for the published mass and cut (bounded spins on pub[]; the
+//   4. wait for the published mass and cut (bounded spins on pub[]; the
 //      select workgroups have the lowest ids, so they were dispatched first,
 //      and they wait on nothing), add, signed, w v of the listed keys the cut
 //      decides against the guess (+ for head keys the guess left out, - for
-//      the others), and add num / den into out with device-scope float
-//      atomics (out is zeroed before the launch).
+//      the others) to the lane sums, reduce them over the workgroup (fp64
+//      per head and V element) and add num / den into out with device-scope
+//      float atomics (out is zeroed before the launch).
 // out is thus a sum of one term per chunk in arrival order: reproducible to
 // fp32 rounding of those terms, not bit for bit.  A timed-out wait adds NaN.
 // pub[] and out must be zero at launch (the score scan zeroes both).
@@ -834,7 +866,6 @@ struct SpecSmem {
   };
   float stash[GB * kFixKeys];  // the chunk's scores, [head][key in chunk]
   float mx[GB][kResolveWaves];
-  double pre[GB * D];  // the provisional head's sums, per (head, V element)
   uint64_t spec[GB];
   uint64_t exact[GB];
   double den[GB];
@@ -864,26 +895,6 @@ struct SpecFinish {
     const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
     const int seg = lane % LPR, rg = lane / LPR;
     __syncthreads();  // every wave is past its stream loop: the staging LDS is free
-    // The provisional head's sums over the workgroup, while the select may
-    // still run: the row groups of a wave by cross-lane adds, then the waves
-    // in order through LDS, in fp64 per (head, V element).
-#pragma unroll
-    for (int j = 0; j < GB; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
-    if (rg == 0) {
-#pragma unroll
-      for (int j = 0; j < GB; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sm->v.red[0][wave][j * D + seg * EPL + e] = ln.acc[j][e];
-    }
-    __syncthreads();
-    for (int col = t; col < nh * D; col += NT) {
-      double sum = 0.0;
-#pragma unroll
-      for (int g = 0; g < NW; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
-      sm->pre[col] = sum;
-    }
     // The level-0 bin [f0, f1) of each head's cut, published by its select
     // as soon as it is known (well before the cut itself).  Keys below the
     // bin are outside the head and keys above it inside, whatever the cut;
@@ -958,13 +969,10 @@ struct SpecFinish {
     // of a round, row group e % RPW, so a short list occupies few waves.
     constexpr int ITB = 4;
     constexpr int PER = ITB * RPW;
-    // Adds the listed rows' signed w v to the lane sums, the V rows of the
-    // first round having been loaded into u0 already when `preloaded`.
+    // Adds the listed rows' signed w v to the lane sums (which hold the
+    // provisional head's), the V rows of the first round having been loaded
+    // into u0 already when `preloaded`.
     auto accumulate = [&](int nb, uint4 (&u0)[ITB], bool preloaded) {
-#pragma unroll
-      for (int j = 0; j < GB; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ln.acc[j][e] = Acc(0);
       bool first = true;
       for (int k0 = wave * PER; k0 < nb; k0 += NW * PER) {
         uint4 u[ITB];
@@ -995,18 +1003,16 @@ struct SpecFinish {
         }
       }
     };
-    // The lane sums over the waves that hold the nb entries, added to the
-    // provisional sums; each column's num / den into out.
-    auto finish_out = [&](int nb) {
-      const int nwb = min(NW, (nb + PER - 1) / PER);
-      if (wave < nwb) {
+    // The lane sums over the workgroup: the row groups of a wave by
+    // cross-lane adds, then the waves in order through LDS in fp64; each
+    // column's num / den into out.
+    auto finish_out = [&]() {
 #pragma unroll
-        for (int j = 0; j < GB; ++j)
+      for (int j = 0; j < GB; ++j)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
-      }
+        for (int e = 0; e < EPL; ++e) ln.acc[j][e] = stride_sum<LPR>(ln.acc[j][e]);
       __syncthreads();  // the list is read: its LDS takes the reduction
-      if (wave < nwb && rg == 0) {
+      if (rg == 0) {
 #pragma unroll
         for (int j = 0; j < GB; ++j)
 #pragma unroll
@@ -1015,8 +1021,9 @@ struct SpecFinish {
       __syncthreads();
       for (int col = t; col < nh * D; col += NT) {
         const int j = col / D;
-        double sum = sm->pre[col];
-        for (int g = 0; g < nwb; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
+        double sum = 0.0;
+#pragma unroll
+        for (int g = 0; g < NW; ++g) sum += static_cast<double>(sm->v.red[0][g][col]);
         unsafeAtomicAdd(out + static_cast<size_t>(h0 + j) * D + (col - j * D),
                         static_cast<float>(sum / sm->den[j]));
       }
@@ -1095,7 +1102,7 @@ struct SpecFinish {
       __syncthreads();
       accumulate(nb, u0, true);
     }
-    finish_out(nb);
+    finish_out();
   }
 };
 
