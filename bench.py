@@ -52,10 +52,12 @@ KERNELS_BY_PLAN = {
     2: ("score_scan", "hist0", "resolve", "vsum", "finalize"),
     3: ("score_scan", "hist0", "select_spec"),
     4: ("score_scan", "hist0", "bound", "vsum", "finalize"),
+    5: ("short_row",),
 }
 # The kernel of each plan that streams the V rows of the head sets.
 V_KERNEL = {2: "vsum", 3: "select_spec", 4: "vsum"}
-PLAN_NAMES = {1: "encoder", 2: "decode", 3: "decode_overlap", 4: "decode_bound"}
+PLAN_NAMES = {1: "encoder", 2: "decode", 3: "decode_overlap", 4: "decode_bound",
+              5: "decode_fused"}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_gqa_decode_n32768.md")
 CSRC = os.path.join(ROOT, "certified_top_sparse_amd", "csrc")
 _COMMON = ("kernels.h", "device_common.h")
@@ -373,7 +375,8 @@ def single_query_leg(ct, lib, torch, timer, steps):
 
     us = timer.per_call_us(step, steps, 20)
     kern = timer.per_kernel_us(step, min(steps, 200), names)
-    kern["hist0"] = None
+    if "hist0" in kern:
+        kern["hist0"] = None
     return {"workload": "single query: 1 head, n=1024, d=64, fp32, scale 0.25", "eps": 0.01,
             "plan": PLAN_NAMES.get(plan, plan), "steps": steps, "us_per_call": round(us, 3),
             "kernel_us": kern, "k_eps": int(k_eps.item())}

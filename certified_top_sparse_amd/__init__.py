@@ -7,7 +7,7 @@ whose functions carry the C names.
 """
 from .ctopk import (  # noqa: F401
     CTOPK_BF16, CTOPK_F32, CTOPK_FLAG_BOUND, CTOPK_PLAN_DECODE, CTOPK_PLAN_DECODE_BOUND,
-    CTOPK_PLAN_DECODE_OVERLAP, CTOPK_PLAN_ENCODER,
+    CTOPK_PLAN_DECODE_FUSED, CTOPK_PLAN_DECODE_OVERLAP, CTOPK_PLAN_ENCODER,
     CtopkArgs, CtopkError, CtopkK4Args, EXPORTED, LIB_PATH, ctopk_candidates_k4, ctopk_certify,
     ctopk_certify_ex, ctopk_certify_logits, ctopk_certify_noalloc, CTOPK_NOALLOC_SCRATCH_BYTES, ctopk_last_error_string,
     ctopk_logits_workspace_bytes, ctopk_plan, ctopk_record_kernel_events, ctopk_validate,

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libctopk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "score_scan.hip", "select.hip", "bound.hip", "vsum.hip", "encoder.hip",
-           "k4.hip"]
+           "k4.hip", "shortrow.hip"]
 
 COMPILE_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -235,6 +235,7 @@ int plan_of(const ctopk_args* a) {
   if (certificate) return CTOPK_PLAN_DECODE;
   if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads))
     return CTOPK_PLAN_ENCODER;
+  if (a->n <= ctopk::kShortRowMaxN) return CTOPK_PLAN_DECODE_FUSED;
   if (ctopk::select_spec_nchunk(a->n, a->n_q_heads, a->n_kv_heads, a->dtype, a->d) > 0)
     return CTOPK_PLAN_DECODE_OVERLAP;
   return CTOPK_PLAN_DECODE;
@@ -356,6 +357,14 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
                                          a->n, a->n_q_heads, a->n_kv_heads, a->eps, a->out,
                                          a->k_eps, a->tau, a->sel_mask, a->scores, a->lse, st),
                    "encoder launch");
+    return rc == CTOPK_OK ? ok() : rc;
+  }
+  if (plan == CTOPK_PLAN_DECODE_FUSED) {
+    rc = hip_check(ctopk::launch_short_row(a->q, a->K, a->V, a->dtype, a->d, a->head_scale,
+                                           default_scale, a->n, a->n_q_heads, a->n_kv_heads,
+                                           a->eps, a->out, a->k_eps, a->tau, a->lse,
+                                           a->sel_mask, a->scores, st),
+                   "short-row launch");
     return rc == CTOPK_OK ? ok() : rc;
   }
 

@@ -138,6 +138,15 @@ hipError_t launch_bound(const float* scores, int64_t n, int rows, const float2* 
                         const float* blkz, int nblk, double eps, RowSel* rs, int32_t* k_eps,
                         double* tau, double* lse, uint32_t* sel_mask, hipStream_t st);
 
+// Fused decode for short rows (n <= kShortRowMaxN): one workgroup per query
+// row computes its scores (bitwise the score scan's), selects the certified
+// head and writes out, k_eps, tau, and lse, sel_mask and scores when given.
+constexpr int kShortRowMaxN = 1024;
+hipError_t launch_short_row(const void* q, const void* K, const void* V, int dtype, int d,
+                            const float* head_scale, float default_scale, int64_t n, int n_q,
+                            int n_kv, double eps, float* out, int32_t* k_eps, double* tau,
+                            double* lse, uint32_t* sel_mask, float* scores, hipStream_t st);
+
 // Encoder-shaped path (all queries of a head, n <= 512, bf16, MFMA QK^T).
 hipError_t launch_encoder(const void* q, const void* K, const void* V, int d,
                           const float* head_scale, float default_scale, int64_t n, int n_q,

@@ -30,6 +30,7 @@ CTOPK_PLAN_ENCODER = 1
 CTOPK_PLAN_DECODE = 2
 CTOPK_PLAN_DECODE_OVERLAP = 3
 CTOPK_PLAN_DECODE_BOUND = 4
+CTOPK_PLAN_DECODE_FUSED = 5
 CTOPK_FLAG_BOUND = 1
 
 STATUS_NAMES = {

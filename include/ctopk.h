@@ -158,9 +158,11 @@ typedef struct ctopk_args {
  * scale, caller-owned workspace, optional selection mask, scores and lse.
  * bf16 inputs with d 64 or 128, n <= 512 and n_q_heads/n_kv_heads >= 64 (all
  * queries of a head against few keys, as in an encoder) run on a fused path
- * whose QK^T and head-only output use MFMA; it needs no workspace.  Calls that
- * ask for out_err or out_dense take the general path.  Results follow the same
- * definitions on both paths.
+ * whose QK^T and head-only output use MFMA; it needs no workspace.  Other rows
+ * of at most 1024 keys run on one fused kernel per call (scores, select and
+ * head-only output by one workgroup per query row; no workspace either).
+ * Calls that ask for out_err or out_dense take the general path.  Results
+ * follow the same definitions on every path.
  */
 CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
 
@@ -190,13 +192,20 @@ CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
  *     out_dense;
  *   CTOPK_PLAN_DECODE_BOUND (calls with CTOPK_FLAG_BOUND): score scan with
  *     per-block masses; the blockwise bound (one workgroup per row, in place
- *     of the select); value stream over the kept keys; combine.
+ *     of the select); value stream over the kept keys; combine;
+ *   CTOPK_PLAN_DECODE_FUSED: rows of at most 1024 keys that the encoder path
+ *     does not take, without out_err or out_dense: one kernel, one workgroup
+ *     per query row, one key per thread: the scores (the same arithmetic as
+ *     the score scan, so the same values), the select as a mass-weighted
+ *     radix descent over 8-bit digits of the 64-bit key order, and the
+ *     head-only output from the head keys' value rows.
  */
 typedef enum {
   CTOPK_PLAN_ENCODER = 1,
   CTOPK_PLAN_DECODE = 2,
   CTOPK_PLAN_DECODE_OVERLAP = 3,
-  CTOPK_PLAN_DECODE_BOUND = 4
+  CTOPK_PLAN_DECODE_BOUND = 4,
+  CTOPK_PLAN_DECODE_FUSED = 5
 } ctopk_plan_id;
 
 /*

@@ -208,6 +208,15 @@ def test_missing_library_fails_loudly(tmp_path):
     ({"n": 512, "d": 64, "n_q_heads": 512, "n_kv_heads": 8}, cb.CTOPK_PLAN_ENCODER),
     ({"n": 512, "d": 64, "n_q_heads": 512, "n_kv_heads": 8, "out_err": A16 * 7},
      cb.CTOPK_PLAN_DECODE),
+    # rows of at most 1024 keys the encoder path does not take: one fused kernel
+    ({"n": 1024, "d": 64, "n_q_heads": 1, "n_kv_heads": 1, "dtype": cb.CTOPK_F32},
+     cb.CTOPK_PLAN_DECODE_FUSED),
+    ({"n": 1024}, cb.CTOPK_PLAN_DECODE_FUSED),
+    ({"n": 1}, cb.CTOPK_PLAN_DECODE_FUSED),
+    ({"n": 1025}, cb.CTOPK_PLAN_DECODE),
+    ({"n": 512, "d": 64, "n_q_heads": 32, "n_kv_heads": 8}, cb.CTOPK_PLAN_DECODE_FUSED),
+    ({"n": 1024, "out_err": A16 * 7}, cb.CTOPK_PLAN_DECODE),
+    ({"n": 1024, "out_dense": A16 * 7}, cb.CTOPK_PLAN_DECODE),
 ])
 def test_plan_choice(lib, kw, plan):
     assert ct.ctopk_plan(good_args(**kw)) == plan
@@ -225,6 +234,7 @@ def test_bound_flag_plan_and_limits(lib):
     assert ct.ctopk_plan(good_args(n=512, d=64, n_q_heads=512, n_kv_heads=8,
                                    flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
     assert ct.ctopk_plan(good_args(n=262144, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
+    assert ct.ctopk_plan(good_args(n=1024, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_PLAN_DECODE_BOUND
     assert ct.ctopk_validate(good_args(n=262145, flags=cb.CTOPK_FLAG_BOUND)) == cb.CTOPK_ERR_UNSUPPORTED
     assert ct.ctopk_validate(good_args(flags=2)) == cb.CTOPK_ERR_UNSUPPORTED
 

@@ -119,6 +119,64 @@ def test_decode_shapes(ct, d, dtype, G):
 
 
 # ---------------------------------------------------------------------------
+# rows of at most 1024 keys: the fused plan (scores, select and output in one
+# kernel)
+# ---------------------------------------------------------------------------
+def _to_f32(wl):
+    return dict(wl, q=workloads.bf16_to_f32(wl["q"]), K=workloads.bf16_to_f32(wl["K"]),
+                V=workloads.bf16_to_f32(wl["V"]), dtype="f32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 3, 4, 8, 16])
+def test_fused_short_row_shapes(ct, d, dtype, G):
+    n_kv = 2
+    wl = workloads.gqa_decode(n=999, n_q=G * n_kv, n_kv=n_kv, d=d, planted=5)
+    if dtype == "f32":
+        wl = _to_f32(wl)
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_FUSED
+    check_decode(ct, wl, 0.05, f"fused short row d={d} {dtype} G={G}", want_lse=True)
+
+
+@pytest.mark.parametrize("n", [64, 65, 1024])
+@pytest.mark.parametrize("eps", [0.01, 0.1])
+def test_fused_short_row_matches_general_plan(ct, n, eps):
+    """The fused plan against the general one (taken when out_err is asked
+    for) on the same inputs: bitwise the same scores (one dot-product
+    arithmetic), so the same head and k_eps wherever no prefix mass lies
+    within 1e-6 of eps (the two sum Z in different orders), tau and lse to
+    fp64 rounding and out to fp32 rounding."""
+    wl = workloads.gqa_decode(n=n, n_q=8, n_kv=2, planted=5)
+    _say(f"fused vs general plan n={n} eps={eps}")
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_FUSED
+    q, K, V = dev(wl["q"]), dev(wl["K"]), dev(wl["V"])
+    hs = dev(wl["head_scale"])
+    kw = dict(head_scale=hs, want_mask=True, want_scores=True, want_lse=True)
+    a = to_np(ct.ctopk_certify_ex(q, K, V, eps, **kw))
+    b = to_np(ct.ctopk_certify_ex(q, K, V, eps, want_err=True, **kw))
+    torch.cuda.synchronize()
+    assert np.array_equal(a["scores"].view(np.uint32), b["scores"].view(np.uint32))
+    checked = 0
+    for h in range(wl["n_q_heads"]):
+        s = a["scores"][h].astype(np.float64)
+        p = np.sort(np.exp(s - s.max()))
+        p /= p.sum()
+        tails = np.concatenate([[0.0], np.cumsum(p)])  # tails[j] = mass of the j smallest
+        k = int(a["k_eps"][h])
+        near = min(abs(tails[n - k] - eps), abs(tails[min(n, n - k + 1)] - eps))
+        if near <= 1e-6:
+            continue
+        checked += 1
+        assert int(b["k_eps"][h]) == k, h
+        assert np.array_equal(a["sel_mask"][h], b["sel_mask"][h]), h
+        assert abs(a["tau"][h] - b["tau"][h]) <= 1e-12 * max(1.0, abs(b["tau"][h])), h
+        assert abs(a["lse"][h] - b["lse"][h]) <= 1e-12 * max(1.0, abs(b["lse"][h])), h
+    assert checked >= wl["n_q_heads"] // 2
+    assert rel_l2(a["out"], b["out"]).max() <= 1e-5
+
+
+# ---------------------------------------------------------------------------
 # GQA decode workloads
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("eps", [0.01, 0.1])
