@@ -176,6 +176,52 @@ def test_fused_short_row_matches_general_plan(ct, n, eps):
     assert rel_l2(a["out"], b["out"]).max() <= 1e-5
 
 
+@pytest.mark.parametrize("n", [65, 1000, 1024])
+def test_fused_all_equal_scores(ct, n):
+    """q = 0: every score is +0 or -0 (keys whose K row is all negative score
+    -0), equal for the select; the head is the k lowest indices, and the
+    value bin holding everything is narrowed by key64 digits (index bits)."""
+    wl = workloads.single_query(n=n, seed_extra=(n, 7))
+    wl["q"] = np.zeros_like(wl["q"])
+    K = wl["K"].copy()
+    K[0, ::7] = -np.abs(K[0, ::7])
+    wl["K"] = K
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_FUSED
+    g, ref, S = check_decode(ct, wl, 0.0123, f"fused all-equal scores n={n}")
+    k = int(g["k_eps"][0])
+    assert k == n - int(math.floor(0.0123 * n + 1e-9))
+    assert g["sel_mask"][0][:k].all() and not g["sel_mask"][0][k:].any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [777, 1024])
+def test_fused_tied_block(ct, n, dtype):
+    """600 keys share one K row (bitwise-equal scores) and eps puts the cut
+    in the middle of that block: the value bin of the cut holds more than 64
+    keys, so the select descends through key64 digits, first the score bits
+    that separate the block from its neighbours in the bin, then the index
+    bits that order the block."""
+    wl = workloads.single_query(n=n, seed_extra=(n, 11))
+    K = wl["K"].copy()
+    K[0, 100:700] = K[0, 50]
+    wl["K"] = K
+    if dtype == "bf16":
+        wl = dict(wl, q=workloads.bf16_rne(wl["q"]), K=workloads.bf16_rne(wl["K"]),
+                  V=workloads.bf16_rne(wl["V"]), dtype="bf16")
+    assert plan_of(ct, wl) == ct.CTOPK_PLAN_DECODE_FUSED
+    sc = float(np.float32(wl["head_scale"][0]))
+    S = sc * (oracle.as_f64(wl["K"])[0] @ oracle.as_f64(wl["q"])[0])
+    P = oracle.softmax(S)
+    s_tie = S[50]
+    below = P[S < s_tie].sum()
+    p_tie = P[50]
+    eps = float(below + 300.5 * p_tie)  # between two steps of the tail mass inside the block
+    g, ref, _ = check_decode(ct, wl, eps, f"fused tied block n={n} {dtype}")
+    k = int(g["k_eps"][0])
+    above = int((S > s_tie).sum())
+    assert above < k <= above + 601  # the cut is a key of the block
+
+
 # ---------------------------------------------------------------------------
 # GQA decode workloads
 # ---------------------------------------------------------------------------
