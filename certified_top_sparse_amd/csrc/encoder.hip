@@ -52,10 +52,14 @@ constexpr int kFinishMax = 32;            // exact finish at or below this many 
 // Every level below the first drops at least one candidate, so n levels suffice.
 constexpr int kMaxLevels = 2 * kEncMaxKeys;
 
+// A row's finish list: up to kFinishMax (key64, weight) entries, one 16-byte
+// word each, rows kFinStride words apart (the pad keeps the 16 rows' entry j
+// in different banks).
+constexpr int kFinStride = kFinishMax + 1;
 struct GroupSel {  // select scratch of one row group (two waves), aliased with the stages
   double hist[16 * kHistStride];
   uint64_t key[2 * kWave * kLaneSlots];
-  float w[2 * kWave * kLaneCand];
+  uint4 fin[16 * kFinStride];
 };
 struct GroupXchg {  // per-row values the two waves of a row group exchange
   float f[2][16][4];   // max, min, candidate min, candidate max
@@ -129,6 +133,18 @@ __device__ __forceinline__ uint32_t pack_weight(float w) {
   const __bf16 wl = static_cast<__bf16>(w - static_cast<float>(wh));
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wh)) |
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wl)) << 16);
+}
+
+// The weight e^{s - m} for the output pass when level 0's packed weights do
+// not fit in registers: one hardware base-2 exponential of the fp32
+// (s - m) * log2(e).  Its relative error (about |s - m| * 2^-23 plus the
+// instruction's own) stays below the 2^-17 to which the packed bf16 high and
+// low parts carry any weight into the MFMA, for every weight above e^-16 of
+// the row maximum; the head's mass Z - R, by which the sums are divided,
+// still comes from the select's exact weights.
+__device__ __forceinline__ float output_weight(float s, float m) {
+  constexpr float kLog2e = 1.44269502162933349609375f;
+  return __builtin_amdgcn_exp2f((s - m) * kLog2e);
 }
 
 template <int D, int NT>
@@ -273,7 +289,6 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   uint64_t cut = 0;
   double R = 0.0;
   uint64_t* klist = gs.key + (kh * kWave + lane) * kLaneSlots;
-  float* wlist = gs.w + (kh * kWave + lane) * kLaneCand;
 
   for (int level = 0; level < kMaxLevels; ++level) {
     // Opaque to the optimiser: keeps per-key values derived from s from being
@@ -385,13 +400,22 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const bool fin_eq = active && !fin_list && cmn == cmx;
 
     // Exact finish on <= 32 candidates: the cut is the largest candidate key
-    // whose strictly smaller keys carry mass <= thr.
-    if (fin_list) {  // entries become (key64, weight)
+    // whose strictly smaller keys carry mass <= thr.  The row's candidates go
+    // into one list (each lane's after those of the row's lanes before it),
+    // and lane (kh, g) of the row tests candidates 4 kh + g, + 8, ...
+    // against the whole list.
+    if (fin_list) {
+      int off = 0;
+#pragma unroll
+      for (int li = 0; li < 8; ++li)
+        off += li < 4 * kh + g ? xg.lcnt[li >> 2][r + 16 * (li & 3)] : 0;
+      uint4* dst = gs.fin + r * kFinStride + off;
       for (int y = 0; y < cnt; ++y) {
         const uint64_t en = klist[y];
         const float v = __uint_as_float(static_cast<uint32_t>(en));
-        klist[y] = key64(v, static_cast<uint32_t>(en >> 32));
-        wlist[y] = weight(v, mx);
+        const uint64_t kk = key64(v, static_cast<uint32_t>(en >> 32));
+        dst[y] = make_uint4(static_cast<uint32_t>(kk), static_cast<uint32_t>(kk >> 32),
+                            __float_as_uint(weight(v, mx)), 0u);
       }
     }
     // Equal scores: the candidates differ only in index; rank by index.
@@ -401,35 +425,21 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
     __syncthreads();
     if (fin_list) {
+      const uint4* lst = gs.fin + r * kFinStride;
       uint64_t bk = 0;
       double bR = 0.0;
-      for (int j = 0; j < cnt; ++j) {
-        const uint64_t kj = klist[j];
+      for (int c = 4 * kh + g; c < ctot; c += 8) {
+        const uint4 ec = lst[c];
+        const uint64_t kc = (static_cast<uint64_t>(ec.y) << 32) | ec.x;
         double ml = 0.0;
-#pragma unroll
-        for (int li = 0; li < 8; ++li) {  // the row's 8 lanes: 4 per wave
-          const int hh = li >> 2, gg = li & 3;
-          const int slot = hh * kWave + r + 16 * gg;
-          const uint64_t* ko = gs.key + slot * kLaneSlots;
-          const float* wo = gs.w + slot * kLaneCand;
-          const int ny = xg.lcnt[hh][r + 16 * gg];
-          for (int y = 0; y < ny; y += 4) {  // four entries' loads in flight
-            uint64_t k4[4];
-            float w4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int yy = min(y + u, ny - 1);
-              k4[u] = ko[yy];
-              w4[u] = wo[yy];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (y + u < ny && k4[u] < kj) ml += static_cast<double>(w4[u]);
-          }
+        for (int j = 0; j < ctot; ++j) {
+          const uint4 ej = lst[j];
+          const uint64_t kj = (static_cast<uint64_t>(ej.y) << 32) | ej.x;
+          if (kj < kc) ml += static_cast<double>(__uint_as_float(ej.z));
         }
         const double Pm = bestP + ml;
-        if (Pm <= thr && kj > bk) {
-          bk = kj;
+        if (Pm <= thr && kc > bk) {
+          bk = kc;
           bR = Pm;
         }
       }
@@ -571,7 +581,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
             if constexpr (kKeepW)
               p2[k] = head ? pw[t0 + half][e + k] : 0u;
             else
-              p2[k] = head ? pack_weight(weight(v, mx)) : 0u;
+              p2[k] = head ? pack_weight(output_weight(v, mx)) : 0u;
           }
           ph[2 * half + e / 2] = (p2[0] & 0xFFFFu) | (p2[1] << 16);
           pl[2 * half + e / 2] = (p2[0] >> 16) | (p2[1] & 0xFFFF0000u);
