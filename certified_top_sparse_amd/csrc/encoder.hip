@@ -135,6 +135,14 @@ __device__ __forceinline__ uint32_t pack_weight(float w) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, wl)) << 16);
 }
 
+// Two floats rounded to bf16 (nearest even) in one word, the first in the low
+// half-word: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2v_t));
+}
+
 // The weight e^{s - m} for the output pass when level 0's packed weights do
 // not fit in registers: one hardware base-2 exponential of the fp32
 // (s - m) * log2(e).  Its relative error (about |s - m| * 2^-23 plus the
@@ -572,6 +580,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
           uint32_t p2[2];
+          float w2[2];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const float v = s[t0 + half][e + k];
@@ -581,10 +590,18 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
             if constexpr (kKeepW)
               p2[k] = head ? pw[t0 + half][e + k] : 0u;
             else
-              p2[k] = head ? pack_weight(output_weight(v, mx)) : 0u;
+              w2[k] = head ? output_weight(v, mx) : 0.0f;
           }
-          ph[2 * half + e / 2] = (p2[0] & 0xFFFFu) | (p2[1] << 16);
-          pl[2 * half + e / 2] = (p2[0] >> 16) | (p2[1] & 0xFFFF0000u);
+          if constexpr (kKeepW) {
+            ph[2 * half + e / 2] = (p2[0] & 0xFFFFu) | (p2[1] << 16);
+            pl[2 * half + e / 2] = (p2[0] >> 16) | (p2[1] & 0xFFFF0000u);
+          } else {
+            // both keys' high parts in one conversion, then both residuals
+            const uint32_t hi = bf16_pair(w2[0], w2[1]);
+            ph[2 * half + e / 2] = hi;
+            pl[2 * half + e / 2] = bf16_pair(w2[0] - __uint_as_float(hi << 16),
+                                             w2[1] - __uint_as_float(hi & 0xFFFF0000u));
+          }
         }
       const bf16x8_t bh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
       const bf16x8_t bl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
