@@ -314,6 +314,60 @@ def diam_head_tail(V: np.ndarray, head: np.ndarray) -> float:
     return float(np.sqrt(max(0.0, float(np.max(d2)))))
 
 
+def variance_p(P: np.ndarray, V: np.ndarray) -> float:
+    """Var_P(V) = sum_i P_i ||v_i - Attn||_2^2, the spread of the value rows
+    under the attention distribution P (Attn = sum_i P_i v_i)."""
+    V = as_f64(V)
+    mu = P @ V
+    return float(P @ np.sum((V - mu) ** 2, axis=1))
+
+
+def variance_bound(tau: float, var_p: float) -> float:
+    """Refinement of the output error by Var_P(V) (reading of the Abstract's
+    "refinements linking the error to Var_P(V)"): Attn is the mixture
+    (1 - tau) mu_head + tau mu_tail, so the law of total variance gives
+    Var_P(V) >= tau (1 - tau) ||mu_tail - mu_head||^2, and with the
+    factorisation ||Attn - Attn_k|| = tau ||mu_tail - mu_head|| this is
+    ||Attn - Attn_k||_2 <= sqrt(tau Var_P(V) / (1 - tau)).  Equality holds
+    when every head row equals mu_head and every tail row equals mu_tail."""
+    if tau <= 0.0:
+        return 0.0
+    return math.sqrt(tau * var_p / (1.0 - tau))
+
+
+def gap_bound(s, k: int, ranks=None) -> float:
+    """Deterministic bound on TV(P, P_hat) of the Top-k truncation from the
+    ordered logits (reading of the Abstract's "single boundary gap" and
+    "multi-gap" bounds, whose formulas the page does not print).
+
+    With s_(1) >= ... >= s_(n) the ordered scores, every head key has weight at
+    least e^{s_(k)}, and a tail key of rank in (r_j, r_{j+1}] has weight at
+    most e^{s_(r_j + 1)}.  For ranks k = r_0 < r_1 < ... < r_J = n and the
+    gaps G_j = s_(k) - s_(r_j + 1) >= 0, the tail mass relative to e^{s_(k)}
+    is at most B = sum_j (r_{j+1} - r_j) e^{-G_j} and the head's at least k,
+    and since x / (a + x) grows with x and falls with a,
+        TV <= B / (k + B).
+    ranks=None takes the single boundary gap (J = 1, r_1 = n), which reads
+    (n - k) e^{-Delta} / (k + (n - k) e^{-Delta}) with Delta = s_(k) - s_(k+1);
+    `ranks` lists r_1 < ... < r_{J-1} strictly between k and n for the
+    multi-gap bound.  k = n returns 0."""
+    s = np.asarray(s, dtype=np.float64)
+    n = s.shape[0]
+    if not (1 <= k <= n):
+        raise ValueError("k must lie in 1..n")
+    if k == n:
+        return 0.0
+    ss = s[order_desc(s)]
+    r = [k] + ([] if ranks is None else [int(x) for x in ranks]) + [n]
+    if any(b <= a for a, b in zip(r[:-1], r[1:])):
+        raise ValueError("ranks must increase strictly between k and n")
+    sk = ss[k - 1]
+    B = 0.0
+    for a, b in zip(r[:-1], r[1:]):
+        B += (b - a) * math.exp(ss[a] - sk)  # ss[a] is s_(a + 1)
+    return B / (k + B)
+
+
 def gaussian_design_rule(sigma: float, eps: float) -> float:
     """k_eps / n ~ Phi_c(sigma + Phi^{-1}(eps)) for i.i.d. N(mu, sigma^2)
     scores (Abstract), with Phi_c = 1 - Phi."""

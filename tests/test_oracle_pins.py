@@ -535,3 +535,100 @@ def test_k4_bound_is_attained_for_a_query_along_the_residual():
         s = 0.2 * (Kf[i] @ q)
         shat, R = oracle.k4_score_bounds(q, c[i:i + 1], a[i:i + 1], rho[i:i + 1], 0.2)
         assert s - shat[0] == pytest.approx(R[0], rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# gap bounds and the Var_P(V) refinement (Abstract: deterministic bounds from
+# a single boundary gap and from several gaps; refinements of the output
+# error by Var_P(V))
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("sigma", [0.5, 2.0, 6.0])
+def test_gap_bounds_dominate_the_tail_mass(sigma):
+    rng = np.random.default_rng(71)
+    n = 40
+    for _ in range(5):
+        s = rng.standard_normal(n) * sigma
+        _, _, _, T = oracle.tail_masses(s)
+        for k in range(1, n + 1):
+            single = oracle.gap_bound(s, k)
+            assert T[k] <= single * (1 + 1e-12) + 1e-300
+            if k < n - 1:
+                inner = np.sort(rng.choice(np.arange(k + 1, n), size=min(3, n - k - 1),
+                                           replace=False))
+                multi = oracle.gap_bound(s, k, inner)
+                # more gaps never loosen the bound, and it still holds
+                assert T[k] <= multi * (1 + 1e-12) + 1e-300
+                assert multi <= single * (1 + 1e-12)
+
+
+def test_single_gap_bound_is_exact_on_two_levels():
+    # k keys at a and n - k at b < a: every inequality of the bound is tight,
+    # TV = (n - k) e^{b} / (k e^{a} + (n - k) e^{b}).
+    n, a, b = 23, 1.25, -0.75
+    for k in range(1, n):
+        s = np.full(n, b)
+        s[np.random.default_rng(k).choice(n, size=k, replace=False)] = a
+        exact = (n - k) * math.exp(b) / (k * math.exp(a) + (n - k) * math.exp(b))
+        assert abs(oracle.gap_bound(s, k) - exact) <= 1e-15
+        _, _, _, T = oracle.tail_masses(s)
+        assert abs(T[k] - exact) <= 1e-14
+
+
+def test_multi_gap_bound_with_every_rank_is_exact_for_one_head_key():
+    # k = 1: the head is the top key itself, and with a gap at every rank the
+    # bound sums each tail key's exact weight.
+    rng = np.random.default_rng(5)
+    for n in (2, 7, 31):
+        s = rng.standard_normal(n) * 3.0
+        _, _, _, T = oracle.tail_masses(s)
+        b = oracle.gap_bound(s, 1, list(range(2, n)))
+        assert abs(b - T[1]) <= 1e-13 * max(T[1], 1e-300)
+
+
+def test_gap_bound_closed_form_values():
+    # s = (3, 1, 0, 0, -2): k = 2, Delta = s_(2) - s_(3) = 1.
+    s = np.array([0.0, 3.0, -2.0, 1.0, 0.0])
+    single = 3 * math.exp(-1.0) / (2 + 3 * math.exp(-1.0))
+    assert abs(oracle.gap_bound(s, 2) - single) <= 1e-15
+    # ranks (2, 4, 5): ranks 3-4 score at most s_(3) = 0, rank 5 at most -2.
+    B = 2 * math.exp(-1.0) + math.exp(-3.0)
+    assert abs(oracle.gap_bound(s, 2, [4]) - B / (2 + B)) <= 1e-15
+    assert oracle.gap_bound(s, 5) == 0.0
+    with pytest.raises(ValueError):
+        oracle.gap_bound(s, 2, [2])
+
+
+@pytest.mark.parametrize("sigma,eps", [(1.0, 0.01), (2.5, 0.1), (4.0, 0.3)])
+def test_variance_bound_holds(sigma, eps):
+    rng = np.random.default_rng(17)
+    n, dv = 300, 8
+    S = _random_rows(rng, 4, n, sigma)
+    V = rng.standard_normal((1, n, dv)) * rng.uniform(0.5, 2.0, size=dv)
+    r = oracle.certify_scores(S, V, eps)
+    for i in range(S.shape[0]):
+        P = sp_softmax(S[i])
+        var = oracle.variance_p(P, V[0])
+        # Var_P against its definition through a library mean and variance
+        mu = np.average(V[0], axis=0, weights=P)
+        assert abs(var - float(np.sum(np.average((V[0] - mu) ** 2, axis=0, weights=P)))) \
+            <= 1e-12 * var
+        assert r["out_err"][i] <= oracle.variance_bound(r["tau"][i], var) * (1 + 1e-12)
+
+
+def test_variance_bound_is_attained_by_two_value_rows():
+    # head rows all equal to A and tail rows all equal to B: Var_P(V) is the
+    # between-group part tau (1 - tau) ||A - B||^2 alone, so the bound is met
+    # with equality: sqrt(tau Var / (1 - tau)) = tau ||A - B|| = ||Attn - Attn_k||.
+    rng = np.random.default_rng(3)
+    n, dv = 64, 5
+    s = rng.standard_normal(n) * 1.5
+    r = oracle.certify_scores(s[None], np.zeros((1, n, dv)), 0.1)
+    head = r["head_mask"][0]
+    A, B = rng.standard_normal(dv), rng.standard_normal(dv)
+    V = np.where(head[:, None], A[None, :], B[None, :])
+    r = oracle.certify_scores(s[None], V[None], 0.1)
+    tau = r["tau"][0]
+    var = oracle.variance_p(sp_softmax(s), V)
+    assert abs(var - tau * (1 - tau) * float(np.sum((A - B) ** 2))) <= 1e-12 * var
+    assert abs(oracle.variance_bound(tau, var) - tau * np.linalg.norm(A - B)) <= 1e-12
+    assert abs(r["out_err"][0] - tau * np.linalg.norm(A - B)) <= 1e-12
