@@ -87,8 +87,10 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   L.hchunk = (decode && n > ctopk::resolve_register_row()) ? ctopk::hist_nchunk(n, rows) : 0;
   L.dchunk = decode ? ctopk::select_spec_nchunk(n, rows, n_v, v_dtype, dv) : 0;
   // partial slots per row: head + tail per value-stream chunk, or one per
-  // chunk of the overlapped plan's stream
-  const size_t pslots = 2 * static_cast<size_t>(L.nchunk > L.dchunk ? L.nchunk : L.dchunk);
+  // chunk of the overlapped plan's stream; and one float per chunk for the
+  // sum of w ||v||^2
+  const size_t pchunks = static_cast<size_t>(L.nchunk > L.dchunk ? L.nchunk : L.dchunk);
+  const size_t pslots = 2 * pchunks;
   size_t off = 0;
   L.rowsel = off;
   off += up(static_cast<size_t>(rows) * sizeof(ctopk::RowSel));
@@ -97,7 +99,7 @@ Layout layout(int64_t n, int dv, int rows, int n_v, int v_dtype, bool decode) {
   L.blkz = off;  // per-tile softmax masses (blockwise-bound calls)
   off += up(static_cast<size_t>(rows) * L.nblk * sizeof(float));
   L.part = off;
-  off += up(static_cast<size_t>(rows) * pslots * (dv + 1) * sizeof(float));
+  off += up(static_cast<size_t>(rows) * (pslots * (dv + 1) + pchunks) * sizeof(float));
   L.pmass = off;
   off += up(static_cast<size_t>(rows) * L.hchunk * ctopk::kBins * sizeof(double));
   L.sync = off;  // CutPub [rows]
@@ -215,7 +217,8 @@ int validate_args(const ctopk_args* a) {
   if (!aligned(a->out, 4) || !aligned(a->k_eps, 4) || !aligned(a->tau, 8) ||
       (a->scores && !aligned(a->scores, 4)) || (a->sel_mask && !aligned(a->sel_mask, 4)) ||
       (a->lse && !aligned(a->lse, 8)) || (a->head_scale && !aligned(a->head_scale, 4)) ||
-      (a->out_err && !aligned(a->out_err, 8)) || (a->out_dense && !aligned(a->out_dense, 4)))
+      (a->out_err && !aligned(a->out_err, 8)) || (a->out_dense && !aligned(a->out_dense, 4)) ||
+      (a->out_var && !aligned(a->out_var, 8)))
     return fail(CTOPK_ERR_ALIGN, "outputs must be aligned to their element size");
   if (a->workspace != nullptr) {
     if (!aligned(a->workspace, kAlign)) return fail(CTOPK_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -231,7 +234,8 @@ int validate_args(const ctopk_args* a) {
 // The plan of a validated call (ctopk_plan_id).
 int plan_of(const ctopk_args* a) {
   if (a->flags & CTOPK_FLAG_BOUND) return CTOPK_PLAN_DECODE_BOUND;
-  const bool certificate = a->out_err != nullptr || a->out_dense != nullptr;
+  const bool certificate =
+      a->out_err != nullptr || a->out_dense != nullptr || a->out_var != nullptr;
   if (certificate) return CTOPK_PLAN_DECODE;
   if (ctopk::encoder_supported(a->dtype, a->d, a->n, a->n_q_heads, a->n_kv_heads))
     return CTOPK_PLAN_ENCODER;
@@ -425,7 +429,8 @@ int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream) {
   }
   if (rc != CTOPK_OK) return rc;
   rc = hip_check(ctopk::launch_vsum(scores, a->n, rows, a->n_kv_heads, a->V, a->dtype, a->d, rs,
-                                    part, L.nchunk, a->out, a->out_dense, a->out_err, st),
+                                    part, L.nchunk, a->out, a->out_dense, a->out_err,
+                                    a->out_var, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
   return ok();
@@ -534,7 +539,7 @@ int ctopk_certify_logits(const float* logits, const void* V, int32_t v_dtype, in
                  "resolve launch");
   if (rc != CTOPK_OK) return rc;
   rc = hip_check(ctopk::launch_vsum(logits, n, rows, n_v, V, v_dtype, dv, rs, part, L.nchunk,
-                                    out, nullptr, nullptr, st),
+                                    out, nullptr, nullptr, nullptr, st),
                  "vsum launch");
   if (rc != CTOPK_OK) return rc;
   return ok();

@@ -87,12 +87,13 @@ int vsum_groups(int rows, int n_v, int v_dtype, int dv);
 int vsum_nchunk(int64_t n, int rows, int n_v, int v_dtype, int dv);
 // K4: w * v over kept keys into part [rows, nchunk, dv + 1] (numerator and
 // weight sum per block), then a finalize kernel writes out = num / den.  With
-// dense or err non-NULL the tail is accumulated too (part [rows, nchunk,
-// 2 (dv + 1)]) and the finalize also writes the untruncated output and the
-// output error ||Attn - Attn_k||_2 per row.
+// dense, err or var non-NULL the tail and sum w ||v||^2 are accumulated too
+// (part [rows, nchunk, 2 (dv + 1) + 1]) and the finalize also writes the
+// untruncated output, the output error ||Attn - Attn_k||_2 and Var_P(V) per
+// row (each only where its pointer is non-NULL).
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
                        int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
-                       float* dense, double* err, hipStream_t st);
+                       float* dense, double* err, double* var, hipStream_t st);
 
 // Chunks per group for about `blocks` workgroups in total (whole tiles of
 // kVsumTile keys per chunk, never more chunks than tiles).

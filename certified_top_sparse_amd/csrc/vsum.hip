@@ -47,21 +47,26 @@ __global__ __launch_bounds__(kVsumThreads) void vsum_kernel(
 // makes every block's partials visible (an in-kernel device-scope fence costs
 // a full L2 writeback and invalidate per block on this multi-XCD part).
 // With tail sums (ns == 2) it also writes the untruncated output
-// (num_head + num_tail) / (w_head + w_tail) and the output error
+// (num_head + num_tail) / (w_head + w_tail), the output error
 // ||Attn - Attn_k||_2 = tau * ||mu_tail - mu_head||_2, tau = w_tail / (w_head +
 // w_tail) (the head-tail factorisation in the Abstract of "A Mathematical
 // Theory of Top-k Sparse Attention via Total Variation Distance", arXiv
-// 2512.07647).
+// 2512.07647), and Var_P(V) = sum_i P_i ||v_i||^2 - ||Attn||^2, the spread of
+// the value rows under P that bounds that error by sqrt(tau Var_P(V) /
+// (1 - tau)) (the same Abstract's refinement by Var_P(V); the bound follows
+// from the law of total variance over the head and the tail).
 __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict__ part,
                                                         int nchunk, int dv, int ns,
                                                         float* __restrict__ out,
                                                         float* __restrict__ dense,
-                                                        double* __restrict__ err) {
+                                                        double* __restrict__ err,
+                                                        double* __restrict__ var) {
   __shared__ double s_col[1024];
   __shared__ double s_e2[16];
+  __shared__ double s_d2[16];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
-  const int cols = ns * (dv + 1);
+  const int cols = ns * (dv + 1) + (ns == 2 ? 1 : 0);
   const int NK = 1024 / cols;
   const int k = t / cols;
   const int e = t - k * cols;
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict_
   }
   s_col[t] = a;
   __syncthreads();
-  double e2 = 0.0;
+  double e2 = 0.0, d2 = 0.0;
   double wt_tau = 0.0;
   if (t < dv) {
     double num = 0.0, den = 0.0, numt = 0.0, dent = 0.0;
@@ -97,21 +102,35 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict_
     const double mh = num / den;
     out[static_cast<size_t>(row) * dv + t] = static_cast<float>(mh);
     if (ns == 2) {
-      if (dense != nullptr)
-        dense[static_cast<size_t>(row) * dv + t] = static_cast<float>((num + numt) / (den + dent));
+      const double md = (num + numt) / (den + dent);
+      if (dense != nullptr) dense[static_cast<size_t>(row) * dv + t] = static_cast<float>(md);
       const double diff = dent > 0.0 ? numt / dent - mh : 0.0;
       e2 = diff * diff;
+      d2 = md * md;
       wt_tau = dent / (den + dent);
     }
   }
-  if (ns == 2 && err != nullptr) {  // uniform: the whole block reduces ||mu_t - mu_h||^2
+  if (ns == 2 && (err != nullptr || var != nullptr)) {
+    // uniform: the whole block reduces ||mu_t - mu_h||^2 and ||Attn||^2
     e2 = wave_sum_f64(e2);
-    if ((t & 63) == 0) s_e2[t >> 6] = e2;
+    d2 = wave_sum_f64(d2);
+    if ((t & 63) == 0) {
+      s_e2[t >> 6] = e2;
+      s_d2[t >> 6] = d2;
+    }
     __syncthreads();
     if (t == 0) {
-      double s2 = 0.0;
-      for (int w = 0; w < 16; ++w) s2 += s_e2[w];
-      err[row] = wt_tau * sqrt(s2);
+      double s2 = 0.0, m2 = 0.0, q2 = 0.0, wall = 0.0;
+      for (int w = 0; w < 16; ++w) {
+        s2 += s_e2[w];
+        m2 += s_d2[w];
+      }
+      for (int j = 0; j < NK; ++j) {
+        q2 += s_col[j * cols + 2 * (dv + 1)];
+        wall += s_col[j * cols + dv] + s_col[j * cols + 2 * dv + 1];
+      }
+      if (err != nullptr) err[row] = wt_tau * sqrt(s2);
+      if (var != nullptr) var[row] = fmax(q2 / wall - m2, 0.0);
     }
   }
 }
@@ -119,11 +138,11 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict_
 template <typename T, int D, int GB>
 hipError_t launch_t(const float* scores, int64_t n, int rows, int n_v, const void* V,
                     const RowSel* rs, float* part, int nchunk, float* out, float* dense,
-                    double* err, hipStream_t st) {
+                    double* err, double* var, hipStream_t st) {
   const int G = rows / n_v;
   const int tpb = static_cast<int>(ceil_div(ceil_div(n, kVsumTile), nchunk));
   dim3 grid(nchunk, n_v, static_cast<unsigned>(ceil_div(G, GB)));
-  const bool tail = dense != nullptr || err != nullptr;
+  const bool tail = dense != nullptr || err != nullptr || var != nullptr;
   const hipError_t e =
       tail ? launch(vsum_kernel<T, D, GB, true>, grid, dim3(kVsumThreads), 0, st, scores, n, G,
                     static_cast<const T*>(V), rs, part, nchunk, tpb)
@@ -131,7 +150,7 @@ hipError_t launch_t(const float* scores, int64_t n, int rows, int n_v, const voi
                     static_cast<const T*>(V), rs, part, nchunk, tpb);
   if (e != hipSuccess) return e;
   return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, part, nchunk, D, tail ? 2 : 1,
-                out, dense, err);
+                out, dense, err, var);
 }
 
 
@@ -277,26 +296,27 @@ hipError_t launch_gemm(const float* scores, int64_t n, int rows, int n_v, const 
                               static_cast<const T*>(V), rs, part, nchunk, ck);
   if (e != hipSuccess) return e;
   return launch(finalize_kernel, dim3(rows), dim3(1024), 0, st, static_cast<const float*>(part),
-                nchunk, D, 1, out, static_cast<float*>(nullptr), static_cast<double*>(nullptr));
+                nchunk, D, 1, out, static_cast<float*>(nullptr), static_cast<double*>(nullptr),
+                static_cast<double*>(nullptr));
 }
 
 template <typename T, int D>
 hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const void* V,
                     const RowSel* rs, float* part, int nchunk, float* out, float* dense,
-                    double* err, hipStream_t st) {
+                    double* err, double* var, hipStream_t st) {
   const int G = rows / n_v;
-  if (G >= kGemmRows && dense == nullptr && err == nullptr)
+  if (G >= kGemmRows && dense == nullptr && err == nullptr && var == nullptr)
     return launch_gemm<T, D>(scores, n, rows, n_v, V, rs, part, nchunk, out, st);
   if (G == 1)
-    return launch_t<T, D, 1>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+    return launch_t<T, D, 1>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
   if (G == 2)
-    return launch_t<T, D, 2>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+    return launch_t<T, D, 2>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
   if constexpr (kGroupMax<T, D> == 4) {
-    return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+    return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
   } else {
     if (G <= 4)
-      return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
-    return launch_t<T, D, 8>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+      return launch_t<T, D, 4>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
+    return launch_t<T, D, 8>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
   }
 }
 
@@ -304,16 +324,16 @@ hipError_t launch_d(const float* scores, int64_t n, int rows, int n_v, const voi
 
 hipError_t launch_vsum(const float* scores, int64_t n, int rows, int n_v, const void* V,
                        int v_dtype, int dv, const RowSel* rs, float* part, int nchunk, float* out,
-                       float* dense, double* err, hipStream_t st) {
+                       float* dense, double* err, double* var, hipStream_t st) {
   if (v_dtype == 1) {
     if (dv == 128)
       return launch_d<uint16_t, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err,
-                                     st);
-    return launch_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+                                     var, st);
+    return launch_d<uint16_t, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
   }
   if (dv == 128)
-    return launch_d<float, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
-  return launch_d<float, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, st);
+    return launch_d<float, 128>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
+  return launch_d<float, 64>(scores, n, rows, n_v, V, rs, part, nchunk, out, dense, err, var, st);
 }
 
 int vsum_groups(int rows, int n_v, int v_dtype, int dv) {

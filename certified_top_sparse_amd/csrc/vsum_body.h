@@ -93,6 +93,7 @@ struct StreamSmem {
   using S = StreamShape<T, D, GB, MODE, NW>;
   typename S::Acc red[S::NS][NW][GB * D];
   double wsum[S::NS][NW][GB];
+  double q2[MODE == kStreamHeadTail ? NW : 1][GB];  // head and tail: sum of w ||v||^2
   float w[NW][S::PASS][GB];  // wave-private weight staging
   uint64_t thr[GB];          // given mode: key64 thresholds per head
   float m[GB];               // given mode: row maxima per head
@@ -118,7 +119,8 @@ struct NoHook {
 // and cut from rs; the given mode takes them from StreamSmem.  `hook` sees every lane's sums (StreamLane)
 // after the stream and before the workgroup reduction and may change them.
 // Partials: part[(head, chunk)] holds NS blocks of [D numerators | weight
-// sum].
+// sum], and in head and tail mode one more float: sum over all keys of
+// w ||v||^2 (from which the combine forms Var_P(V)).
 template <typename T, int D, int GB, int MODE, int NW, typename Hook = NoHook>
 __device__ __forceinline__ void value_stream_block(
     StreamSmem<T, D, GB, MODE, NW>& sm, const float* __restrict__ scores, int64_t n, int G,
@@ -174,6 +176,9 @@ __device__ __forceinline__ void value_stream_block(
     for (int e = 0; e < EPL; ++e) acct[j][e] = Acc(0);
   double wsum = 0.0;   // weight of head hw over this lane's pairs
   double wsumt = 0.0;  // and of its tail (TAIL)
+  Acc q2[TAIL ? GB : 1];  // TAIL: sum of w * (this lane's part of ||v||^2), per head
+#pragma unroll
+  for (int j = 0; j < (TAIL ? GB : 1); ++j) q2[j] = Acc(0);
 
   for (int tb = 0; tb < tpb; ++tb) {
     const int64_t p0 = (static_cast<int64_t>(chunk) * tpb + tb) * kVsumTile + wave * PASS;
@@ -230,6 +235,9 @@ __device__ __forceinline__ void value_stream_block(
       float v[EPL];
       VSlice<T>::load(u[it], v);
       if constexpr (TAIL) {
+        Acc vv = Acc(0);  // this lane's slice of ||v||^2
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vv += static_cast<Acc>(v[e]) * static_cast<Acc>(v[e]);
 #pragma unroll
         for (int j = 0; j < GB; ++j) {
           const Acc wh = static_cast<Acc>(fmaxf(wj[j], 0.0f));
@@ -239,6 +247,7 @@ __device__ __forceinline__ void value_stream_block(
             acc[j][e] += wh * static_cast<Acc>(v[e]);
             acct[j][e] += wt * static_cast<Acc>(v[e]);
           }
+          q2[j] += (wh + wt) * vv;
         }
       } else {
 #pragma unroll
@@ -271,6 +280,16 @@ __device__ __forceinline__ void value_stream_block(
   }
   wsum = xrow32_sum(xrow16_sum(wsum));
   if constexpr (TAIL) wsumt = xrow32_sum(xrow16_sum(wsumt));
+  if constexpr (TAIL) {
+    // every lane of the wave holds a part of each head's sum: a fixed tree
+    // over all 64 lanes
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      double x = static_cast<double>(q2[j]);
+      x = wave_sum_f64(x);
+      if (lane == 0) sm.q2[wave][j] = x;
+    }
+  }
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < GB; ++j)
@@ -285,7 +304,16 @@ __device__ __forceinline__ void value_stream_block(
     if constexpr (TAIL) sm.wsum[NS - 1][wave][lane] = wsumt;
   }
   __syncthreads();
-  const size_t pstride = static_cast<size_t>(NS * (D + 1));
+  const size_t pstride = static_cast<size_t>(NS * (D + 1) + (TAIL ? 1 : 0));
+  if constexpr (TAIL) {
+    if (t < nh) {
+      double sum = 0.0;
+#pragma unroll
+      for (int g = 0; g < NW; ++g) sum += sm.q2[g][t];
+      part[(static_cast<size_t>(h0 + t) * nchunk + chunk) * pstride + NS * (D + 1)] =
+          static_cast<float>(sum);
+    }
+  }
   for (int idx = t; idx < NS * GB * (D + 1); idx += NT) {
     const int part_k = idx / (GB * (D + 1));  // 0 head (or dense), 1 tail
     const int rem = idx - part_k * GB * (D + 1);

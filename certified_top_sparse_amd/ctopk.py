@@ -73,6 +73,7 @@ class CtopkArgs(ctypes.Structure):
         ("out_err", ctypes.c_void_p),
         ("out_dense", ctypes.c_void_p),
         ("flags", ctypes.c_uint32),
+        ("out_var", ctypes.c_void_p),
     ]
 
 
@@ -267,7 +268,7 @@ CTOPK_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=None,
               tau=None, sel_mask=None, scores=None, lse=None, out_err=None,
-              out_dense=None, flags=0) -> CtopkArgs:
+              out_dense=None, out_var=None, flags=0) -> CtopkArgs:
     n_q, d = q.shape
     n_kv, n, _ = K.shape
     a = CtopkArgs()
@@ -280,7 +281,7 @@ def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     for f, t in (("out", out), ("k_eps", k_eps), ("tau", tau), ("sel_mask", sel_mask),
                  ("scores", scores), ("lse", lse), ("out_err", out_err),
-                 ("out_dense", out_dense)):
+                 ("out_dense", out_dense), ("out_var", out_var)):
         setattr(a, f, None if t is None else t.data_ptr())
     a.flags = int(flags)
     return a
@@ -288,13 +289,15 @@ def make_args(q, K, V, eps, *, head_scale=None, workspace=None, out=None, k_eps=
 
 def ctopk_certify_ex(q, K, V, eps, *, head_scale=None, workspace=None, want_mask=False,
                      want_scores=False, want_lse=False, want_err=False, want_dense=False,
-                     bound=False, stream=None):
+                     want_var=False, bound=False, stream=None):
     """Full form: q [Hq, d], K/V [Hkv, n, d] in bf16 or fp32, optional per-head
     scale [Hq] fp32 and caller workspace (uint8 tensor).
 
     Returns a dict with out, k_eps, tau and, on request, sel_mask
     [Hq, ceil(n/32)] int32 bit words, scores [Hq, n] fp32, lse [Hq] fp64,
-    out_err [Hq] fp64 (||Attn - Attn_k||_2) and out_dense [Hq, d] fp32 (Attn).
+    out_err [Hq] fp64 (||Attn - Attn_k||_2), out_dense [Hq, d] fp32 (Attn) and
+    out_var [Hq] fp64 (Var_P(V), which bounds the output error by
+    sqrt(tau Var_P(V) / (1 - tau))).
     bound=True certifies with the blockwise bound (CTOPK_FLAG_BOUND): k_eps is
     then the number of keys kept and tau the certified bound on their TV."""
     import torch
@@ -321,6 +324,8 @@ def ctopk_certify_ex(q, K, V, eps, *, head_scale=None, workspace=None, want_mask
         res["out_err"] = torch.empty(n_q, dtype=torch.float64, device=dev)
     if want_dense:
         res["out_dense"] = torch.empty((n_q, d), dtype=torch.float32, device=dev)
+    if want_var:
+        res["out_var"] = torch.empty(n_q, dtype=torch.float64, device=dev)
     if head_scale is not None:
         _require_cuda_contig("head_scale", head_scale)
         if head_scale.dtype != torch.float32 or head_scale.numel() != n_q:
@@ -328,7 +333,8 @@ def ctopk_certify_ex(q, K, V, eps, *, head_scale=None, workspace=None, want_mask
     a = make_args(q, K, V, eps, head_scale=head_scale, workspace=workspace, out=res["out"],
                   k_eps=res["k_eps"], tau=res["tau"], sel_mask=res.get("sel_mask"),
                   scores=res.get("scores"), lse=res.get("lse"), out_err=res.get("out_err"),
-                  out_dense=res.get("out_dense"), flags=CTOPK_FLAG_BOUND if bound else 0)
+                  out_dense=res.get("out_dense"), out_var=res.get("out_var"),
+                  flags=CTOPK_FLAG_BOUND if bound else 0)
     _check(lib.ctopk_certify_ex(ctypes.byref(a), _stream(stream)))
     return res
 

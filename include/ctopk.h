@@ -125,12 +125,19 @@ typedef struct ctopk_args {
                                NULL: kept in the workspace                            */
   double* lse;              /* optional [n_q_heads] log-sum-exp of the scores; NULL    */
   /* Output-level certificate (head-tail factorisation in the Abstract): when
-     either pointer is non-NULL the value pass also accumulates the tail.      */
+     either pointer, or out_var below, is non-NULL the value pass also
+     accumulates the tail.                                                     */
   double* out_err;          /* optional [n_q_heads] ||Attn - Attn_k||_2 = tau *
                                ||mu_tail - mu_head||_2 (fp64); NULL: skip          */
   float* out_dense;         /* optional [n_q_heads, d] untruncated softmax output
                                Attn (fp32); NULL: skip                              */
   uint32_t flags;           /* CTOPK_FLAG_* bits; 0 for the exact certificate        */
+  double* out_var;          /* optional [n_q_heads] Var_P(V) = sum_i P_i ||v_i - Attn||^2
+                               (fp64; accumulated with the tail like out_err): the
+                               Abstract refines the output error by it, and with
+                               the factorisation above the law of total variance
+                               gives ||Attn - Attn_k||_2 <= sqrt(tau Var_P(V) /
+                               (1 - tau)); NULL: skip                                */
 } ctopk_args;
 
 /*
@@ -161,7 +168,7 @@ typedef struct ctopk_args {
  * whose QK^T and head-only output use MFMA; it needs no workspace.  Other rows
  * of at most 1024 keys run on one fused kernel per call (scores, select and
  * head-only output by one workgroup per query row; no workspace either).
- * Calls that ask for out_err or out_dense take the general path.  Results
+ * Calls that ask for out_err, out_dense or out_var take the general path.  Results
  * follow the same definitions on every path.
  */
 CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
@@ -188,14 +195,14 @@ CTOPK_API int ctopk_certify_ex(const ctopk_args* a, ctopk_stream_t stream);
  *     and tau to fp64 rounding.  Taken for decode
  *     rows of 16385..32768 keys when at least half of the compute units (128)
  *     remain beside one workgroup per query row and the stream's chunks hold
- *     at most 2048 keys, and never for calls that ask for out_err or
- *     out_dense;
+ *     at most 2048 keys, and never for calls that ask for out_err,
+ *     out_dense or out_var;
  *   CTOPK_PLAN_DECODE_BOUND (calls with CTOPK_FLAG_BOUND): score scan with
  *     per-block masses; the blockwise bound (one workgroup per row, in place
  *     of the select); value stream over the kept keys; combine;
  *   CTOPK_PLAN_DECODE_FUSED: rows of at most 1024 keys that the encoder path
- *     does not take, without out_err or out_dense: one kernel, one workgroup
- *     per query row, one key per thread: the scores (the same arithmetic as
+ *     does not take, without out_err, out_dense or out_var: one kernel, one
+ *     workgroup per query row, one key per thread: the scores (the same arithmetic as
  *     the score scan, so the same values), the select as a mass-weighted
  *     radix descent over 8-bit digits of the 64-bit key order, and the
  *     head-only output from the head keys' value rows.

@@ -157,7 +157,8 @@ def certify_scores(S, V, eps: float, row_to_v=None, with_diagnostics: bool = Tru
     S: [R, n] scores; V: [Hv, n, dv] value rows; row r reads V[row_to_v[r]]
     (default: all rows read V[0]).  Returns a dict of float64/int64 arrays:
     k_eps [R], tau [R], out [R, dv], out_dense [R, dv] (untruncated softmax
-    output), out_err [R] (= ||out_dense - out||_2), lse [R], T_prev [R] (= T_{k_eps - 1}),
+    output), out_err [R] (= ||out_dense - out||_2), out_var [R] (= Var_P(V)),
+    lse [R], T_prev [R] (= T_{k_eps - 1}),
     near_boundary [R] (bool), head_mask [R, n] (bool), and, with diagnostics,
     s_star [R] (score of the last kept key).
     """
@@ -202,6 +203,13 @@ def certify_scores(S, V, eps: float, row_to_v=None, with_diagnostics: bool = Tru
         dense[sel] = w[sel] @ V[g]
     dense /= Z[:, None]
     out_err = np.linalg.norm(dense - out, axis=-1)
+    # Var_P(V) = sum_i P_i ||v_i - Attn||^2 (the spread the Abstract's
+    # refinement of the output error is stated in; see variance_bound)
+    var_p = np.empty(R, dtype=np.float64)
+    for g in np.unique(row_to_v):
+        sel = np.nonzero(row_to_v == g)[0]
+        for r in sel:
+            var_p[r] = (w[r] / Z[r]) @ np.sum((V[g] - dense[r]) ** 2, axis=1)
 
     res = {
         "k_eps": k.astype(np.int64),
@@ -209,6 +217,7 @@ def certify_scores(S, V, eps: float, row_to_v=None, with_diagnostics: bool = Tru
         "out": out,
         "out_dense": dense,
         "out_err": out_err,
+        "out_var": var_p,
         "lse": np.log(Z) + np.max(S, axis=-1),
         "T_prev": T_prev,
         "near_boundary": near,

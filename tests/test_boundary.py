@@ -97,7 +97,7 @@ def test_eps_errors(lib, eps):
 @pytest.mark.parametrize("field,value", [("q", A16 + 8), ("K", A16 + 2), ("V", A16 + 4),
                                          ("out", A16 + 2), ("tau", A16 + 4),
                                          ("k_eps", A16 + 1), ("out_err", A16 + 4),
-                                         ("out_dense", A16 + 2)])
+                                         ("out_dense", A16 + 2), ("out_var", A16 + 4)])
 def test_alignment_errors(lib, field, value):
     assert ct.ctopk_validate(good_args(**{field: value})) == cb.CTOPK_ERR_ALIGN
 
@@ -205,6 +205,7 @@ def test_missing_library_fails_loudly(tmp_path):
     ({"n_q_heads": 192, "n_kv_heads": 24}, cb.CTOPK_PLAN_DECODE),
     ({"out_err": A16 * 7}, cb.CTOPK_PLAN_DECODE),                 # certificate: serial stream
     ({"out_dense": A16 * 7}, cb.CTOPK_PLAN_DECODE),
+    ({"out_var": A16 * 7}, cb.CTOPK_PLAN_DECODE),
     ({"n": 512, "d": 64, "n_q_heads": 512, "n_kv_heads": 8}, cb.CTOPK_PLAN_ENCODER),
     ({"n": 512, "d": 64, "n_q_heads": 512, "n_kv_heads": 8, "out_err": A16 * 7},
      cb.CTOPK_PLAN_DECODE),
@@ -217,6 +218,7 @@ def test_missing_library_fails_loudly(tmp_path):
     ({"n": 512, "d": 64, "n_q_heads": 32, "n_kv_heads": 8}, cb.CTOPK_PLAN_DECODE_FUSED),
     ({"n": 1024, "out_err": A16 * 7}, cb.CTOPK_PLAN_DECODE),
     ({"n": 1024, "out_dense": A16 * 7}, cb.CTOPK_PLAN_DECODE),
+    ({"n": 1024, "out_var": A16 * 7}, cb.CTOPK_PLAN_DECODE),
 ])
 def test_plan_choice(lib, kw, plan):
     assert ct.ctopk_plan(good_args(**kw)) == plan

@@ -386,7 +386,8 @@ def _certificate_case(ct, wl, eps, label, rtol, same_path=True, same_select=True
     q, K, V = dev(wl["q"]), dev(wl["K"]), dev(wl["V"])
     hs = dev(wl["head_scale"])
     plain = ct.ctopk_certify_ex(q, K, V, eps, head_scale=hs)
-    res = ct.ctopk_certify_ex(q, K, V, eps, head_scale=hs, want_err=True, want_dense=True)
+    res = ct.ctopk_certify_ex(q, K, V, eps, head_scale=hs, want_err=True, want_dense=True,
+                              want_var=True)
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy() for k, v in res.items()}
     p = {k: v.cpu().numpy() for k, v in plain.items()}
@@ -411,8 +412,16 @@ def _certificate_case(ct, wl, eps, label, rtol, same_path=True, same_select=True
     e_gpu = g["out_err"][kok]
     rel = np.abs(e_gpu - e_ref) / np.maximum(e_ref, 1e-12)
     assert rel.max() <= rtol, f"output error off by {rel.max():.3e} (relative)"
+    # Var_P(V) against the oracle's, on every row (it does not depend on the cut)
+    vrel = np.abs(g["out_var"] - ref["out_var"]) / ref["out_var"]
+    assert vrel.max() <= rtol, f"Var_P(V) off by {vrel.max():.3e} (relative)"
+    # and the bound it gives holds for the device's own error and tau
+    vb = np.sqrt(g["tau"] * g["out_var"] / (1.0 - g["tau"]))
+    assert np.all(g["out_err"] <= vb * (1 + rtol)), "Var_P(V) bound violated"
     print(f"{label}: dense rel L2 max {dense_err.max():.2e}, ||Attn - Attn_k|| rel err max "
-          f"{rel.max():.2e}, mean ||Attn - Attn_k|| {e_ref.mean():.3e}", flush=True)
+          f"{rel.max():.2e}, mean ||Attn - Attn_k|| {e_ref.mean():.3e}, Var_P rel err max "
+          f"{vrel.max():.2e}, mean error / Var_P bound {np.mean(g['out_err'] / vb):.3f}",
+          flush=True)
 
 
 @pytest.mark.parametrize("eps", [0.01, 0.1])

@@ -613,6 +613,7 @@ def test_variance_bound_holds(sigma, eps):
         assert abs(var - float(np.sum(np.average((V[0] - mu) ** 2, axis=0, weights=P)))) \
             <= 1e-12 * var
         assert r["out_err"][i] <= oracle.variance_bound(r["tau"][i], var) * (1 + 1e-12)
+        assert abs(r["out_var"][i] - var) <= 1e-11 * var
 
 
 def test_variance_bound_is_attained_by_two_value_rows():
