@@ -543,6 +543,18 @@ def test_streamed_row_maximum_far_above_the_sample(ct, lift):
         _logits_case(ct, L, V, eps, f"streamed row, max {lift} above the sample")
 
 
+@pytest.mark.parametrize("n", [65536, 100000])
+def test_streamed_row_coarse_grid_ties(ct, n):
+    """Streamed rows whose scores sit on a grid of step 1/4: the window that
+    level 0 lists around the sample's estimate of the cut, and the cut bin
+    taken from it, hold long runs of equal scores, ordered by index."""
+    rng = np.random.default_rng(n + 3)
+    L = (np.round(rng.standard_normal((4, n)) * 2.0 * 4.0) / 4.0).astype(np.float32)
+    V = rng.standard_normal((1, n, 64)).astype(np.float32)
+    for eps in (0.01, 0.1, 0.5):
+        _logits_case(ct, L, V, eps, f"streamed row, scores on a 1/4 grid n={n}")
+
+
 def test_streamed_row_cut_below_the_sampled_range(ct):
     """Keys far below every sampled key fall into the first level-0 bin; with
     a tiny eps the cut lies among them, so that bin is resolved by the digit
