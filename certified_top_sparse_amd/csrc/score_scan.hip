@@ -16,6 +16,10 @@
 //   * one short block per tile (thousands of blocks, all loads of a wave
 //     issued before any arithmetic, no branch around a load), so blocks in
 //     different phases keep HBM busy;
+//   * K of at most kScanCachedMax bytes is read with ordinary loads, larger K
+//     with non-temporal ones (measured: at 64 MiB of K the ordinary loads take
+//     the scan from 14.7 to 13.7 us; at 1 GiB they make it 180 -> 200 us and
+//     slow the next kernel's reads of the scores, which they evict);
 //   * the LPR partial dots are combined by DPP butterflies (full-rate VALU,
 //     no LDS round trips), the scores are staged in LDS and written out
 //     coalesced ([n_q_heads, n] fp32, 4*G bytes per key against d*esize bytes
@@ -30,7 +34,9 @@ namespace {
 // One block per tile of kScanTile keys of one KV head and up to GB query
 // heads: 4 waves, each covering kScanTile / 4 keys with all of its K loads
 // issued before any arithmetic.
-template <typename T, int D, int GB, bool HS>
+constexpr size_t kScanCachedMax = size_t(128) << 20;
+
+template <typename T, int D, int GB, bool HS, bool NT>
 __global__ __launch_bounds__(256) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ K, const float* __restrict__ head_scale,
     float default_scale, int64_t n, int G, int nblk, float* __restrict__ scores,
@@ -63,7 +69,11 @@ __global__ __launch_bounds__(256) void score_scan_kernel(
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int64_t r = min(tile0 + lbase + it * RPW + rg, n - 1);
-    kv[it] = load_stream16(Kb + r * D + seg * EPL);
+    if constexpr (NT) {
+      kv[it] = load_stream16(Kb + r * D + seg * EPL);
+    } else {
+      kv[it] = *reinterpret_cast<const uint4*>(Kb + r * D + seg * EPL);
+    }
   }
   // q slices (head slots past nh repeat the last head and are never written).
   uint4 qv[GB];
@@ -130,13 +140,16 @@ hipError_t launch_t(const void* q, const void* K, const float* head_scale, float
   const int G = n_q / n_kv;
   const int nblk = static_cast<int>(ceil_div(n, kScanTile));
   dim3 grid(nblk, n_kv, static_cast<unsigned>(ceil_div(G, GB)));
+  const bool nt = static_cast<size_t>(n_kv) * static_cast<size_t>(n) * D * sizeof(T) >
+                  kScanCachedMax;
+#define CTOPK_SCAN_LAUNCH(HS, NT)                                                              \
+  launch(score_scan_kernel<T, D, GB, HS, NT>, grid, dim3(256), 0, st,                       \
+         static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale, n, G, \
+         nblk, scores, blkstat, blkz, zb, zbytes, zb2, zbytes2)
   if (head_scale != nullptr)
-    return launch(score_scan_kernel<T, D, GB, true>, grid, dim3(256), 0, st,
-                  static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale,
-                  n, G, nblk, scores, blkstat, blkz, zb, zbytes, zb2, zbytes2);
-  return launch(score_scan_kernel<T, D, GB, false>, grid, dim3(256), 0, st,
-                static_cast<const T*>(q), static_cast<const T*>(K), head_scale, default_scale, n,
-                G, nblk, scores, blkstat, blkz, zb, zbytes, zb2, zbytes2);
+    return nt ? CTOPK_SCAN_LAUNCH(true, true) : CTOPK_SCAN_LAUNCH(true, false);
+  return nt ? CTOPK_SCAN_LAUNCH(false, true) : CTOPK_SCAN_LAUNCH(false, false);
+#undef CTOPK_SCAN_LAUNCH
 }
 
 template <typename T, int D>
