@@ -284,6 +284,33 @@ def test_caller_workspace_matches_cached(ct):
     assert np.allclose(a["tau"], b["tau"], rtol=1e-14, atol=0)
 
 
+def _random_case(seed):
+    """Seeded random decode shape: n log-uniform in [1, 140000] (every plan's
+    range: fused rows, the general plan, the overlapped plan, streamed rows
+    with level-0 partials), group width, KV heads, d, dtype, eps and a
+    per-head temperature range."""
+    r = np.random.default_rng(5000 + seed)
+    n = int(np.exp(r.uniform(0.0, np.log(140000.0))))
+    G = int(r.choice([1, 2, 3, 4, 5, 8, 16]))
+    n_kv = int(r.integers(1, 4))
+    d = int(r.choice([64, 128]))
+    dtype = str(r.choice(["f32", "bf16"]))
+    eps = float(np.exp(r.uniform(np.log(1e-4), np.log(0.9))))
+    lo = float(r.uniform(0.25, 1.5))
+    return n, G, n_kv, d, dtype, eps, (lo, lo * float(r.uniform(1.0, 3.0)))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_decode_shapes(ct, seed):
+    n, G, n_kv, d, dtype, eps, tr = _random_case(seed)
+    wl = workloads.gqa_decode(n=n, n_q=G * n_kv, n_kv=n_kv, d=d, planted=int(min(16, n // 8)),
+                              rotation=10 + seed, temp_range=tr)
+    if dtype == "f32":
+        wl = as_f32(wl)
+    check_decode(ct, wl, eps, f"random case {seed} (plan {plan_of(ct, wl)}, {dtype}, "
+                 f"temperature {tr[0]:.2f}..{tr[1]:.2f})")
+
+
 @pytest.mark.parametrize("n", [20000, 40000])
 def test_determinism(ct, n):
     # k, the head and tau repeat bit for bit on every plan; out too on the
