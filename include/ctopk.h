@@ -23,7 +23,13 @@
  *     [n_kv_heads, n, d]; query head h reads KV head h / (n_q_heads / n_kv_heads)
  *     (grouped-query attention; batch is folded into the head dimensions).
  *   - Calls are asynchronous: work is enqueued on `stream` (NULL = the default
- *     stream) and the call returns.  No device-to-host copy, no host sync.
+ *     stream) and the call returns.  No device-to-host copy, no host sync,
+ *     with one exception: a call made without a caller workspace (other than
+ *     ctopk_certify_noalloc) uses the library's cached per-device workspace,
+ *     and when it needs more scratch than that holds it first waits for the
+ *     whole device (hipDeviceSynchronize), frees it and allocates a larger one
+ *     (hipMalloc); later calls with the same or smaller sizes never do.  Pass
+ *     a workspace, or use ctopk_certify_noalloc, to avoid it.
  *   - Argument errors are detected on the host before anything is enqueued and
  *     return a negative ctopk_status; ctopk_last_error_string() describes the
  *     last error of the calling thread.  A failed kernel launch returns
