@@ -612,6 +612,37 @@ __device__ __forceinline__ void resolve_row(
           }
         }
       }
+    } else if constexpr (!kPrefix && PT == 0) {
+      // A streamed row's first pass, batch by batch, in the same vector form:
+      // per lane the count of its keys below f0 and one bit per slot of the
+      // batch in [f0, f1); the few lanes with a set bit append their keys.
+      static_assert(kReadBatch <= 32, "one bit per slot");
+      uint32_t cnt = 0u;
+      for (int64_t base = 0; base < n; base += static_cast<int64_t>(kReadBatch) * kResolveThreads) {
+        float vv[kReadBatch];
+        load_batch(sr, n, base, t, vv);
+        uint32_t inm = 0u;
+#pragma unroll
+        for (int u = 0; u < kReadBatch; ++u) {
+          const bool valid = base + u * kResolveThreads + t < n;
+          cnt += (valid & (vv[u] < f0)) ? 1u : 0u;
+          inm |= (valid & (vv[u] >= f0) & (vv[u] < f1)) ? (1u << u) : 0u;
+        }
+        if (inm != 0u) {
+#pragma unroll
+          for (int u = 0; u < kReadBatch; ++u) {
+            if (inm & (1u << u)) {
+              const uint64_t k =
+                  key64(vv[u], static_cast<uint32_t>(base + u * kResolveThreads + t));
+              const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+              if (slot < static_cast<uint32_t>(kCandCap)) sh.cand[slot] = k;
+              kmn = k < kmn ? k : kmn;
+              kmx = k > kmx ? k : kmx;
+            }
+          }
+        }
+      }
+      nbelow = wave_sum_u32_dpp(cnt);
     } else {
     E.for_each_all([&](int64_t i, float s, bool valid) {
       // One lane mask per comparison (each a single vector compare), combined
