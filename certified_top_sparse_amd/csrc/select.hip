@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void hist0_kernel(const float* __restrict__ sc
   const float* sr = scores + static_cast<size_t>(row) * static_cast<size_t>(n);
   const int64_t c0 = static_cast<int64_t>(cb) * chunk;
   const int64_t c1 = min(n, c0 + chunk);
-  constexpr int U = 8;
+  constexpr int U = 16;
   for (int64_t base = c0; base < c1; base += U * 256) {
     float v[U];
 #pragma unroll
