@@ -228,17 +228,6 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ sr, int64_t
   for (int u = 0; u < kReadBatch; ++u) v[u] = sr[min(base + u * kResolveThreads + t, n - 1)];
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int j) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), j);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), j);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ double readlane_f64(double v, int j) {
-  const uint64_t b = readlane_u64(static_cast<uint64_t>(__double_as_longlong(v)), j);
-  return __longlong_as_double(static_cast<long long>(b));
-}
-
 // The workgroup ends the search over c <= 64 keys (all in the current range):
 // the cut key is the largest whose lower candidates carry mass <= epsZ - R.
 // Lane i of every wave holds candidate i; wave w sums, for each i, the
