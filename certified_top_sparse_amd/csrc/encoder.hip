@@ -10,7 +10,7 @@
 //
 // One workgroup = 4 wavefronts = 32 query rows of one KV head: two row
 // groups of 16 rows, each row's keys split into two halves of NT / 2 tiles,
-// one wave per (row group, half).  About 49 KiB of LDS and up to 256 VGPRs
+// one wave per (row group, half).  About 69 KiB of LDS and up to 256 VGPRs
 // (the scores stay in registers), so two workgroups share a CU.  Lane (r, g) = (lane % 16, lane / 16) of a
 // wave holds row r and the keys kh * 8 NT + 16 t + 4 g + e (t < NT / 2, e < 4),
 // which is the fp32 result layout of a 16x16x32 bf16 MFMA computing
@@ -24,7 +24,7 @@
 //     over 64 bins per row (equal-width value bins first, bins over the
 //     order-preserving integer encoding of the score below that), each level
 //     keeping the one bin that holds the cut.  It ends exactly, either by
-//     pairwise key comparison once a row has <= 32 candidates, or by index
+//     pairwise key comparison once a row has <= 48 candidates, or by index
 //     rank when all remaining candidates share one score.
 //  3. out^T = V^T P^T on MFMA, V staged transposed through LDS.  P holds the
 //     head weights split into bf16 high and low parts, so the products carry
@@ -46,9 +46,9 @@ constexpr int kEncMaxKeys = 512;
 constexpr int kEncMinGroup = 64;
 constexpr int kEncBins = 64;              // bins per row and level
 constexpr int kHistStride = kEncBins + 1; // doubles per histogram row (bank padding)
-constexpr int kLaneCand = 8;              // candidate slots per lane
+constexpr int kLaneCand = 10;             // candidate slots per lane
 constexpr int kLaneSlots = kLaneCand + 1; // plus one slot that takes every other write
-constexpr int kFinishMax = 32;            // exact finish at or below this many candidates
+constexpr int kFinishMax = 48;            // exact finish at or below this many candidates
 // Every level below the first drops at least one candidate, so n levels suffice.
 constexpr int kMaxLevels = 2 * kEncMaxKeys;
 
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const bool fin_list = active && over == 0 && ctot <= kFinishMax;
     const bool fin_eq = active && !fin_list && cmn == cmx;
 
-    // Exact finish on <= 32 candidates: the cut is the largest candidate key
+    // Exact finish on <= kFinishMax candidates: the cut is the largest candidate key
     // whose strictly smaller keys carry mass <= thr.  The row's candidates go
     // into one list (each lane's after those of the row's lanes before it),
     // and lane (kh, g) of the row tests candidates 4 kh + g, + 8, ...
