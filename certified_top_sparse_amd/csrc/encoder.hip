@@ -10,7 +10,7 @@
 //
 // One workgroup = 4 wavefronts = 32 query rows of one KV head: two row
 // groups of 16 rows, each row's keys split into two halves of NT / 2 tiles,
-// one wave per (row group, half).  About 69 KiB of LDS and up to 256 VGPRs
+// one wave per (row group, half).  72 KiB of LDS and up to 256 VGPRs
 // (the scores stay in registers), so two workgroups share a CU.  Lane (r, g) = (lane % 16, lane / 16) of a
 // wave holds row r and the keys kh * 8 NT + 16 t + 4 g + e (t < NT / 2, e < 4),
 // which is the fp32 result layout of a 16x16x32 bf16 MFMA computing
@@ -69,15 +69,15 @@ struct GroupXchg {  // per-row values the two waves of a row group exchange
   int lcnt[2][kWave];  // candidates per lane
   uint32_t bm[16][16]; // candidate bitmap per row (tied scores)
 };
-// The K and V stages (at most 2 x 128 x 72 bf16) share the buffer with the
+// The K and V stages (at most 2 x 256 x 72 bf16) share the buffer with the
 // select scratch of the row groups.
-constexpr int kEncStage = 2 * 128 * 72 * 2;
+constexpr int kEncStage = 2 * 256 * 72 * 2;
 constexpr int kEncSelect = kEncGroups * static_cast<int>(sizeof(GroupSel));
 constexpr int kEncSmem = kEncSelect > kEncStage ? kEncSelect : kEncStage;
 
 template <int D>
 struct Geo {
-  static constexpr int kChunk = D == 64 ? 128 : 64;  // keys per staged chunk and half
+  static constexpr int kChunk = D == 64 ? 256 : 64;  // keys per staged chunk and half
   static constexpr int kKStride = D + 8;              // bf16 per staged K row
 };
 static_assert(2 * Geo<64>::kChunk * Geo<64>::kKStride * 2 <= kEncSmem, "K stage");
