@@ -10,7 +10,7 @@
 //
 // One workgroup = 4 wavefronts = 32 query rows of one KV head: two row
 // groups of 16 rows, each row's keys split into two halves of NT / 2 tiles,
-// one wave per (row group, half).  72 KiB of LDS and up to 256 VGPRs
+// one wave per (row group, half).  About 79 KiB of LDS and up to 256 VGPRs
 // (the scores stay in registers), so two workgroups share a CU.  Lane (r, g) = (lane % 16, lane / 16) of a
 // wave holds row r and the keys kh * 8 NT + 16 t + 4 g + e (t < NT / 2, e < 4),
 // which is the fp32 result layout of a 16x16x32 bf16 MFMA computing
