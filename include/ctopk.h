@@ -63,7 +63,7 @@ typedef enum {
   CTOPK_ERR_SHAPE = -2,       /* n, d, head counts or their ratio are invalid    */
   CTOPK_ERR_EPS = -3,         /* eps is not a finite number in (0, 1)           */
   CTOPK_ERR_ALIGN = -4,       /* an input/output pointer is not 16-byte aligned  */
-  CTOPK_ERR_UNSUPPORTED = -5, /* valid request this build does not handle        */
+  CTOPK_ERR_UNSUPPORTED = -5, /* valid request the library does not handle       */
   CTOPK_ERR_WORKSPACE = -6,   /* caller workspace too small                      */
   CTOPK_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed      */
 } ctopk_status;
