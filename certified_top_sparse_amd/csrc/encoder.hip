@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int TPC = CK / 16;                            // tiles per chunk
   constexpr int NCH = H / CK;                             // chunks per half
   constexpr int KS = Gm::kKStride;
-  constexpr int VS = CK + 8;                              // bf16 per staged V^T row
+  constexpr int VS = CK + 4;                              // bf16 per staged V^T row
   static_assert(H % CK == 0 && TPC % 2 == 0, "chunking");
   __shared__ __align__(16) unsigned char smem[kEncSmem];
   __shared__ GroupXchg xs[kEncGroups];
